@@ -1,0 +1,194 @@
+"""Benchmark: the Gated DeltaNet speculative-verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one spec-decode round of one GDN layer on the 64-slot workload (64 slots, 16 key /
+32 value heads, d = 128, K+1 = 16 bf16 tokens per slot, fp32 state and capture): gdn_verify
+(conv, gate, delta rule, readout, norm/gate, per-position capture) followed by gdn_rollback_batch
+with a random per-slot trim.  Inputs are seeded synthetic data already resident in HBM; input
+sets rotate so the 128 MiB state never sits in the 256 MB Infinity Cache between its uses.
+
+Prints one JSON line: tokens/s (value), the verify kernel's achieved HBM bandwidth against the
+8 TB/s peak (roofline, timed with HIP events on the launch stream over the timed region), and
+the CPU oracle's throughput on a bounded sample (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN verify tokens/s (64 slots, K+1=16) + achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_multi_slot_verify.json")
+VERIFY_SRC = os.path.join(ROOT, "gated_deltanet_linear_verify_amd", "csrc", "gdn_verify.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(n_units: int):
+    """HBM bytes per verify launch from the committed rocprofv3 counter summary, or None when
+    the summary is missing or was taken from a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_digest(VERIFY_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(shape, inp, target_s: float = 10.0) -> dict:
+    """The fp64 oracle (test infrastructure, untuned) on the same workload: every (slot, value
+    head) unit with capture, repeated until about target_s seconds of host time; the median
+    repetition is reported."""
+    from oracle import ref
+
+    threads = ref.max_threads()
+    times = []
+    t_all = time.perf_counter()
+    while time.perf_counter() - t_all < target_s or len(times) < 3:
+        t0 = time.perf_counter()
+        ref.verify_units(shape, inp)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": shape.n_batch * shape.n_tok / med, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole call ({shape.n_batch} slots x {shape.n_vh} value heads x "
+                      f"{shape.n_tok} tokens, fp64, with capture), {len(times)} repetitions in "
+                      f"{sum(times):.1f} s, median {med * 1e3:.0f} ms"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="rotating input/state sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU code (got --gpus "
+              f"{args.gpus}); sharding is described in DESIGN.md", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from gated_deltanet_linear_verify_amd import bytemodel, device, gdn
+    from gated_deltanet_linear_verify_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    gdn.lib()
+    torch.cuda.set_device(0)
+    shape = W.MULTI_SLOT_VERIFY
+    B, T = shape.n_batch, shape.n_tok
+
+    log(f"[bench] allocating {args.sets} input sets + capture for {W.describe(shape)}")
+    sets = []
+    base = None
+    for i in range(args.sets):
+        inp = W.make_inputs(shape, seed=i)
+        if base is None:
+            base = inp
+            d = device.upload(shape, inp, fill_capture=0.0)
+        else:
+            d = device.upload(shape, inp, capture=False)
+            # one capture buffer, re-described for this set's state (rollback restores into it)
+            d["cap_ssm"], d["cap_conv"] = sets[0]["cap_ssm"], sets[0]["cap_conv"]
+            d["capture"] = gdn.Capture(d["dims"], d["cap_ssm"], d["cap_conv"], d["state"],
+                                       d["conv_state"], T, gdn.GDN_CHAIN)
+        acc = (T - 1 - inp["trims"]).astype(np.int32)
+        d["accepted"] = torch.from_numpy(acc).cuda()
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+
+    def step(i: int, ev=None):
+        d = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        device.verify(d, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        gdn.gdn_rollback_batch(d["capture"], d["slot_ids"], d["accepted"], B, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    verify_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = total_ms / args.steps
+    v_avg = sum(verify_ms) / len(verify_ms)
+    vb = bytemodel.verify_bytes(shape)
+    rb = bytemodel.rollback_bytes(shape, B)
+    achieved = vb / (v_avg * 1e-3) / 1e9
+    traffic = measured_traffic(B * shape.n_vh)
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us), "
+        f"verify {v_avg * 1e3:.1f} us avg (p10 {np.percentile(verify_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(verify_ms, 90) * 1e3:.1f}) -> {achieved:.0f} GB/s; "
+        f"step {(vb + rb) / (ms_step * 1e-3) / 1e9:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": B * T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "multi_slot_verify", "slots": B, "tokens_per_slot": T,
+                   "key_heads": shape.n_kh, "value_heads": shape.n_vh, "head_dim": shape.d_k,
+                   "activations": "bf16", "state_and_capture": "f32",
+                   "step": "gdn_verify + gdn_rollback_batch", "rotating_sets": args.sets},
+        "hbm_gbps_step": (vb + rb) / (ms_step * 1e-3) / 1e9,
+        "roofline": {"kernel": "verify_chain_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": vb,
+                     "avg_launch_us": v_avg * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(shape, base)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

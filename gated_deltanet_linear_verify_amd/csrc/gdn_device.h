@@ -1,0 +1,66 @@
+// gdn_device.h - device helpers shared by the libgdn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------------------------
+// bf16 <-> f32.  bf16 is the top half of an f32; f32 -> bf16 rounds to nearest, ties to even.
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_act(const void *p, size_t i)
+{
+    if constexpr (BF16)
+        return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+    else
+        return static_cast<const float *>(p)[i];
+}
+
+// ---------------------------------------------------------------------------------------------
+// Cross-lane sums inside a row of 16 lanes with DPP (no LDS traffic):
+//   quad_perm [1,0,3,2] and [2,3,0,1] give every lane its quad's sum, row_ror 4 and row_ror 8
+//   then fold the four quads of the row.  All 16 lanes end with the row total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_mov<0x124>(x);  // row_ror:4
+    x += dpp_mov<0x128>(x);  // row_ror:8
+    return x;
+}
+
+// Sum over the whole 64-lane wave (prologue use only).
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x = row16_sum(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+}  // namespace gdn

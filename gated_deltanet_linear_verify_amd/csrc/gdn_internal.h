@@ -1,0 +1,55 @@
+// gdn_internal.h - launch interface between the C ABI (gdn_abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kTokenTile = 16;  // tokens per LDS tile in the verify kernels
+
+struct VerifyArgs {
+    int32_t n_kh, n_vh, d, n_pool, T, t_cap, C;
+    float eps;
+    float *state;
+    float *conv_state;
+    const void *qkv, *z, *alpha, *beta;
+    const float *A_log, *dt_bias, *conv_w, *norm_w;
+    float *cap_ssm;   // NULL: no capture
+    float *cap_conv;
+    void *out;
+    const int32_t *slot_ids;
+    const int32_t *parent;  // tree only
+    int32_t n_batch;
+};
+
+struct LaunchCfg {
+    bool act_bf16, out_bf16, qk_norm;
+};
+
+// Chain verify: grid B * H_k workgroups of (H_v/H_k) * waves_per_head(d) waves.
+hipError_t launch_verify_chain(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream);
+// Tree verify: grid B * H_v workgroups.
+hipError_t launch_verify_tree(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream);
+
+int verify_waves_per_head(int d);
+size_t verify_chain_lds_bytes(int d, int ratio);
+size_t verify_tree_lds_bytes(int d, int T);
+
+struct RollbackArgs {
+    float *state, *conv_state;
+    const float *cap_ssm, *cap_conv;
+    int32_t n_pool, t_cap, mode;
+    size_t ssm_elems;   // H_v * d_v * d_k floats per slot and position
+    size_t conv_elems;  // 3 * C floats
+    size_t C;
+    const int32_t *slots;  // device array, or NULL: use slot0 / idx0
+    const int32_t *idx;
+    int32_t slot0, idx0, n;
+};
+hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream);
+
+hipError_t launch_fill_zero(float *p, size_t n, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,79 @@
+// gdn_rollback.hip - restore a slot's recurrent and conv state from the per-position capture.
+//
+// The state after accepted position a is capture element a (lucebox-hub internal.h, struct
+// DeltaNetCapture: rollback reads offset (commit_n - 1)); the conv state is rows
+// [a+1 .. a+3] of the chain capture window (same struct: slice [commit_n .. commit_n+kernel-2])
+// or the per-node 3-row record of a tree capture.  hf2q qwen35_target.rs, rollback_la_to copies
+// capture[accepted_idx] back into the live recurrent and conv buffers.  Both are bitwise copies:
+// one flat float4 stream per entry, HBM bound.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+__global__ __launch_bounds__(256) void rollback_kernel(RollbackArgs a)
+{
+    const int n = blockIdx.y;
+    const int slot = a.slots ? a.slots[n] : a.slot0;
+    const int idx = a.idx ? a.idx[n] : a.idx0;
+    if (slot < 0 || slot >= a.n_pool || idx < 0 || idx >= a.t_cap) return;  // uniform per block
+
+    const f4 *src_s = reinterpret_cast<const f4 *>(a.cap_ssm + ((size_t)slot * a.t_cap + idx) * a.ssm_elems);
+    f4 *dst_s = reinterpret_cast<f4 *>(a.state + (size_t)slot * a.ssm_elems);
+    const float *csrc = a.mode == 0 ? a.cap_conv + ((size_t)slot * (3 + a.t_cap) + idx + 1) * a.C
+                                    : a.cap_conv + ((size_t)slot * a.t_cap + idx) * a.conv_elems;
+    const f4 *src_c = reinterpret_cast<const f4 *>(csrc);
+    f4 *dst_c = reinterpret_cast<f4 *>(a.conv_state + (size_t)slot * a.conv_elems);
+
+    const size_t ns = a.ssm_elems / 4, nc = a.conv_elems / 4;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < ns; i += 4 * stride) {
+        const f4 v0 = src_s[i], v1 = src_s[i + stride], v2 = src_s[i + 2 * stride], v3 = src_s[i + 3 * stride];
+        dst_s[i] = v0;
+        dst_s[i + stride] = v1;
+        dst_s[i + 2 * stride] = v2;
+        dst_s[i + 3 * stride] = v3;
+    }
+    for (; i < ns; i += stride) dst_s[i] = src_s[i];
+    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < nc; j += stride) dst_c[j] = src_c[j];
+}
+
+hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream)
+{
+    if (a.n <= 0) return hipSuccess;
+    const size_t vec = (a.ssm_elems + a.conv_elems) / 4;
+    size_t blocks = (vec + 256 * 4 - 1) / (256 * 4);
+    if (blocks > 512) blocks = 512;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(rollback_kernel, dim3((unsigned)blocks, (unsigned)a.n), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(f4 *p, size_t n4)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) p[i] = f4{0.f, 0.f, 0.f, 0.f};
+}
+
+__global__ void fill_zero_tail_kernel(float *p, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+// Zero n floats at p (p 16-byte aligned).  A kernel rather than hipMemsetAsync so the call can
+// sit inside a captured graph.
+hipError_t launch_fill_zero(float *p, size_t n, hipStream_t stream)
+{
+    const size_t n4 = n / 4;
+    if (n4) {
+        size_t blocks = (n4 + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<f4 *>(p), n4);
+    }
+    if (n % 4) hipLaunchKernelGGL(fill_zero_tail_kernel, dim3(1), dim3(64), 0, stream, p + n4 * 4, n % 4);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

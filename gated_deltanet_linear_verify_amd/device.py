@@ -1,0 +1,74 @@
+"""Device buffers for the verify path: torch owns the memory, libgdn computes.
+
+Plumbing only: uploads the seeded inputs of ``workloads`` in the storage dtypes of include/gdn.h
+and allocates outputs, capture buffers and workspaces with the documented shapes.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import gdn
+from .workloads import BF16, Shape
+
+
+def act_torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def upload(shape: Shape, inp: dict, *, device: str = "cuda", t_cap: Optional[int] = None,
+           mode: int = gdn.GDN_CHAIN, capture: bool = True, fill_capture: float = float("nan"),
+           flags: int = 0, eps: float = 1e-6) -> dict:
+    """Device tensors for one call plus the ctypes dims / capture descriptors."""
+    act = act_torch_dtype(shape.act_dtype)
+    outd = act_torch_dtype(shape.out_dtype)
+    B, T, P = shape.n_batch, shape.n_tok, shape.n_pool
+    Hv, dv, dk, C = shape.n_vh, shape.d_v, shape.d_k, shape.conv_channels
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    d = {
+        "qkv": f32(inp["qkv"]).to(act).contiguous(),
+        "z": f32(inp["z"]).to(act).contiguous(),
+        "alpha": f32(inp["alpha"]).to(act).contiguous(),
+        "beta": f32(inp["beta"]).to(act).contiguous(),
+        "A_log": f32(inp["A_log"]),
+        "dt_bias": f32(inp["dt_bias"]),
+        "conv_w": f32(inp["conv_w"]),
+        "norm_w": f32(inp["norm_w"]),
+        "state": f32(inp["state"]),
+        "conv_state": f32(inp["conv_state"]),
+        "slot_ids": torch.from_numpy(np.ascontiguousarray(inp["slot_ids"], dtype=np.int32)).to(device),
+        "out": torch.empty((B, T, Hv, dv), dtype=outd, device=device),
+    }
+    if "parent" in inp:
+        d["parent"] = torch.from_numpy(np.ascontiguousarray(inp["parent"], dtype=np.int32)).to(device)
+    dims = gdn.make_dims(shape, flags=flags, eps=eps)
+    d["dims"] = dims
+    if capture:
+        tc = T if t_cap is None else t_cap
+        d["cap_ssm"] = torch.full((P, tc, Hv, dv, dk), fill_capture, dtype=torch.float32, device=device)
+        conv_shape = (P, 3 + tc, C) if mode == gdn.GDN_CHAIN else (P, tc, 3, C)
+        d["cap_conv"] = torch.full(conv_shape, fill_capture, dtype=torch.float32, device=device)
+        d["capture"] = gdn.Capture(dims, d["cap_ssm"], d["cap_conv"], d["state"], d["conv_state"],
+                                   tc, mode)
+    return d
+
+
+def verify(d: dict, n_batch: Optional[int] = None, stream=None, with_capture: bool = True) -> None:
+    """gdn_verify over every token of the uploaded inputs (qkv is [B][T][C], so n_tok = T);
+    ``n_batch`` may cut the batch to a prefix."""
+    T = d["qkv"].shape[1]
+    B = d["qkv"].shape[0] if n_batch is None else n_batch
+    gdn.gdn_verify(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"], d["beta"],
+                   d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"],
+                   d.get("capture") if with_capture else None, d["out"], T, d["slot_ids"], B,
+                   stream)
+
+
+def verify_tree(d: dict, stream=None) -> None:
+    B, T = d["parent"].shape
+    gdn.gdn_verify_tree(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"],
+                        d["beta"], d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], d["parent"],
+                        d["capture"], d["out"], T, d["slot_ids"], B, stream)

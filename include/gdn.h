@@ -1,0 +1,204 @@
+/*
+ * gdn.h - C ABI of libgdn.so: the Gated DeltaNet speculative-decode verify path on AMD MI355X
+ * (gfx950), as hand-written HIP kernels.
+ *
+ * What is computed (per slot s and value head h; the recurrent layer of a Qwen3.5-style hybrid
+ * model, "GATED DELTANET block" in lucebox-hub server/src/internal.h, struct TargetLayer):
+ *
+ *   xext      = concat(conv_state[s] (3 rows, oldest first), qkv rows of the new tokens)
+ *   xhat[t]   = sum_j conv_w[c][j] * xext[t + j]          depthwise causal conv, kernel 4, no bias
+ *   q, k, v   = the q / k channels of key head h / (H_v / H_k) and the v channels of head h
+ *   g_t       = -exp(A_log[h]) * softplus(alpha_t + dt_bias[h]),   rho_t = exp(g_t)
+ *   S_t       = rho_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *   o_t       = S_t q_t
+ *   out_t     = o_t / sqrt(mean(o_t^2) + eps) * norm_w * z_t * sigmoid(z_t)
+ *
+ * (gated delta rule: Yang, Kautz & Hatamizadeh, "Gated Delta Networks", 2024; the parameter
+ * tensors ssm_conv1d, ssm_a, ssm_dt_bias, ssm_beta, ssm_alpha, ssm_norm and the z projection
+ * are listed in lucebox-hub internal.h, struct TargetLayer; rms_eps in struct TargetWeights.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Layouts are row-major, last index fastest.  C = 2*H_k*d_k + H_v*d_v conv channels, in
+ *   blocks q [H_k][d_k] | k [H_k][d_k] | v [H_v][d_v].
+ *     qkv        act   [B][T][C]           z, out  act/out [B][T][H_v][d_v]
+ *     alpha,beta act   [B][T][H_v]         (beta already passed through its sigmoid)
+ *     state      f32   [P][H_v][d_v][d_k]  S[i][j]: row i = value index, column j = key index
+ *     conv_state f32   [P][3][C]           oldest row first
+ *     conv_w     f32   [C][4]              tap 3 multiplies the current token
+ *     norm_w     f32   [d_v] (shared by all heads);  A_log, dt_bias  f32 [H_v]
+ *     capture->ssm   f32 [P][t_cap][H_v][d_v][d_k]  element t = state after token t
+ *     capture->conv  f32 chain: [P][3 + t_cap][C]  the whole conv input window xext
+ *                        tree:  [P][t_cap][3][C]   the 3-row conv state after each node
+ *   (lucebox-hub internal.h, struct TargetCache, ssm_state / conv_state / ssm_intermediate /
+ *   conv_input_cache comments; the pages give ggml shapes, the orientation here is a choice.)
+ * - Every pointer is caller-owned device memory (the model does not own its cache: hf2q
+ *   qwen35_target.rs, Qwen35DFlashTarget).  The library allocates nothing, keeps no device
+ *   state, and only enqueues work on `stream` (a hipStream_t, NULL = the null stream); calls
+ *   return before the GPU finishes.
+ * - Batch entry b uses slot slot_ids[b] (device int32 [B]).  Slots within one call must be
+ *   distinct.  Entries whose slot is outside [0, n_pool) are skipped by the kernels (nothing is
+ *   read or written for them); GDN_F_CHECK_INDICES makes the host copy the index arrays back
+ *   (synchronously) and fail with GDN_ERR_RANGE instead.
+ * - Return value: GDN_OK or an error code.  On error nothing has been enqueued and nothing is
+ *   mutated; gdn_last_error() returns a thread-local description (lucebox-hub internal.h keeps
+ *   one error sink, set_last_error).  GDN_ERR_HIP reports a failed launch.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_ARG = 1,    /* null pointer or inconsistent argument */
+    GDN_ERR_SHAPE = 2,  /* unsupported or inconsistent dimensions */
+    GDN_ERR_DTYPE = 3,  /* unsupported activation / output dtype */
+    GDN_ERR_RANGE = 4,  /* slot, accepted index, token count or parent out of range */
+    GDN_ERR_HIP = 5     /* the HIP runtime reported an error */
+};
+
+enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
+
+enum gdn_capture_mode { GDN_CHAIN = 0, GDN_TREE = 1 };
+
+/* SiLU after the conv on q, k and v; q and k scaled to unit length (x / sqrt(sum x^2 + 1e-6));
+ * q scaled by d_k^-1/2.  Off by default: the recurrence as stated has none of these. */
+#define GDN_F_QK_NORM_SILU 0x1u
+/* Copy device index arrays (slot_ids, parent, rollback slots / indices) to the host and
+ * validate them before launching.  Synchronises with `stream`. */
+#define GDN_F_CHECK_INDICES 0x2u
+
+typedef struct gdn_dims {
+    int32_t n_kh;      /* key heads H_k */
+    int32_t n_vh;      /* value heads H_v, a multiple of H_k */
+    int32_t d_k;       /* key head dim (64 or 128) */
+    int32_t d_v;       /* value head dim, equal to d_k */
+    int32_t d_conv;    /* conv kernel, must be 4 */
+    int32_t n_pool;    /* P: slots in the state pool */
+    int32_t act_dtype; /* gdn_dtype of qkv, z, alpha, beta */
+    int32_t out_dtype; /* gdn_dtype of out */
+    uint32_t flags;    /* GDN_F_* */
+    float eps;         /* RMS-norm epsilon (1e-6 in the pages' model) */
+} gdn_dims;
+
+/* Persistent per-position capture written by a verify and read by rollback.  `state` and
+ * `conv_state` name the buffers that rollback restores into.  lucebox-hub internal.h, struct
+ * DeltaNetCapture ("persistent cache buffers ... not managed by the per-call allocator"). */
+typedef struct gdn_capture {
+    gdn_dims dims;
+    float *ssm;        /* [P][t_cap][H_v][d_v][d_k] */
+    float *conv;       /* chain [P][3 + t_cap][C] or tree [P][t_cap][3][C] */
+    float *state;      /* [P][H_v][d_v][d_k] */
+    float *conv_state; /* [P][3][C] */
+    int32_t t_cap;     /* capacity in positions (>= n_tok of every verify that writes it) */
+    int32_t mode;      /* gdn_capture_mode */
+} gdn_capture;
+
+/*
+ * Chain verify of n_tok tokens for n_batch slots (the K+1 drafted tokens of a speculative
+ * round).  For each batch entry b and value head h: conv, gate, delta-rule update, readout and
+ * norm/gate epilogue for every token, in order.  state[slot] and conv_state[slot] are advanced
+ * to after the last token (so trim 0 needs no rollback: hf2q qwen35_target.rs, rollback_kv
+ * returns at once for trim 0).  When `capture` is not NULL (mode GDN_CHAIN, t_cap >= n_tok), the
+ * state after every token t goes to capture->ssm[slot][t] and the whole conv input window to
+ * capture->conv[slot][0 .. 3+n_tok) (lucebox-hub internal.h, struct TargetCache: ssm_intermediate
+ * and conv_input_cache).  capture == NULL is plain decode with no rollback support.
+ *   qkv, z, alpha, beta: act_dtype;  out: out_dtype [n_batch][n_tok][H_v][d_v].
+ *   1 <= n_tok;  1 <= n_batch <= n_pool.
+ */
+int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
+               const void *z, const void *alpha, const void *beta, const float *A_log,
+               const float *dt_bias, const float *conv_w, const float *norm_w,
+               const gdn_capture *capture, void *out, int32_t n_tok, const int32_t *slot_ids,
+               int32_t n_batch, void *stream);
+
+/*
+ * Tree verify: n_tok draft-tree nodes per batch entry, node i hanging off parent[b][i]
+ * (device int32 [n_batch][n_tok]; -1 = starts from the committed state, else 0 <= parent < i;
+ * node 0 is the root and must have parent -1).  lucebox-hub internal.h, QwenGraphInputs::
+ * parent_ids ("tree mode when non-null"); create_target_cache sizes the capture for
+ * 1 + tree budget positions.  Node i's state is its parent's state advanced by node i's token;
+ * its conv window runs along the ancestor path, filled from conv_state above the root.  Writes
+ * out for every node, capture->ssm[slot][i] (state after node i) and capture->conv[slot][i]
+ * (3-row conv state after node i; capture->mode must be GDN_TREE, t_cap >= n_tok).  state and
+ * conv_state are NOT advanced: the caller commits a node with gdn_rollback.  Nodes with a
+ * malformed parent are treated as children of the committed state unless GDN_F_CHECK_INDICES
+ * is set (then GDN_ERR_RANGE).
+ */
+int gdn_verify_tree(const gdn_dims *dims, const float *state, const float *conv_state,
+                    const void *qkv, const void *z, const void *alpha, const void *beta,
+                    const float *A_log, const float *dt_bias, const float *conv_w,
+                    const float *norm_w, const int32_t *parent, const gdn_capture *capture,
+                    void *out, int32_t n_tok, const int32_t *slot_ids, int32_t n_batch,
+                    void *stream);
+
+/*
+ * Restore slot `slot` to the state after accepted position `accepted_idx` (host ints):
+ *   capture->state[slot]      <- capture->ssm[slot][accepted_idx]            (bitwise copy)
+ *   capture->conv_state[slot] <- capture->conv[slot][accepted_idx+1 .. +3]   (chain)
+ *                                capture->conv[slot][accepted_idx]           (tree)
+ * Only this slot is touched (hf2q qwen35_target.rs, rollback_kv "mutates ONLY" the slot;
+ * lucebox-hub internal.h, DeltaNetCapture: offset (commit_n-1) and conv slice
+ * [commit_n .. commit_n+kernel-2]).  Errors: slot not in [0, n_pool) or accepted_idx not in
+ * [0, t_cap) -> GDN_ERR_RANGE (the pages skip silently; here the caller hears of it).
+ */
+int gdn_rollback(const gdn_capture *capture, int32_t slot, int32_t accepted_idx, void *stream);
+
+/*
+ * Batched rollback of n entries in one launch: slots and accepted_idx are device int32 [n].
+ * Entries with an out-of-range slot or index are skipped (GDN_F_CHECK_INDICES in
+ * capture->dims.flags: validated on the host, GDN_ERR_RANGE).  Slots must be distinct.
+ */
+int gdn_rollback_batch(const gdn_capture *capture, const int32_t *slots,
+                       const int32_t *accepted_idx, int32_t n, void *stream);
+
+/*
+ * The pages' trim form (hf2q qwen35_target.rs, rollback_kv): n_tok positions were verified,
+ * the last `trim` are rejected.  trim == 0 -> GDN_OK with nothing enqueued; trim >= n_tok ->
+ * GDN_ERR_RANGE; else gdn_rollback(capture, slot, n_tok - 1 - trim).
+ */
+int gdn_rollback_trim(const gdn_capture *capture, int32_t slot, int32_t trim, int32_t n_tok,
+                      void *stream);
+
+/*
+ * Chunked prefill of n_tok tokens into slot `slot` (no capture: a prefill-only cache skips the
+ * rollback tensors, lucebox-hub internal.h, create_target_cache prefill_only).  Same result as
+ * gdn_verify with capture == NULL, computed in chunks of 64 tokens in the WY/UT form with the
+ * dense intra-chunk products on MFMA.  workspace: device memory of at least
+ * gdn_prefill_workspace_bytes(dims, n_tok) bytes, 256-byte aligned.
+ *   qkv [n_tok][C], z and out [n_tok][H_v][d_v], alpha and beta [n_tok][H_v].
+ */
+int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
+                const void *z, const void *alpha, const void *beta, const float *A_log,
+                const float *dt_bias, const float *conv_w, const float *norm_w, void *out,
+                int32_t n_tok, int32_t slot, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes gdn_prefill needs for n_tok tokens (0 on invalid dims). */
+size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t n_tok);
+
+/* Bytes of capture->ssm for t_cap positions; *conv_bytes (if not NULL) receives the bytes of
+ * capture->conv for the mode (0 on invalid dims). */
+size_t gdn_capture_bytes(const gdn_dims *dims, int32_t t_cap, int32_t mode, size_t *conv_bytes);
+
+/* Zero the recurrent state and conv state of one slot (lucebox-hub internal.h,
+ * reset_recurrent_state: zero SSM + conv state between requests). */
+int gdn_reset(const gdn_dims *dims, float *state, float *conv_state, int32_t slot,
+              void *stream);
+
+/* Thread-local description of the last error of this thread ("" after success). */
+const char *gdn_last_error(void);
+
+/* Library version string. */
+const char *gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

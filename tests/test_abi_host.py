@@ -1,0 +1,110 @@
+"""The C ABI on the host: the library loads, exports every symbol gdn.h declares, and rejects
+bad arguments before touching the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_linear_verify_amd import gdn
+from gated_deltanet_linear_verify_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.skip("libgdn.so not built")
+    return gdn.lib()
+
+
+def test_header_declarations_are_all_exported():
+    L = _lib_or_skip()
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    declared = set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", hdr))
+    assert declared == set(gdn.EXPORTS), declared ^ set(gdn.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_empty_error():
+    _lib_or_skip()
+    assert "gfx950" in gdn.version()
+
+
+FAKE = ctypes.c_void_p(0x1000)  # an aligned non-null address never dereferenced (rejected first)
+
+
+def _dims(**kw):
+    d = gdn.make_dims(W.SINGLE_SLOT_VERIFY)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"d_conv": 3}, gdn.GDN_ERR_SHAPE),
+    ({"d_k": 96, "d_v": 96}, gdn.GDN_ERR_SHAPE),
+    ({"d_v": 64}, gdn.GDN_ERR_SHAPE),
+    ({"n_vh": 24, "n_kh": 16}, gdn.GDN_ERR_SHAPE),
+    ({"n_vh": 80, "n_kh": 16}, gdn.GDN_ERR_SHAPE),
+    ({"n_pool": 0}, gdn.GDN_ERR_SHAPE),
+    ({"act_dtype": 7}, gdn.GDN_ERR_DTYPE),
+    ({"flags": 0x100}, gdn.GDN_ERR_ARG),
+    ({"eps": -1.0}, gdn.GDN_ERR_ARG),
+])
+def test_verify_rejects_bad_dims(kw, code):
+    L = _lib_or_skip()
+    d = _dims(**kw)
+    rc = L.gdn_verify(ctypes.byref(d), *([FAKE] * 10), None, FAKE, 4, FAKE, 1, None)
+    assert rc == code, gdn.last_error()
+    assert gdn.last_error()
+
+
+def test_verify_rejects_null_and_range_before_launch():
+    L = _lib_or_skip()
+    d = _dims()
+    args = [FAKE] * 10
+    assert L.gdn_verify(ctypes.byref(d), *args, None, None, 4, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    assert L.gdn_verify(ctypes.byref(d), *args, None, FAKE, 0, FAKE, 1, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_verify(ctypes.byref(d), *args, None, FAKE, 4, FAKE, 2, None) == gdn.GDN_ERR_RANGE
+    mis = ctypes.c_void_p(0x1004)
+    assert L.gdn_verify(ctypes.byref(d), mis, *args[1:], None, FAKE, 4, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    # capture too small for n_tok
+    cap = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 3, gdn.GDN_CHAIN)
+    assert L.gdn_verify(ctypes.byref(d), *args, ctypes.byref(cap), FAKE, 4, FAKE, 1, None) == gdn.GDN_ERR_RANGE
+    cap = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 16, gdn.GDN_TREE)
+    assert L.gdn_verify(ctypes.byref(d), *args, ctypes.byref(cap), FAKE, 4, FAKE, 1, None) == gdn.GDN_ERR_ARG
+
+
+def test_rollback_validation():
+    L = _lib_or_skip()
+    d = _dims(n_pool=4)
+    cap = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 16, gdn.GDN_CHAIN)
+    assert L.gdn_rollback(ctypes.byref(cap), 4, 0, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback(ctypes.byref(cap), -1, 0, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback(ctypes.byref(cap), 0, 16, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback(ctypes.byref(cap), 0, -1, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback(None, 0, 0, None) == gdn.GDN_ERR_ARG
+    # trim form: trim 0 is a no-op that enqueues nothing; trim >= n_tok is a range error
+    assert L.gdn_rollback_trim(ctypes.byref(cap), 0, 0, 16, None) == gdn.GDN_OK
+    assert L.gdn_rollback_trim(ctypes.byref(cap), 0, 16, 16, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback_trim(ctypes.byref(cap), 0, 3, 17, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback_batch(ctypes.byref(cap), None, None, 0, None) == gdn.GDN_OK
+    assert L.gdn_rollback_batch(ctypes.byref(cap), None, None, 2, None) == gdn.GDN_ERR_ARG
+    assert L.gdn_rollback_batch(ctypes.byref(cap), FAKE, FAKE, 5, None) == gdn.GDN_ERR_RANGE
+    bad = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 16, 5)
+    assert L.gdn_rollback(ctypes.byref(bad), 0, 0, None) == gdn.GDN_ERR_ARG
+
+
+def test_capture_bytes_match_layout():
+    _lib_or_skip()
+    s = W.MULTI_SLOT_VERIFY
+    d = gdn.make_dims(s)
+    ssm, conv = gdn.capture_bytes(d, 16, gdn.GDN_CHAIN)
+    assert ssm == 4 * 64 * 16 * 32 * 128 * 128 == 2 * 1024 ** 3
+    assert conv == 4 * 64 * (3 + 16) * 8192
+    ssm_t, conv_t = gdn.capture_bytes(d, 64, gdn.GDN_TREE)
+    assert conv_t == 4 * 64 * 64 * 3 * 8192
+    assert gdn.capture_bytes(d, 0, gdn.GDN_CHAIN) == (0, 0)

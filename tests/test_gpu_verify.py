@@ -1,0 +1,303 @@
+"""GPU parity of chain verify and rollback against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+from gated_deltanet_linear_verify_amd import workloads as W
+from oracle import ref
+from tests.gpu_util import out_err, rel_err, say, to_np, tol_for
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_linear_verify_amd import gdn
+    gdn.lib()  # fail loudly if the HIP library is missing
+
+
+def _dev():
+    from gated_deltanet_linear_verify_amd import device
+    return device
+
+
+def _gdn():
+    from gated_deltanet_linear_verify_amd import gdn
+    return gdn
+
+
+def _check_pool(shape, inp, d, tol, *, flags=0, check_capture=True):
+    """Compare every output of a small verify call with the oracle."""
+    o = ref.verify_pool(shape, inp, flags=flags)
+    st = to_np(d["state"])
+    out = to_np(d["out"])
+    worst = {"state": 0.0, "cap": 0.0, "out": 0.0}
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        for h in range(shape.n_vh):
+            worst["state"] = max(worst["state"], rel_err(st[s, h], o["state"][s, h]))
+            worst["out"] = max(worst["out"], out_err(shape, out[b, :, h], o["out"][b, :, h]))
+    if check_capture:
+        cap = to_np(d["cap_ssm"])
+        for b in range(shape.n_batch):
+            s = int(inp["slot_ids"][b])
+            for h in range(shape.n_vh):
+                for t in range(shape.n_tok):
+                    worst["cap"] = max(worst["cap"], rel_err(cap[s, t, h], o["cap_ssm"][s, t, h]))
+        # conv window and conv state are copies: bit exact
+        cc = to_np(d["cap_conv"])
+        for b in range(shape.n_batch):
+            s = int(inp["slot_ids"][b])
+            np.testing.assert_array_equal(cc[s, :3 + shape.n_tok], o["cap_conv"][s])
+    np.testing.assert_array_equal(to_np(d["conv_state"]), o["conv_state"])
+    # slots not in the batch are untouched, bit for bit
+    used = set(int(x) for x in inp["slot_ids"])
+    for s in range(shape.n_pool):
+        if s not in used:
+            np.testing.assert_array_equal(st[s], inp["state"][s])
+    say(f"  {W.describe(shape)} worst rel err {worst} (tol {tol})")
+    for k, v in worst.items():
+        assert v <= tol, (k, v, tol)
+    return o
+
+
+CASES = {
+    # name: (shape, flags)
+    "tiny_verify": (W.TINY_VERIFY, 0),
+    "single_slot_verify": (W.SINGLE_SLOT_VERIFY, 0),
+    "ragged_three_tiles": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=37, n_pool=3, n_batch=2), 0),
+    "one_token": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=1, n_pool=2, n_batch=2), 0),
+    "two_tokens_conv_from_state": (W.shape_with(W.TINY_VERIFY, n_tok=2, n_pool=4, n_batch=3), 0),
+    "fp32_act_bf16_out": (W.shape_with(W.TINY_VERIFY, out_dtype=W.BF16, n_tok=17), 0),
+    "bf16_act_fp32_out": (W.shape_with(W.SINGLE_SLOT_VERIFY, out_dtype=W.F32, n_vh=16, n_kh=16), 0),
+    "gqa4_d128": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_kh=4, n_vh=16, n_tok=9), 0),
+    "gqa8_d64": (W.shape_with(W.TINY_VERIFY, n_kh=1, n_vh=8, n_tok=5), 0),
+    "qk_norm_silu_flag": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=12), 1),
+    "qk_norm_silu_fp32": (W.shape_with(W.TINY_VERIFY, n_tok=20), 1),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_verify_parity(name):
+    shape, flags = CASES[name]
+    say(f"[verify parity] {name}")
+    inp = W.make_inputs(shape, 0)
+    dev = _dev()
+    gdn = _gdn()
+    d = dev.upload(shape, inp, flags=(gdn.GDN_F_QK_NORM_SILU if flags else 0))
+    dev.verify(d)
+    torch.cuda.synchronize()
+    _check_pool(shape, inp, d, tol_for(shape), flags=flags)
+
+
+def test_verify_without_capture_matches_capture_path():
+    shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=2, n_batch=2, n_tok=7)
+    inp = W.make_inputs(shape, 3)
+    dev = _dev()
+    a = dev.upload(shape, inp)
+    b = dev.upload(shape, inp, capture=False)
+    dev.verify(a)
+    dev.verify(b, with_capture=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a["state"], b["state"])
+    assert torch.equal(a["conv_state"], b["conv_state"])
+    assert torch.equal(a["out"], b["out"])
+
+
+def test_verify_is_deterministic():
+    shape = W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=8, n_batch=8)
+    inp = W.make_inputs(shape, 4)
+    dev = _dev()
+    a = dev.upload(shape, inp)
+    b = dev.upload(shape, inp)
+    dev.verify(a)
+    dev.verify(b)
+    torch.cuda.synchronize()
+    for k in ("state", "conv_state", "out", "cap_ssm", "cap_conv"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_beta_zero_no_decay_is_identity_on_gpu():
+    shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=5)
+    inp = W.make_inputs(shape, 5)
+    inp["beta"][:] = 0.0
+    inp["alpha"][:] = -1e30
+    dev = _dev()
+    d = dev.upload(shape, inp)
+    dev.verify(d)
+    torch.cuda.synchronize()
+    st = to_np(d["state"])
+    np.testing.assert_array_equal(st, inp["state"])
+    cap = to_np(d["cap_ssm"])
+    for t in range(shape.n_tok):
+        np.testing.assert_array_equal(cap[:, t], inp["state"])
+
+
+@pytest.mark.parametrize("shape_name", ["tiny_verify", "single_slot_verify"])
+def test_rollback_equals_shorter_verify(shape_name):
+    """verify(T) + rollback(a) leaves bit for bit what verify(a+1) leaves, for every a; and
+    both match the oracle's state after a+1 tokens."""
+    base = W.WORKLOADS[shape_name]
+    shape = W.shape_with(base, n_pool=3, n_batch=2)
+    inp = W.make_inputs(shape, 6)
+    dev = _dev()
+    gdn = _gdn()
+    full = dev.upload(shape, inp)
+    dev.verify(full)
+    torch.cuda.synchronize()
+    cap_ssm = full["cap_ssm"].clone()
+    cap_conv = full["cap_conv"].clone()
+    tol = tol_for(shape)
+    for a in range(shape.n_tok):
+        say(f"[rollback] {shape_name} a={a}")
+        short_shape = W.shape_with(shape, n_tok=a + 1)
+        sinp = dict(inp)
+        for k in ("qkv", "z", "alpha", "beta"):
+            sinp[k] = np.ascontiguousarray(inp[k][:, :a + 1])
+        short = dev.upload(short_shape, sinp)
+        dev.verify(short)
+        # restore into a fresh copy of the full call's capture
+        rb = dev.upload(shape, inp)
+        rb["cap_ssm"].copy_(cap_ssm)
+        rb["cap_conv"].copy_(cap_conv)
+        for b in range(shape.n_batch):
+            gdn.gdn_rollback(rb["capture"], int(inp["slot_ids"][b]), a)
+        torch.cuda.synchronize()
+        assert torch.equal(rb["state"], short["state"])
+        assert torch.equal(rb["conv_state"], short["conv_state"])
+        o = ref.verify_pool(short_shape, sinp)
+        st = to_np(rb["state"])
+        for b in range(shape.n_batch):
+            s = int(inp["slot_ids"][b])
+            for h in range(shape.n_vh):
+                assert rel_err(st[s, h], o["state"][s, h]) <= tol
+
+
+def test_rollback_batch_and_trim_multi_slot():
+    """Per-slot random trims through the batched rollback == per-slot single rollbacks == the
+    capture element accepted_idx = K - trim, bit for bit."""
+    shape = W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=12, n_batch=10)
+    inp = W.make_inputs(shape, 7)
+    dev = _dev()
+    gdn = _gdn()
+    d = dev.upload(shape, inp)
+    dev.verify(d)
+    torch.cuda.synchronize()
+    K = shape.n_tok - 1
+    trims = inp["trims"]
+    acc = np.array([K - int(t) for t in trims], dtype=np.int32)
+    cap_ssm = to_np(d["cap_ssm"])
+    cap_conv = to_np(d["cap_conv"])
+    state_after_verify = to_np(d["state"])
+    slots_t = d["slot_ids"]
+    acc_t = torch.from_numpy(acc).cuda()
+    gdn.gdn_rollback_batch(d["capture"], slots_t, acc_t, shape.n_batch)
+    torch.cuda.synchronize()
+    st = to_np(d["state"])
+    cs = to_np(d["conv_state"])
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        np.testing.assert_array_equal(st[s], cap_ssm[s, acc[b]])
+        np.testing.assert_array_equal(cs[s], cap_conv[s, acc[b] + 1:acc[b] + 4])
+    # trim form on a second copy: trim 0 is a no-op, otherwise the same restore
+    e = dev.upload(shape, inp)
+    dev.verify(e)
+    for b in range(shape.n_batch):
+        gdn.gdn_rollback_trim(e["capture"], int(inp["slot_ids"][b]), int(trims[b]), shape.n_tok)
+    torch.cuda.synchronize()
+    st2 = to_np(e["state"])
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        if trims[b] == 0:
+            np.testing.assert_array_equal(st2[s], state_after_verify[s])
+        np.testing.assert_array_equal(st2[s], st[s])
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.gdn_rollback_trim(e["capture"], 0, shape.n_tok, shape.n_tok)
+    assert ei.value.code == gdn.GDN_ERR_RANGE
+
+
+def test_multi_slot_full_size_sampled():
+    """The 64-slot workload at full size, in the benchmark's launch configuration: sampled
+    (slot, head) units against the oracle, conv copies bit exact for every slot."""
+    shape = W.MULTI_SLOT_VERIFY
+    inp = W.make_inputs(shape, 0)
+    dev = _dev()
+    d = dev.upload(shape, inp)
+    dev.verify(d)
+    torch.cuda.synchronize()
+    units = ref.sample_units(shape, 24)
+    o = ref.verify_units(shape, inp, units)
+    st = to_np(d["state"])
+    out = to_np(d["out"])
+    cap = d["cap_ssm"]
+    worst = 0.0
+    for u in range(len(units[0])):
+        b, h = int(units[0][u]), int(units[1][u])
+        s = int(inp["slot_ids"][b])
+        worst = max(worst, rel_err(st[s, h], o["state"][u]), out_err(shape, out[b, :, h], o["y"][u]))
+        c = to_np(cap[s, :, h])
+        for t in range(shape.n_tok):
+            worst = max(worst, rel_err(c[t], o["cap"][u, t]))
+    say(f"  multi-slot sampled worst rel err {worst}")
+    assert worst <= tol_for(shape)
+    win = ref.conv_window(shape, inp)
+    cc = to_np(d["cap_conv"])
+    cs = to_np(d["conv_state"])
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        np.testing.assert_array_equal(cc[s], win[b])
+        np.testing.assert_array_equal(cs[s], win[b, -3:])
+
+
+def test_check_indices_rejects_bad_slots_without_mutation():
+    gdn = _gdn()
+    dev = _dev()
+    shape = W.shape_with(W.TINY_VERIFY, n_pool=4, n_batch=2)
+    inp = W.make_inputs(shape, 8)
+    for bad in ([1, 1], [0, 4], [-1, 2]):
+        inp2 = dict(inp)
+        inp2["slot_ids"] = np.array(bad, dtype=np.int32)
+        d = dev.upload(shape, inp2, flags=gdn.GDN_F_CHECK_INDICES)
+        before = d["state"].clone()
+        with pytest.raises(gdn.GdnError) as ei:
+            dev.verify(d)
+        assert ei.value.code == gdn.GDN_ERR_RANGE
+        torch.cuda.synchronize()
+        assert torch.equal(before, d["state"])
+
+
+def test_out_of_range_slot_is_skipped_by_the_kernel():
+    """Without the host check, an entry whose slot is outside the pool is skipped (its bounds
+    check in the kernel stops it before any access); the other entries are unaffected."""
+    dev = _dev()
+    shape = W.shape_with(W.TINY_VERIFY, n_pool=3, n_batch=2)
+    inp = W.make_inputs(shape, 9)
+    good = dev.upload(shape, inp)
+    dev.verify(good)
+    inp2 = dict(inp)
+    inp2["slot_ids"] = np.array([int(inp["slot_ids"][0]), 7], dtype=np.int32)
+    d = dev.upload(shape, inp2)
+    dev.verify(d)
+    torch.cuda.synchronize()
+    s0 = int(inp["slot_ids"][0])
+    assert torch.equal(d["state"][s0], good["state"][s0])
+    others = [s for s in range(3) if s != s0]
+    for s in others:
+        np.testing.assert_array_equal(to_np(d["state"][s]), inp["state"][s])
+
+
+def test_reset_zeroes_one_slot():
+    gdn = _gdn()
+    dev = _dev()
+    shape = W.shape_with(W.TINY_VERIFY, n_pool=3)
+    inp = W.make_inputs(shape, 10)
+    d = dev.upload(shape, inp)
+    gdn.gdn_reset(d["dims"], d["state"], d["conv_state"], 1)
+    torch.cuda.synchronize()
+    st = to_np(d["state"])
+    assert np.all(st[1] == 0) and np.all(to_np(d["conv_state"])[1] == 0)
+    np.testing.assert_array_equal(st[0], inp["state"][0])
+    np.testing.assert_array_equal(st[2], inp["state"][2])
