@@ -155,7 +155,7 @@ def main() -> int:
     rb = bytemodel.rollback_bytes(shape, B)
     achieved = vb / (v_avg * 1e-3) / 1e9
     traffic = measured_traffic(B * shape.n_vh)
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us), "
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us), "
         f"verify {v_avg * 1e3:.1f} us avg (p10 {np.percentile(verify_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(verify_ms, 90) * 1e3:.1f}) -> {achieved:.0f} GB/s; "
         f"step {(vb + rb) / (ms_step * 1e-3) / 1e9:.0f} GB/s")

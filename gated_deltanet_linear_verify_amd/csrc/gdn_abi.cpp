@@ -147,14 +147,14 @@ GDN_API int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, co
     if (!state || !conv_state || !qkv || !z || !alpha || !beta || !A_log || !dt_bias || !conv_w || !norm_w || !out ||
         !slot_ids)
         return fail(GDN_ERR_ARG, "gdn_verify: a required pointer is NULL");
-    if (!aligned16(state) || !aligned16(conv_state) || !aligned16(conv_w))
-        return fail(GDN_ERR_ARG, "gdn_verify: state, conv_state and conv_w must be 16-byte aligned");
+    if (!aligned16(state) || !aligned16(conv_state) || !aligned16(conv_w) || !aligned16(z) || !aligned16(qkv))
+        return fail(GDN_ERR_ARG, "gdn_verify: state, conv_state, conv_w, qkv and z must be 16-byte aligned");
     if (n_tok < 1) return fail(GDN_ERR_RANGE, "gdn_verify: n_tok must be >= 1 (got %d)", n_tok);
     if (n_batch < 1 || n_batch > d.n_pool)
         return fail(GDN_ERR_RANGE, "gdn_verify: n_batch %d outside [1, n_pool = %d]", n_batch, d.n_pool);
     if (capture)
         if (int r = check_capture(capture, GDN_CHAIN, n_tok, dims)) return r;
-    if (gdn::verify_chain_lds_bytes(d.d_k, d.n_vh / d.n_kh) > kMaxLds)
+    if (gdn::verify_chain_lds_bytes(d.d_k, d.n_vh / d.n_kh, d.act_dtype == GDN_BF16) > kMaxLds)
         return fail(GDN_ERR_SHAPE, "gdn_verify: LDS tile exceeds 160 KiB");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (d.flags & GDN_F_CHECK_INDICES)

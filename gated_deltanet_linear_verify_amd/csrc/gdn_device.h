@@ -60,6 +60,20 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4).  The LDS address must be
+// the same for the whole wave up to lane * 16: lane i lands at lds + 16 i of the first active lane.
+// Tracked by the vector-memory counter like any load.  The builtin exists only for the device
+// compilation pass; the host pass just needs the declaration to emit launch stubs.
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#else
+    (void)g;
+    (void)lds;
+#endif
+}
+
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 

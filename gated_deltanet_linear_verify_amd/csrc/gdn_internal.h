@@ -11,6 +11,7 @@ constexpr int kTokenTile = 16;  // tokens per LDS tile in the verify kernels
 
 struct VerifyArgs {
     int32_t n_kh, n_vh, d, n_pool, T, t_cap, C;
+    int32_t t0, nt;  // chain verify: first token and token count of one launch (set by the launcher)
     float eps;
     float *state;
     float *conv_state;
@@ -34,7 +35,7 @@ hipError_t launch_verify_chain(const VerifyArgs &a, const LaunchCfg &c, hipStrea
 hipError_t launch_verify_tree(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream);
 
 int verify_waves_per_head(int d);
-size_t verify_chain_lds_bytes(int d, int ratio);
+size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16);
 size_t verify_tree_lds_bytes(int d, int T);
 
 struct RollbackArgs {

@@ -16,10 +16,19 @@
 // Per token (Yang, Kautz & Hatamizadeh 2024, gated delta rule):
 //   p = S k,  u = beta (v - rho p),  S <- rho S + u k^T,  o = rho (S_old q) + (k.q) u  (= S_new q)
 // The capture of S after every token (lucebox-hub internal.h, struct TargetCache,
-// ssm_intermediate) is streamed out with nontemporal stores; the RMS norm + SiLU(z) epilogue
-// (ssm_norm, z projection: internal.h, struct TargetLayer) runs per token tile from LDS.
+// ssm_intermediate) streams out while the next token is computed; the RMS norm + SiLU(z)
+// epilogue (ssm_norm, z projection: internal.h, struct TargetLayer) runs per token tile.
+//
+// Memory schedule.  gfx950 has one vector-memory counter for loads and stores, so a load issued
+// after the capture stores would have to wait for them.  A launch therefore stages everything it
+// reads (raw qkv rows and z straight into LDS with global_load_lds, alpha, beta, conv taps, conv
+// state and the recurrent state into registers) before the token loop; the token loop and the
+// epilogue only read LDS and only store to global memory.  One launch covers up to 16 tokens;
+// longer chains are consecutive launches that pick up the state the previous one left.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+
+#include <type_traits>
 
 namespace gdn {
 
@@ -49,14 +58,43 @@ struct WavesPerHead<64> {
     static constexpr int value = 2;
 };
 
-__device__ __forceinline__ void store_nt(float *p, f4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(p)); }
+// Capture stores are nontemporal: plain stores leave ~2 GB of dirty lines in L2 / Infinity Cache
+// that the next kernel (the rollback) pays to write back; measured on MI355X, the verify +
+// rollback step is faster with nt stores.
+__device__ __forceinline__ void store_cap(float *p, f4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(p)); }
+
+// Occupancy cap: about 8 waves per CU.  The capture stream writes faster with fewer concurrent
+// write streams per CU (measured: ~5.9 vs ~5.6 TB/s for the bare store pattern), and 2 waves per
+// SIMD still hide the token loop's arithmetic under the stores.  The cap is applied by requesting
+// enough LDS that no more workgroups fit on a CU (160 KiB of LDS per CU).
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr int kTargetWavesPerCu = 8;
+
+// LDS carve-up of one workgroup (R value heads per key head, act_t = activation storage type).
+template <int D, typename act_t>
+struct VerifyLds {
+    static constexpr int TT = kTokenTile;
+    __host__ __device__ static size_t raw_bytes(int R) { return (size_t)TT * (2 + R) * D * sizeof(act_t); }
+    __host__ __device__ static size_t o_bytes(int R) { return (size_t)R * TT * D * sizeof(float); }
+    __host__ __device__ static size_t region(int R) { return raw_bytes(R) > o_bytes(R) ? raw_bytes(R) : o_bytes(R); }
+    __host__ __device__ static size_t total(int R)
+    {
+        return sizeof(float) * (2 * TT * D + (size_t)R * TT * D)  // ks, qs, vs
+               + region(R)                                          // os, aliased by the raw rows
+               + (size_t)R * TT * D * sizeof(act_t)                 // zs
+               + sizeof(float) * (2 * (size_t)R * TT + TT + D);      // rb, kqs, norm_w
+    }
+};
 
 template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN, bool CAP>
 __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
 {
+    using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
+    using L = VerifyLds<D, act_t>;
     constexpr int NW = WavesPerHead<D>::value;
     using G = Geo<D, NW>;
     constexpr int TT = kTokenTile;
+    constexpr int VEC = 16 / (int)sizeof(act_t);  // activations per 16-byte load
     const int R = a.n_vh / a.n_kh;
     const int nthr = blockDim.x;
     const int tid = threadIdx.x;
@@ -71,22 +109,71 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the workgroup
 
-    extern __shared__ float smem[];
-    float *ks = smem;                  // [TT][D]
-    float *qs = ks + TT * D;           // [TT][D]
-    float *vs = qs + TT * D;           // [R][TT][D]   rows in perm order
-    float *os = vs + R * TT * D;       // [R][TT][D]   rows in perm order
-    float *rb = os + R * TT * D;       // [R][TT][2]   (rho, beta)
-    float *kqs = rb + R * TT * 2;      // [TT]         k . q
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    float *ks = reinterpret_cast<float *>(smem_raw);  // [TT][D]
+    float *qs = ks + TT * D;                            // [TT][D]
+    float *vs = qs + TT * D;                            // [R][TT][D]   rows in perm order
+    float *os = vs + R * TT * D;                        // [R][TT][D]   rows in perm order
+    act_t *raw = reinterpret_cast<act_t *>(os);         // [TT][nch]    staged qkv rows (prologue only)
+    act_t *zs = reinterpret_cast<act_t *>(reinterpret_cast<unsigned char *>(os) + L::region(R));  // [TT][R*D]
+    float *rb = reinterpret_cast<float *>(zs + R * TT * D);  // [R][TT][2]   (rho, beta)
+    float *kqs = rb + R * TT * 2;                              // [TT]         k . q
+    float *nws = kqs + TT;                                     // [D]          norm_w
 
     const int C = a.C;
-    const int T = a.T;
+    const int T = a.T;    // tokens of the whole call: the row stride of qkv, z, alpha, beta, out
+    const int t0 = a.t0;  // first token of this launch
+    const int nt = a.nt;  // tokens of this launch, 1 .. TT
     const int nch = (2 + R) * D;
     const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + hk * R * D;
     float *cs_s = a.conv_state + (size_t)s * 3 * C;
     const size_t hd = (size_t)D * D;
+    const act_t *qkv_b = static_cast<const act_t *>(a.qkv) + ((size_t)b * T + t0) * C;
+    const act_t *z_b = static_cast<const act_t *>(a.z) + ((size_t)b * T + t0) * a.n_vh * D + (size_t)hk * R * D;
+    auto to_f32 = [](act_t x) -> float {
+        if constexpr (ACT_BF16)
+            return bf16_to_f32(x);
+        else
+            return x;
+    };
+    // local channel -> global channel of the fused qkv stream (blocks q | k | v)
+    auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
 
-    // ---- state -> registers
+    // ================= stage: every global load of the launch is issued up front =================
+    // The qkv rows go straight from HBM into LDS (global_load_lds_dwordx4: lane i of a wave lands
+    // at the wave's LDS base + 16 i) in row-major [token][local channel] order: no VGPR holds them.
+    const int nvr = nch / VEC;  // 16-byte vectors per staged row
+    for (int it = tid; it < nt * nvr; it += nthr) {
+        const int r = it / nvr, lc = (it % nvr) * VEC;
+        lds_dma16(qkv_b + (uint32_t)(r * C + gchan(lc)), raw + it * VEC);
+    }
+    // z: [nt][R*D] is contiguous in HBM and in LDS
+    for (int it = tid; it < nt * R * D / VEC; it += nthr) {
+        const int e0 = it * VEC, t = e0 / (R * D), within = e0 % (R * D);
+        lds_dma16(z_b + (uint32_t)(t * a.n_vh * D + within), zs + e0);
+    }
+    // alpha and beta: at most one (token, head) per thread
+    float al = 0.f, be = 0.f;
+    if (tid < nt * R) {
+        const int t = tid / R, hh = tid % R;
+        const size_t tok = ((size_t)b * T + t0 + t) * a.n_vh + hk * R + hh;
+        al = load_act<ACT_BF16>(a.alpha, tok);
+        be = load_act<ACT_BF16>(a.beta, tok);
+    }
+    // conv taps and the slot's conv state (xext rows 0..2 of the launch) of this thread's channels
+    f4 wv[2];
+    float csv[2][3];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int lc = tid + it * nthr;
+        if (lc < nch) {
+            const int gc = gchan(lc);
+            wv[it] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
+#pragma unroll
+            for (int r = 0; r < 3; ++r) csv[it][r] = cs_s[(uint32_t)(r * C + gc)];
+        }
+    }
+    // the recurrent state, into registers
     float S[G::RPL][G::CPL];  // S[i][4 c4 + e] = state row (row0 + 4 i), column (64 c4 + 4 cg + e)
     const int row0 = wih * G::RPW + rg;
     float *st_ptr = a.state + ((size_t)s * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
@@ -98,49 +185,41 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[i][4 * c4 + e] = v[e];
         }
-
-    float *cap_ptr = nullptr;
-    size_t cap_tstride = 0;
-    if constexpr (CAP) {
-        cap_ptr = a.cap_ssm + ((size_t)s * a.t_cap * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
-        cap_tstride = (size_t)a.n_vh * hd;
+    float nw = 0.f;
+    if (tid < D) nw = a.norm_w[tid];
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): registers loaded, LDS rows landed
+    if (tid < D) nws[tid] = nw;
+    if (tid < nt * R) {
+        const int t = tid / R, hh = tid % R, h2 = hk * R + hh;
+        const float g = -expf(a.A_log[h2]) * softplus_f(al + a.dt_bias[h2]);
+        rb[(hh * TT + t) * 2 + 0] = expf(g);
+        rb[(hh * TT + t) * 2 + 1] = be;
     }
+    __syncthreads();
 
-    auto xext = [&](int r, int gc) -> float {
-        return r < 3 ? cs_s[(size_t)r * C + gc]
-                     : load_act<ACT_BF16>(a.qkv, ((size_t)b * T + (r - 3)) * C + gc);
-    };
-
-#pragma unroll 1
-    for (int t0 = 0; t0 < T; t0 += TT) {
-        const int nt = min(TT, T - t0);
-        // ---- depthwise causal conv of this tile (one thread per channel)
-#pragma unroll 1
-        for (int lc = tid; lc < nch; lc += nthr) {
-            int gc;
+    // ================= depthwise causal conv (one thread per channel) =================
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int lc = tid + it * nthr;
+        if (lc < nch) {
+            const int gc = gchan(lc);
             float *dst;
-            if (lc < D) {
-                gc = q0 + lc;
+            if (lc < D)
                 dst = qs + lc;
-            } else if (lc < 2 * D) {
-                gc = k0 + (lc - D);
+            else if (lc < 2 * D)
                 dst = ks + (lc - D);
-            } else {
-                const int vr = lc - 2 * D;
-                gc = v0 + vr;
-                dst = vs + (vr / D) * TT * D + G::perm(vr % D);
-            }
-            const f4 w = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
-            float x0 = xext(t0, gc), x1 = xext(t0 + 1, gc), x2 = xext(t0 + 2, gc);
+            else
+                dst = vs + ((lc - 2 * D) / D) * TT * D + G::perm((lc - 2 * D) % D);
+            float x0 = csv[it][0], x1 = csv[it][1], x2 = csv[it][2];
+            const f4 w = wv[it];
             float *cc = CAP ? a.cap_conv + (size_t)s * (3 + a.t_cap) * C + gc : nullptr;
-            if (CAP && t0 == 0) {
+            if (CAP && t0 == 0) {  // the window starts with the conv state the call began from
                 cc[0] = x0;
                 cc[(size_t)C] = x1;
                 cc[(size_t)2 * C] = x2;
             }
-#pragma unroll 2
             for (int t = 0; t < nt; ++t) {
-                const float x3 = xext(t0 + t + 3, gc);
+                const float x3 = to_f32(raw[t * nch + lc]);
                 float y = w[0] * x0 + w[1] * x1 + w[2] * x2 + w[3] * x3;
                 if constexpr (QKN) y = y * sigmoid_f(y);
                 dst[t * D] = y;
@@ -149,184 +228,191 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
                 x1 = x2;
                 x2 = x3;
             }
-        }
-        // ---- per-token gate and beta
-        for (int i = tid; i < nt * R; i += nthr) {
-            const int t = i / R, hh = i % R, h2 = hk * R + hh;
-            const size_t tok = ((size_t)b * T + t0 + t) * a.n_vh + h2;
-            const float al = load_act<ACT_BF16>(a.alpha, tok);
-            const float be = load_act<ACT_BF16>(a.beta, tok);
-            const float g = -expf(a.A_log[h2]) * softplus_f(al + a.dt_bias[h2]);
-            rb[(hh * TT + t) * 2 + 0] = expf(g);
-            rb[(hh * TT + t) * 2 + 1] = be;
-        }
-        __syncthreads();
-        // ---- optional q/k scaling, and k . q (one wave per token)
-        for (int t = wave; t < nt; t += nwaves) {
-            constexpr int E = D / 64;
-            float qv[E], kv[E];
-            float dq = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                qv[e] = qs[t * D + lane + 64 * e];
-                kv[e] = ks[t * D + lane + 64 * e];
-            }
-            if constexpr (QKN) {
-                float nq = 0.f, nk = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    nq += qv[e] * qv[e];
-                    nk += kv[e] * kv[e];
-                }
-                nq = wave_sum(nq);
-                nk = wave_sum(nk);
-                const float sq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)D);
-                const float sk = 1.0f / sqrtf(nk + 1e-6f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    qv[e] *= sq;
-                    kv[e] *= sk;
-                    qs[t * D + lane + 64 * e] = qv[e];
-                    ks[t * D + lane + 64 * e] = kv[e];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e) dq += qv[e] * kv[e];
-            dq = wave_sum(dq);
-            if (lane == 0) kqs[t] = dq;
-        }
-        __syncthreads();
-
-        // ---- the recurrence over the tile's tokens, state in registers.  Nothing but capture
-        // stores touches global memory in this loop; draining the loads first keeps the
-        // compiler from placing a full vmcnt wait (which would also wait for the stores) in it.
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
-#pragma unroll 1
-        for (int t = 0; t < nt; ++t) {
-            // p = S k and S q, accumulated chunk by chunk to keep few values live
-            float pk[G::RPL], pq[G::RPL];
-#pragma unroll
-            for (int i = 0; i < G::RPL; ++i) pk[i] = pq[i] = 0.f;
-#pragma unroll
-            for (int c4 = 0; c4 < G::NC4; ++c4) {
-                const f4 kk = *reinterpret_cast<const f4 *>(ks + t * D + 64 * c4 + 4 * cg);
-                const f4 qq = *reinterpret_cast<const f4 *>(qs + t * D + 64 * c4 + 4 * cg);
-#pragma unroll
-                for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pk[i] += S[i][4 * c4 + e] * kk[e];
-                        pq[i] += S[i][4 * c4 + e] * qq[e];
-                    }
-            }
-#pragma unroll
-            for (int i = 0; i < G::RPL; ++i) {
-                pk[i] = row16_sum(pk[i]);
-                pq[i] = row16_sum(pq[i]);
-            }
-            const f2 rbv = *reinterpret_cast<const f2 *>(rb + (hl * TT + t) * 2);
-            const float rho = rbv[0], be = rbv[1];
-            const float kq = kqs[t];
-            const float *vsrc = vs + (hl * TT + t) * D + wih * G::RPW + rg * G::RPL;
-#pragma unroll
-            for (int i = 0; i < G::RPL; ++i) {
-                const float u = be * (vsrc[i] - rho * pk[i]);
-                pq[i] = rho * pq[i] + kq * u;  // o = S_new q for row i
-                pk[i] = u;
-            }
-            if (cg == 0) {
-                float *od = os + (hl * TT + t) * D + wih * G::RPW + rg * G::RPL;
-#pragma unroll
-                for (int i = 0; i < G::RPL; ++i) od[i] = pq[i];
-            }
-#pragma unroll
-            for (int c4 = 0; c4 < G::NC4; ++c4) {
-                const f4 kk = *reinterpret_cast<const f4 *>(ks + t * D + 64 * c4 + 4 * cg);
-#pragma unroll
-                for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)  // S <- rho S + u k^T, scaled in place then accumulated
-                        S[i][4 * c4 + e] = __builtin_fmaf(pk[i], kk[e], S[i][4 * c4 + e] * rho);
-            }
-            if constexpr (CAP) {
-                float *cp = cap_ptr + (size_t)(t0 + t) * cap_tstride;
-#pragma unroll
-                for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                    for (int c4 = 0; c4 < G::NC4; ++c4) {
-                        const f4 v = {S[i][4 * c4], S[i][4 * c4 + 1], S[i][4 * c4 + 2], S[i][4 * c4 + 3]};
-                        store_nt(cp + (size_t)(4 * i) * D + 64 * c4, v);
-                    }
-            }
-        }
-        __syncthreads();
-
-        // ---- epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z), 16 lanes per row
-        {
-            constexpr int EPL = D / 16;
-            const int grp = tid >> 4, ngrp = nthr >> 4;
-#pragma unroll 1
-            for (int row = grp; row < R * nt; row += ngrp) {
-                const int hh = row / nt, t = row % nt, h2 = hk * R + hh;
-                const float *osrc = os + (hh * TT + t) * D;
-                float ov[EPL];
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    ov[e] = osrc[G::perm(cg * EPL + e)];
-                    ss += ov[e] * ov[e];
-                }
-                ss = row16_sum(ss);
-                const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-                const size_t base = (((size_t)b * T + t0 + t) * a.n_vh + h2) * D + cg * EPL;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const float zz = load_act<ACT_BF16>(a.z, base + e);
-                    const float y = ov[e] * inv * a.norm_w[cg * EPL + e] * (zz * sigmoid_f(zz));
-                    if constexpr (OUT_BF16)
-                        static_cast<uint16_t *>(a.out)[base + e] = f32_to_bf16(y);
-                    else
-                        static_cast<float *>(a.out)[base + e] = y;
-                }
-            }
+            // conv state after the launch's last token (xext rows nt .. nt+2); this thread was the
+            // only reader of these elements
+            cs_s[gc] = x0;
+            cs_s[(size_t)C + gc] = x1;
+            cs_s[(size_t)2 * C + gc] = x2;
         }
     }
-
-    // ---- final state and conv state (each conv channel is updated by the thread that read it)
-    float *sp = a.state + ((size_t)s * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
+    __syncthreads();
+    // ---- optional q/k scaling, and k . q (one wave per token)
+    for (int t = wave; t < nt; t += nwaves) {
+        constexpr int E = D / 64;
+        float qv[E], kv[E];
+        float dq = 0.f;
 #pragma unroll
-    for (int i = 0; i < G::RPL; ++i)
+        for (int e = 0; e < E; ++e) {
+            qv[e] = qs[t * D + lane + 64 * e];
+            kv[e] = ks[t * D + lane + 64 * e];
+        }
+        if constexpr (QKN) {
+            float nq = 0.f, nk = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                nq += qv[e] * qv[e];
+                nk += kv[e] * kv[e];
+            }
+            nq = wave_sum(nq);
+            nk = wave_sum(nk);
+            const float sq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)D);
+            const float sk = 1.0f / sqrtf(nk + 1e-6f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                qv[e] *= sq;
+                kv[e] *= sk;
+                qs[t * D + lane + 64 * e] = qv[e];
+                ks[t * D + lane + 64 * e] = kv[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) dq += qv[e] * kv[e];
+        dq = wave_sum(dq);
+        if (lane == 0) kqs[t] = dq;
+    }
+    __syncthreads();
+
+    // ================= the recurrence, state in registers =================
+    // Only LDS reads and capture stores from here on: no wait on the memory counter, which the
+    // capture stores occupy.
+    float *cap_ptr = nullptr;
+    size_t cap_tstride = 0;
+    if constexpr (CAP) {
+        cap_ptr = a.cap_ssm + (((size_t)s * a.t_cap + t0) * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
+        cap_tstride = (size_t)a.n_vh * hd;
+    }
+#pragma unroll 1
+    for (int t = 0; t < nt; ++t) {
+        // p = S k and S q, accumulated chunk by chunk to keep few values live
+        float pk[G::RPL], pq[G::RPL];
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i) pk[i] = pq[i] = 0.f;
 #pragma unroll
         for (int c4 = 0; c4 < G::NC4; ++c4) {
-            const f4 v = {S[i][4 * c4], S[i][4 * c4 + 1], S[i][4 * c4 + 2], S[i][4 * c4 + 3]};
-            *reinterpret_cast<f4 *>(sp + (size_t)(4 * i) * D + 64 * c4) = v;
+            const f4 kk = *reinterpret_cast<const f4 *>(ks + t * D + 64 * c4 + 4 * cg);
+            const f4 qq = *reinterpret_cast<const f4 *>(qs + t * D + 64 * c4 + 4 * cg);
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pk[i] += S[i][4 * c4 + e] * kk[e];
+                    pq[i] += S[i][4 * c4 + e] * qq[e];
+                }
         }
-    for (int lc = tid; lc < nch; lc += nthr) {
-        const int gc = lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D));
-        const float r0 = xext(T, gc), r1 = xext(T + 1, gc), r2 = xext(T + 2, gc);
-        cs_s[gc] = r0;
-        cs_s[(size_t)C + gc] = r1;
-        cs_s[(size_t)2 * C + gc] = r2;
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i) {
+            pk[i] = row16_sum(pk[i]);
+            pq[i] = row16_sum(pq[i]);
+        }
+        const f2 rbv = *reinterpret_cast<const f2 *>(rb + (hl * TT + t) * 2);
+        const float rho = rbv[0], be = rbv[1];
+        const float kq = kqs[t];
+        const float *vsrc = vs + (hl * TT + t) * D + wih * G::RPW + rg * G::RPL;
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i) {
+            const float u = be * (vsrc[i] - rho * pk[i]);
+            pq[i] = rho * pq[i] + kq * u;  // o = S_new q for row i
+            pk[i] = u;
+        }
+        if (cg == 0) {
+            float *od = os + (hl * TT + t) * D + wih * G::RPW + rg * G::RPL;
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i) od[i] = pq[i];
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < G::NC4; ++c4) {
+            const f4 kk = *reinterpret_cast<const f4 *>(ks + t * D + 64 * c4 + 4 * cg);
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)  // S <- rho S + u k^T, scaled in place then accumulated
+                    S[i][4 * c4 + e] = __builtin_fmaf(pk[i], kk[e], S[i][4 * c4 + e] * rho);
+        }
+        if constexpr (CAP) {
+            float *cp = cap_ptr + (size_t)t * cap_tstride;
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int c4 = 0; c4 < G::NC4; ++c4) {
+                    const f4 v = {S[i][4 * c4], S[i][4 * c4 + 1], S[i][4 * c4 + 2], S[i][4 * c4 + 3]};
+                    store_cap(cp + (size_t)(4 * i) * D + 64 * c4, v);
+                }
+        }
+    }
+    // ---- final state (address rebuilt from a wave-uniform base so none is kept across the loop)
+    {
+        uint32_t off = (uint32_t)(row0 * D + cg * 4);
+        asm volatile("" : "+v"(off));
+        float *sp = a.state + ((size_t)s * a.n_vh + h) * hd;
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+            for (int c4 = 0; c4 < G::NC4; ++c4) {
+                const f4 v = {S[i][4 * c4], S[i][4 * c4 + 1], S[i][4 * c4 + 2], S[i][4 * c4 + 3]};
+                *reinterpret_cast<f4 *>(sp + off + (uint32_t)(4 * i * D + 64 * c4)) = v;
+            }
+    }
+    __syncthreads();
+
+    // ================= epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) =================
+    constexpr int EPL = D / 16;  // 16 lanes per (head, token) row
+    const int grp = tid >> 4, ngrp = nthr >> 4;
+#pragma unroll 1
+    for (int row = grp; row < R * nt; row += ngrp) {
+        const int hh = row / nt, t = row % nt, h2 = hk * R + hh;
+        const float *osrc = os + (hh * TT + t) * D;
+        float ov[EPL];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            ov[e] = osrc[G::perm(cg * EPL + e)];
+            ss += ov[e] * ov[e];
+        }
+        ss = row16_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+        const size_t base = (((size_t)b * T + t0 + t) * a.n_vh + h2) * D + cg * EPL;
+        const act_t *zrow = zs + t * R * D + hh * D + cg * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float zz = to_f32(zrow[e]);
+            const float y = ov[e] * inv * nws[cg * EPL + e] * (zz * sigmoid_f(zz));
+            if constexpr (OUT_BF16)
+                static_cast<uint16_t *>(a.out)[base + e] = f32_to_bf16(y);
+            else
+                static_cast<float *>(a.out)[base + e] = y;
+        }
     }
 }
 
 int verify_waves_per_head(int d) { return d == 128 ? WavesPerHead<128>::value : WavesPerHead<64>::value; }
 
-size_t verify_chain_lds_bytes(int d, int ratio)
+size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16)
 {
-    const size_t TT = kTokenTile;
-    return sizeof(float) * (2 * TT * d + 2 * (size_t)ratio * TT * d + 2 * (size_t)ratio * TT + TT);
+    if (d == 128) return act_bf16 ? VerifyLds<128, uint16_t>::total(ratio) : VerifyLds<128, float>::total(ratio);
+    return act_bf16 ? VerifyLds<64, uint16_t>::total(ratio) : VerifyLds<64, float>::total(ratio);
 }
 
+// One launch covers at most kTokenTile tokens; longer chains are consecutive launches on the same
+// stream, each starting from the state and conv state the previous one left.
 template <int D, bool AB, bool OB, bool QKN, bool CAP>
-static hipError_t launch_t(const VerifyArgs &a, hipStream_t stream)
+static hipError_t launch_t(const VerifyArgs &a0, hipStream_t stream)
 {
-    const int R = a.n_vh / a.n_kh;
+    const int R = a0.n_vh / a0.n_kh;
     const int threads = R * WavesPerHead<D>::value * 64;
-    const size_t lds = verify_chain_lds_bytes(D, R);
-    hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP>), dim3(a.n_batch * a.n_kh), dim3(threads),
-                       lds, stream, a);
-    return hipGetLastError();
+    size_t lds = verify_chain_lds_bytes(D, R, AB);
+    const int waves = R * WavesPerHead<D>::value;
+    const int wgs_per_cu = waves >= kTargetWavesPerCu ? 1 : kTargetWavesPerCu / waves;
+    const size_t lds_cap = kLdsPerCu / (wgs_per_cu + 1) + 16;  // wgs_per_cu + 1 workgroups no longer fit
+    if (lds < lds_cap) lds = lds_cap;
+    for (int t0 = 0; t0 < a0.T; t0 += kTokenTile) {
+        VerifyArgs a = a0;
+        a.t0 = t0;
+        a.nt = a0.T - t0 < kTokenTile ? a0.T - t0 : kTokenTile;
+        hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP>), dim3(a.n_batch * a.n_kh), dim3(threads), lds,
+                           stream, a);
+        if (hipError_t e = hipGetLastError()) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D, bool AB, bool OB, bool QKN>
