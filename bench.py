@@ -76,6 +76,53 @@ def cpu_baseline(shape, inp, target_s: float = 10.0) -> dict:
                       f"{sum(times):.1f} s, median {med * 1e3:.0f} ms"}
 
 
+def time_launches(fn, n: int, warmup: int = 3) -> float:
+    """Average duration in microseconds of fn() over n launches, HIP events on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def components(args) -> dict:
+    """Secondary timings of the other kernels on their own workloads (not part of the step)."""
+    import numpy as np
+    import torch
+
+    from gated_deltanet_linear_verify_amd import bytemodel, device, gdn
+    from gated_deltanet_linear_verify_amd import workloads as W
+
+    out = {}
+    # tree verify: 8 slots x 64-node trees
+    s = W.TREE_VERIFY
+    d = device.upload(s, W.make_tree_inputs(s, 0), mode=gdn.GDN_TREE, fill_capture=0.0)
+    us = time_launches(lambda: device.verify_tree(d), 50)
+    out["tree_verify"] = {"workload": "8 slots x 64-node trees, 16/32 heads, d=128, bf16",
+                          "us": us, "tokens_per_s": s.n_batch * s.n_tok / (us * 1e-6),
+                          "hbm_gbps": bytemodel.tree_bytes(s) / (us * 1e-6) / 1e9,
+                          "algorithmic_bytes": bytemodel.tree_bytes(s)}
+    del d
+    # single-slot verify: 1 slot x 16 tokens
+    s = W.SINGLE_SLOT_VERIFY
+    d = device.upload(s, W.make_inputs(s, 0), fill_capture=0.0)
+    us = time_launches(lambda: device.verify(d), 200)
+    out["single_slot_verify"] = {"workload": "1 slot x 16 tokens, 16/32 heads, d=128, bf16", "us": us,
+                                 "tokens_per_s": s.n_tok / (us * 1e-6),
+                                 "hbm_gbps": bytemodel.verify_bytes(s) / (us * 1e-6) / 1e9}
+    del d
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +130,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotating input/state sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true",
+                    help="skip the secondary timings (tree verify, single-slot verify, rollback)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU code (got --gpus "
@@ -130,13 +179,14 @@ def main() -> int:
         if ev is not None:
             ev[1].record(stream)
         gdn.gdn_rollback_batch(d["capture"], d["slot_ids"], d["accepted"], B, stream)
+        if ev is not None:
+            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -148,7 +198,9 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    verify_ms = [a.elapsed_time(b) for a, b in evs]
+    verify_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    rollback_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    r_avg = sum(rollback_ms) / len(rollback_ms)
     ms_step = total_ms / args.steps
     v_avg = sum(verify_ms) / len(verify_ms)
     vb = bytemodel.verify_bytes(shape)
@@ -178,11 +230,14 @@ def main() -> int:
                    "activations": "bf16", "state_and_capture": "f32",
                    "step": "gdn_verify + gdn_rollback_batch", "rotating_sets": args.sets},
         "hbm_gbps_step": (vb + rb) / (ms_step * 1e-3) / 1e9,
+        "rollback": {"us": r_avg * 1e3, "hbm_gbps": rb / (r_avg * 1e-3) / 1e9, "algorithmic_bytes": rb},
         "roofline": {"kernel": "verify_chain_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": vb,
                      "avg_launch_us": v_avg * 1e3},
     }
+    if not args.no_components:
+        result["components"] = components(args)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(shape, base)

@@ -192,14 +192,14 @@ GDN_API int gdn_verify_tree(const gdn_dims *dims, const float *state, const floa
     if (!state || !conv_state || !qkv || !z || !alpha || !beta || !A_log || !dt_bias || !conv_w || !norm_w ||
         !parent || !capture || !out || !slot_ids)
         return fail(GDN_ERR_ARG, "gdn_verify_tree: a required pointer is NULL");
-    if (!aligned16(state) || !aligned16(conv_state) || !aligned16(conv_w))
-        return fail(GDN_ERR_ARG, "gdn_verify_tree: state, conv_state and conv_w must be 16-byte aligned");
+    if (!aligned16(state) || !aligned16(conv_state) || !aligned16(conv_w) || !aligned16(qkv))
+        return fail(GDN_ERR_ARG, "gdn_verify_tree: state, conv_state, conv_w and qkv must be 16-byte aligned");
     if (n_tok < 1) return fail(GDN_ERR_RANGE, "gdn_verify_tree: n_tok must be >= 1 (got %d)", n_tok);
     if (n_batch < 1 || n_batch > d.n_pool)
         return fail(GDN_ERR_RANGE, "gdn_verify_tree: n_batch %d outside [1, n_pool = %d]", n_batch, d.n_pool);
     if (int r = check_capture(capture, GDN_TREE, n_tok, dims)) return r;
-    if (gdn::verify_tree_lds_bytes(d.d_k, n_tok) > kMaxLds)
-        return fail(GDN_ERR_SHAPE, "gdn_verify_tree: %d nodes exceed the LDS tile", n_tok);
+    if (gdn::verify_tree_lds_bytes(d.d_k, n_tok, d.act_dtype == GDN_BF16) > kMaxLds)
+        return fail(GDN_ERR_SHAPE, "gdn_verify_tree: %d nodes do not fit one workgroup's LDS (at most 64 nodes)", n_tok);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (d.flags & GDN_F_CHECK_INDICES) {
         if (int r = check_slots(slot_ids, n_batch, d.n_pool, st)) return r;

@@ -74,6 +74,13 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds)
 #endif
 }
 
+// Depthwise causal conv tap sum, oldest input first; tap 3 multiplies the current token.  One
+// fixed rounding order so every kernel produces identical bits for identical windows.
+__device__ __forceinline__ float conv4(f4 w, float x0, float x1, float x2, float x3)
+{
+    return __builtin_fmaf(w[3], x3, __builtin_fmaf(w[2], x2, __builtin_fmaf(w[1], x1, w[0] * x0)));
+}
+
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 

@@ -31,12 +31,12 @@ struct LaunchCfg {
 
 // Chain verify: grid B * H_k workgroups of (H_v/H_k) * waves_per_head(d) waves.
 hipError_t launch_verify_chain(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream);
-// Tree verify: grid B * H_v workgroups.
+// Tree verify: grid B * H_v workgroups of waves_per_head(d) waves; at most 64 nodes.
 hipError_t launch_verify_tree(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream);
 
 int verify_waves_per_head(int d);
 size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16);
-size_t verify_tree_lds_bytes(int d, int T);
+size_t verify_tree_lds_bytes(int d, int T, bool act_bf16);  // (size_t)-1 above the node limit
 
 struct RollbackArgs {
     float *state, *conv_state;

@@ -1,11 +1,408 @@
-// gdn_tree.hip - tree verify (placeholder until the kernel lands).
+// gdn_tree.hip - tree verify: every node of a draft tree verified in one launch (gfx950).
+//
+// Tree mode of the verify forward (lucebox-hub internal.h, QwenGraphInputs::parent_ids; the
+// capture is sized for 1 + tree budget positions in create_target_cache).  Node i hangs off
+// parent[i] (-1: the committed state); its state is its parent's state advanced by node i's
+// token and its conv window runs along its root path, filled from the slot's conv state above the
+// root.  Every node's state and 3-row conv state are captured so that gdn_rollback can commit any
+// accepted node; the committed state and conv state are left untouched.
+//
+// One workgroup per (batch entry, value head).  A prologue stages the raw q|k|v rows of all nodes
+// in LDS (global_load_lds), computes every node's conv output, gate, beta and k.q into LDS, and
+// builds a depth-first processing schedule.  The node loop then runs in DFS order: a node whose
+// parent is the node just processed continues from the state in registers; any other node
+// restarts from a register copy of the committed state and re-runs its parent's root path
+// (compute only, nothing stored) before its own step.  No state is ever re-read from memory, so
+// the loop never waits on the memory counter that the capture stores occupy.
 #include "gdn_device.h"
+#include "gdn_geo.h"
 #include "gdn_internal.h"
+
+#include <type_traits>
 
 namespace gdn {
 
-size_t verify_tree_lds_bytes(int d, int T) { return sizeof(float) * (size_t)T * d; }
+constexpr int kTreeMaxNodes = 64;
+// Schedule entry: node index | restart-from-committed-state flag | capture-and-output flag.
+constexpr int kSchedRestart = 0x100;
+constexpr int kSchedEmit = 0x200;
+constexpr int kSchedMax = kTreeMaxNodes * (kTreeMaxNodes + 1) / 2 + kTreeMaxNodes;
 
-hipError_t launch_verify_tree(const VerifyArgs &, const LaunchCfg &, hipStream_t) { return hipErrorNotSupported; }
+template <int D, typename act_t>
+struct TreeLds {
+    __host__ __device__ static size_t raw_bytes(int T) { return (size_t)T * 3 * D * sizeof(act_t); }
+    __host__ __device__ static size_t o_bytes(int T) { return (size_t)T * D * sizeof(float); }
+    __host__ __device__ static size_t region(int T)
+    {
+        const size_t r = raw_bytes(T) > o_bytes(T) ? raw_bytes(T) : o_bytes(T);
+        return (r + 15) & ~(size_t)15;
+    }
+    __host__ __device__ static size_t total(int T)
+    {
+        return sizeof(float) * 3 * (size_t)T * D         // qs, ks, vs
+               + region(T)                                // raw rows, then os
+               + sizeof(float) * 4 * (size_t)T            // rho, beta, k.q
+               + sizeof(int) * 4 * (size_t)T              // ancestors 1..3 (+ pad)
+               + sizeof(int) * 4 * kTreeMaxNodes          // DFS scratch
+               + sizeof(uint16_t) * kSchedMax + 16;       // schedule + its length
+    }
+};
+
+template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN>
+__global__ __launch_bounds__(256) void verify_tree_kernel(VerifyArgs a)
+{
+    using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
+    using L = TreeLds<D, act_t>;
+    constexpr int NW = WavesPerHead<D>::value;
+    using G = Geo<D, NW>;
+    constexpr int VEC = 16 / (int)sizeof(act_t);
+    constexpr int NCH = 3 * D;  // q | k | v channels of this value head
+    const int R = a.n_vh / a.n_kh;
+    const int T = a.T;
+    const int tid = threadIdx.x;
+    const int nthr = NW * 64;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int rg = lane >> 4, cg = lane & 15;
+
+    const int b = blockIdx.x / a.n_vh;
+    const int h = blockIdx.x % a.n_vh;
+    const int hk = h / R;
+    const bool lead = (h % R) == 0;  // writes the shared q / k channels of the conv capture
+    const int s = a.slot_ids[b];
+    if (s < 0 || s >= a.n_pool) return;  // uniform over the workgroup
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    float *qs = reinterpret_cast<float *>(smem_raw);  // [T][D]
+    float *ks = qs + T * D;                            // [T][D]
+    float *vs = ks + T * D;                            // [T][D]   rows in perm order
+    act_t *raw = reinterpret_cast<act_t *>(vs + T * D);  // [T][3D]  raw q|k|v rows (prologue)
+    float *os = reinterpret_cast<float *>(raw);          // [T][D]   readout, rows in perm order (loop)
+    float *rbk = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(raw) + L::region(T));  // [T][4]
+    int *anc = reinterpret_cast<int *>(rbk + 4 * T);  // [T][4]: ancestors 1..3 (>= 0 node, -1-r conv row r)
+    int *dfs = anc + 4 * T;                                        // [4][kTreeMaxNodes] DFS scratch
+    uint16_t *sched = reinterpret_cast<uint16_t *>(dfs + 4 * kTreeMaxNodes);
+    int *nsched = reinterpret_cast<int *>(sched + kSchedMax);
+
+    const int C = a.C;
+    const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + h * D;
+    const float *cs_s = a.conv_state + (size_t)s * 3 * C;
+    const int32_t *par = a.parent + (size_t)b * T;
+    const act_t *qkv_b = static_cast<const act_t *>(a.qkv) + (size_t)b * T * C;
+    auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
+    auto to_f32 = [](act_t x) -> float {
+        if constexpr (ACT_BF16)
+            return bf16_to_f32(x);
+        else
+            return x;
+    };
+    // a malformed parent (outside [-1, i)) is treated as -1: the node starts from the committed state
+    auto parent_of = [&](int i) -> int {
+        const int p = par[i];
+        return (p >= -1 && p < i) ? p : -1;
+    };
+
+    // ================= stage: raw rows of all nodes into LDS, everything else into registers ====
+    const int nvr = NCH / VEC;
+    for (int it = tid; it < T * nvr; it += nthr) {
+        const int r = it / nvr, lc = (it % nvr) * VEC;
+        lds_dma16(qkv_b + (uint32_t)(r * C + gchan(lc)), raw + it * VEC);
+    }
+    constexpr int CPT = (NCH + 63) / 64 / NW + 1;  // channels per thread (upper bound)
+    f4 wv[CPT];
+    float csv[CPT][3];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int lc = tid + j * nthr;
+        if (lc < NCH) {
+            const int gc = gchan(lc);
+            wv[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
+#pragma unroll
+            for (int r = 0; r < 3; ++r) csv[j][r] = cs_s[(uint32_t)(r * C + gc)];
+        }
+    }
+    float al = 0.f, be = 0.f;
+    if (tid < T) {
+        const size_t tok = ((size_t)b * T + tid) * a.n_vh + h;
+        al = load_act<ACT_BF16>(a.alpha, tok);
+        be = load_act<ACT_BF16>(a.beta, tok);
+    }
+    // the committed state: kept in registers for the whole launch (restart point)
+    float R0[G::RPL][G::CPL];
+    const int wih = wave;
+    const int row0 = wih * G::RPW + rg;
+    const float *st_ptr = a.state + ((size_t)s * a.n_vh + h) * (size_t)D * D + (size_t)row0 * D + cg * 4;
+#pragma unroll
+    for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+        for (int c4 = 0; c4 < G::NC4; ++c4) {
+            const f4 v = *reinterpret_cast<const f4 *>(st_ptr + (size_t)(4 * i) * D + 64 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R0[i][4 * c4 + e] = v[e];
+        }
+    // ancestors 1..3 of every node (its conv window); where the root path ends, the slot's conv
+    // state rows fill in: with L path nodes inside the window, ancestor j > L-1 is conv row 2-(j-L)
+    if (tid < T) {
+        int code[3];
+        int m = tid, L = 1;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            m = m >= 0 ? parent_of(m) : -1;
+            code[k] = m;
+            L += m >= 0 ? 1 : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            if (code[k] < 0) code[k] = -1 - (2 - (k + 1 - L));  // -1 - conv row
+        anc[tid * 4 + 0] = code[0];
+        anc[tid * 4 + 1] = code[1];
+        anc[tid * 4 + 2] = code[2];
+        const float g = -expf(a.A_log[h]) * softplus_f(al + a.dt_bias[h]);
+        rbk[tid * 4 + 0] = expf(g);
+        rbk[tid * 4 + 1] = be;
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): raw rows landed, registers loaded
+    __syncthreads();
+
+    // ================= conv of every node (one thread per channel) + conv-state capture =========
+    float *cct = a.cap_conv + (size_t)s * a.t_cap * 3 * C;  // [t_cap][3][C] of this slot
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int lc = tid + j * nthr;
+        if (lc < NCH) {
+            const int gc = gchan(lc);
+            const f4 w = wv[j];
+            const bool own = lc >= 2 * D || lead;
+            float *dst = lc < D ? qs + lc : (lc < 2 * D ? ks + (lc - D) : vs + G::perm(lc - 2 * D));
+            auto X = [&](int code) -> float {
+                return code >= 0 ? to_f32(raw[code * NCH + lc]) : csv[j][-1 - code];
+            };
+            for (int n = 0; n < T; ++n) {
+                const int a1 = anc[n * 4 + 0], a2 = anc[n * 4 + 1], a3 = anc[n * 4 + 2];
+                const float x1 = X(a1), x2 = X(a2), xn = to_f32(raw[n * NCH + lc]);
+                float y = conv4(w, X(a3), x2, x1, xn);
+                if constexpr (QKN) y = y * sigmoid_f(y);
+                dst[n * D] = y;
+                if (own) {  // 3-row conv state after node n: [ancestor 2, ancestor 1, n]
+                    float *cp = cct + (size_t)n * 3 * C + gc;
+                    cp[0] = x2;
+                    cp[(size_t)C] = x1;
+                    cp[(size_t)2 * C] = xn;
+                }
+            }
+        }
+    }
+    // depth-first schedule (thread 0): children in increasing index, roots in increasing index
+    if (tid == 0) {
+        int *first = dfs, *sib = dfs + kTreeMaxNodes, *stack = dfs + 2 * kTreeMaxNodes;
+        int *path = dfs + 3 * kTreeMaxNodes;
+        for (int n = 0; n < T; ++n) first[n] = -1;
+        int first_root = -1;
+        for (int n = T - 1; n >= 0; --n) {  // prepend in reverse: lists come out in increasing order
+            const int p = parent_of(n);
+            int *head = p >= 0 ? &first[p] : &first_root;
+            sib[n] = *head;
+            *head = n;
+        }
+        int cnt = 0, in_regs = -1, sp = 0;  // in_regs: node whose state the registers hold (-1: none)
+        // the stack holds sibling-list cursors: pop a node, push its next sibling, then its first child
+        if (first_root >= 0) stack[sp++] = first_root;
+        while (sp > 0) {
+            const int n = stack[--sp];
+            if (sib[n] >= 0) stack[sp++] = sib[n];
+            if (first[n] >= 0) stack[sp++] = first[n];
+            const int p = parent_of(n);
+            if (p >= 0 && p == in_regs) {
+                sched[cnt++] = (uint16_t)(n | kSchedEmit);
+            } else if (p < 0) {
+                sched[cnt++] = (uint16_t)(n | kSchedRestart | kSchedEmit);
+            } else {  // re-run the parent's root path from the committed state, then the node
+                int L = 0;
+                for (int m = p; m >= 0; m = parent_of(m)) path[L++] = m;
+                for (int k = L - 1; k >= 0; --k)
+                    sched[cnt++] = (uint16_t)(path[k] | (k == L - 1 ? kSchedRestart : 0));
+                sched[cnt++] = (uint16_t)(n | kSchedEmit);
+            }
+            in_regs = n;
+        }
+        *nsched = cnt;
+    }
+    __syncthreads();
+    // ---- optional q/k scaling and k . q of every node (one wave per node)
+    for (int n = wave; n < T; n += NW) {
+        constexpr int E = D / 64;
+        float qv[E], kv[E];
+        float dq = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            qv[e] = qs[n * D + lane + 64 * e];
+            kv[e] = ks[n * D + lane + 64 * e];
+        }
+        if constexpr (QKN) {
+            float nq = 0.f, nk = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                nq += qv[e] * qv[e];
+                nk += kv[e] * kv[e];
+            }
+            nq = wave_sum(nq);
+            nk = wave_sum(nk);
+            const float sq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)D);
+            const float sk = 1.0f / sqrtf(nk + 1e-6f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                qv[e] *= sq;
+                kv[e] *= sk;
+                qs[n * D + lane + 64 * e] = qv[e];
+                ks[n * D + lane + 64 * e] = kv[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) dq += qv[e] * kv[e];
+        dq = wave_sum(dq);
+        if (lane == 0) rbk[n * 4 + 2] = dq;
+    }
+    __syncthreads();
+
+    // ================= the node loop in schedule order =================
+    float S[G::RPL][G::CPL];
+#pragma unroll
+    for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+        for (int c = 0; c < G::CPL; ++c) S[i][c] = R0[i][c];
+    const size_t hd = (size_t)D * D;
+    float *cap_base = a.cap_ssm + ((size_t)s * a.t_cap * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
+    const size_t cap_nstride = (size_t)a.n_vh * hd;
+    const int ns = *nsched;
+#pragma unroll 1
+    for (int k = 0; k < ns; ++k) {
+        const int e = sched[k];
+        const int n = e & 0xff;
+        if (e & kSchedRestart) {
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int c = 0; c < G::CPL; ++c) S[i][c] = R0[i][c];
+        }
+        float pk[G::RPL], pq[G::RPL];
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i) pk[i] = pq[i] = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < G::NC4; ++c4) {
+            const f4 kk = *reinterpret_cast<const f4 *>(ks + n * D + 64 * c4 + 4 * cg);
+            const f4 qq = *reinterpret_cast<const f4 *>(qs + n * D + 64 * c4 + 4 * cg);
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    pk[i] += S[i][4 * c4 + e2] * kk[e2];
+                    pq[i] += S[i][4 * c4 + e2] * qq[e2];
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i) {
+            pk[i] = row16_sum(pk[i]);
+            pq[i] = row16_sum(pq[i]);
+        }
+        const f4 sc = *reinterpret_cast<const f4 *>(rbk + n * 4);
+        const float rho = sc[0], bet = sc[1], kq = sc[2];
+        const float *vsrc = vs + n * D + wih * G::RPW + rg * G::RPL;
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i) {
+            const float u = bet * (vsrc[i] - rho * pk[i]);
+            pq[i] = rho * pq[i] + kq * u;
+            pk[i] = u;
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < G::NC4; ++c4) {
+            const f4 kk = *reinterpret_cast<const f4 *>(ks + n * D + 64 * c4 + 4 * cg);
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2)
+                    S[i][4 * c4 + e2] = __builtin_fmaf(pk[i], kk[e2], S[i][4 * c4 + e2] * rho);
+        }
+        if (e & kSchedEmit) {
+            if (cg == 0) {
+                float *od = os + n * D + wih * G::RPW + rg * G::RPL;
+#pragma unroll
+                for (int i = 0; i < G::RPL; ++i) od[i] = pq[i];
+            }
+            float *cp = cap_base + (size_t)n * cap_nstride;
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int c4 = 0; c4 < G::NC4; ++c4) {
+                    const f4 v = {S[i][4 * c4], S[i][4 * c4 + 1], S[i][4 * c4 + 2], S[i][4 * c4 + 3]};
+                    __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(cp + (size_t)(4 * i) * D + 64 * c4));
+                }
+        }
+    }
+    __syncthreads();
+
+    // ================= epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) =================
+    constexpr int EPL = D / 16;
+    const int grp = tid >> 4, ngrp = nthr >> 4;
+#pragma unroll 1
+    for (int n = grp; n < T; n += ngrp) {
+        const float *osrc = os + n * D;
+        float ov[EPL];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            ov[e] = osrc[G::perm(cg * EPL + e)];
+            ss += ov[e] * ov[e];
+        }
+        ss = row16_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+        const size_t base = (((size_t)b * T + n) * a.n_vh + h) * D + cg * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float zz = load_act<ACT_BF16>(a.z, base + e);
+            const float y = ov[e] * inv * a.norm_w[cg * EPL + e] * (zz * sigmoid_f(zz));
+            if constexpr (OUT_BF16)
+                static_cast<uint16_t *>(a.out)[base + e] = f32_to_bf16(y);
+            else
+                static_cast<float *>(a.out)[base + e] = y;
+        }
+    }
+}
+
+size_t verify_tree_lds_bytes(int d, int T, bool act_bf16)
+{
+    if (T < 1 || T > kTreeMaxNodes) return (size_t)-1;
+    if (d == 128) return act_bf16 ? TreeLds<128, uint16_t>::total(T) : TreeLds<128, float>::total(T);
+    return act_bf16 ? TreeLds<64, uint16_t>::total(T) : TreeLds<64, float>::total(T);
+}
+
+template <int D, bool AB, bool OB, bool QKN>
+static hipError_t launch_tree_t(const VerifyArgs &a, hipStream_t stream)
+{
+    const size_t lds = verify_tree_lds_bytes(D, a.T, AB);
+    hipLaunchKernelGGL((verify_tree_kernel<D, AB, OB, QKN>), dim3(a.n_batch * a.n_vh), dim3(WavesPerHead<D>::value * 64),
+                       lds, stream, a);
+    return hipGetLastError();
+}
+template <int D, bool AB, bool OB>
+static hipError_t launch_tree_q(const VerifyArgs &a, const LaunchCfg &c, hipStream_t s)
+{
+    return c.qk_norm ? launch_tree_t<D, AB, OB, true>(a, s) : launch_tree_t<D, AB, OB, false>(a, s);
+}
+template <int D, bool AB>
+static hipError_t launch_tree_o(const VerifyArgs &a, const LaunchCfg &c, hipStream_t s)
+{
+    return c.out_bf16 ? launch_tree_q<D, AB, true>(a, c, s) : launch_tree_q<D, AB, false>(a, c, s);
+}
+template <int D>
+static hipError_t launch_tree_a(const VerifyArgs &a, const LaunchCfg &c, hipStream_t s)
+{
+    return c.act_bf16 ? launch_tree_o<D, true>(a, c, s) : launch_tree_o<D, false>(a, c, s);
+}
+
+hipError_t launch_verify_tree(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream)
+{
+    if (a.d == 128) return launch_tree_a<128>(a, c, stream);
+    if (a.d == 64) return launch_tree_a<64>(a, c, stream);
+    return hipErrorInvalidValue;
+}
 
 }  // namespace gdn

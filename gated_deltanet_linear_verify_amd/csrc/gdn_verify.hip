@@ -26,37 +26,12 @@
 // epilogue only read LDS and only store to global memory.  One launch covers up to 16 tokens;
 // longer chains are consecutive launches that pick up the state the previous one left.
 #include "gdn_device.h"
+#include "gdn_geo.h"
 #include "gdn_internal.h"
 
 #include <type_traits>
 
 namespace gdn {
-
-template <int D, int NW>
-struct Geo {
-    static constexpr int RPL = D / (NW * 4);  // state rows per lane
-    static constexpr int CPL = D / 16;        // state columns per lane
-    static constexpr int NC4 = CPL / 4;       // float4 column chunks per lane
-    static constexpr int RPW = 4 * RPL;       // rows per wave
-    static_assert(RPL >= 1 && NC4 >= 1, "bad geometry");
-    // LDS position of natural row r in the per-lane-contiguous order used for v and o.
-    __device__ static int perm(int r)
-    {
-        const int w = r / RPW, rem = r % RPW;
-        return w * RPW + (rem & 3) * RPL + (rem >> 2);
-    }
-};
-
-template <int D>
-struct WavesPerHead;
-template <>
-struct WavesPerHead<128> {
-    static constexpr int value = 4;
-};
-template <>
-struct WavesPerHead<64> {
-    static constexpr int value = 2;
-};
 
 // Capture stores are nontemporal: plain stores leave ~2 GB of dirty lines in L2 / Infinity Cache
 // that the next kernel (the rollback) pays to write back; measured on MI355X, the verify +
@@ -220,7 +195,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
             }
             for (int t = 0; t < nt; ++t) {
                 const float x3 = to_f32(raw[t * nch + lc]);
-                float y = w[0] * x0 + w[1] * x1 + w[2] * x2 + w[3] * x3;
+                float y = conv4(w, x0, x1, x2, x3);
                 if constexpr (QKN) y = y * sigmoid_f(y);
                 dst[t * D] = y;
                 if constexpr (CAP) cc[(size_t)(t0 + t + 3) * C] = x3;

@@ -1,0 +1,174 @@
+"""GPU parity of tree verify (and tree-mode rollback) against the fp64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+
+from gated_deltanet_linear_verify_amd import workloads as W
+from oracle import ref
+from tests.gpu_util import out_err, rel_err, say, to_np, tol_for
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_linear_verify_amd import gdn
+    gdn.lib()
+
+
+def _mods():
+    from gated_deltanet_linear_verify_amd import device, gdn
+    return device, gdn
+
+
+def _tree_upload(shape, inp, **kw):
+    device, gdn = _mods()
+    return device.upload(shape, inp, mode=gdn.GDN_TREE, **kw)
+
+
+def _check_tree(shape, inp, d, units=None, flags=0):
+    """Node states, node outputs and per-node conv states against the oracle."""
+    o = ref.tree_units(shape, inp, units, flags=flags)
+    cap = d["cap_ssm"]
+    out = to_np(d["out"])
+    worst_s, worst_o = 0.0, 0.0
+    ub, uh = o["units"]
+    for u in range(len(ub)):
+        b, h = int(ub[u]), int(uh[u])
+        s = int(inp["slot_ids"][b])
+        c = to_np(cap[s, :, h])
+        for i in range(shape.n_tok):
+            worst_s = max(worst_s, rel_err(c[i], o["cap"][u, i]))
+            worst_o = max(worst_o, out_err(shape, out[b, i, h], o["y"][u, i]))
+    cc = to_np(d["cap_conv"])
+    expect_cc = ref.tree_conv(shape, inp)
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        np.testing.assert_array_equal(cc[s, :shape.n_tok], expect_cc[b])
+    say(f"  tree {W.describe(shape)} worst rel err state {worst_s:.2e} out {worst_o:.2e}")
+    tol = tol_for(shape)
+    assert worst_s <= tol and worst_o <= tol
+
+
+TREE_CASES = {
+    "tiny_fp32_depth3": (W.shape_with(W.TINY_VERIFY, n_tok=12, n_pool=2, n_batch=2), 3, 0),
+    "bf16_d128_depth8": (W.shape_with(W.TREE_VERIFY, n_pool=3, n_batch=2, n_tok=40), 8, 0),
+    "bf16_d128_64_nodes": (W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=1), 8, 0),
+    "deep_comb": (W.shape_with(W.TINY_VERIFY, n_tok=30, act_dtype=W.BF16, out_dtype=W.BF16), 64, 0),
+    "qk_norm_flag": (W.shape_with(W.TREE_VERIFY, n_pool=1, n_batch=1, n_tok=20), 5, 1),
+}
+
+
+@pytest.mark.parametrize("name", list(TREE_CASES))
+def test_tree_parity(name):
+    shape, depth, flags = TREE_CASES[name]
+    say(f"[tree parity] {name}")
+    device, gdn = _mods()
+    inp = W.make_tree_inputs(shape, 0)
+    rng = np.random.default_rng(5)
+    inp["parent"] = np.stack([W.random_tree(rng, shape.n_tok, depth) for _ in range(shape.n_batch)])
+    d = _tree_upload(shape, inp, flags=(gdn.GDN_F_QK_NORM_SILU if flags else 0))
+    st0 = d["state"].clone()
+    cs0 = d["conv_state"].clone()
+    device.verify_tree(d)
+    torch.cuda.synchronize()
+    # tree verify leaves the committed state alone
+    assert torch.equal(d["state"], st0) and torch.equal(d["conv_state"], cs0)
+    _check_tree(shape, inp, d, flags=flags)
+
+
+def test_tree_full_size_sampled():
+    """The 8-slot, 64-node tree workload at full size: sampled (slot, head) units."""
+    shape = W.TREE_VERIFY
+    device, gdn = _mods()
+    inp = W.make_tree_inputs(shape, 0)
+    d = _tree_upload(shape, inp)
+    device.verify_tree(d)
+    torch.cuda.synchronize()
+    _check_tree(shape, inp, d, units=ref.sample_units(shape, 12))
+
+
+def test_chain_shaped_tree_equals_chain_verify_bitwise():
+    shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=2, n_batch=2, n_tok=16)
+    device, gdn = _mods()
+    inp = W.make_inputs(shape, 3)
+    inp["parent"] = np.stack([W.chain_parents(shape.n_tok)] * shape.n_batch)
+    t = _tree_upload(shape, inp)
+    device.verify_tree(t)
+    c = device.upload(shape, inp)
+    device.verify(c)
+    torch.cuda.synchronize()
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        assert torch.equal(t["cap_ssm"][s], c["cap_ssm"][s])
+    assert torch.equal(t["out"], c["out"])
+    # per-node conv state of a chain = rows i+1 .. i+3 of the chain's conv window
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        for i in range(shape.n_tok):
+            assert torch.equal(t["cap_conv"][s, i], c["cap_conv"][s, i + 1:i + 4])
+
+
+def test_tree_rollback_equals_chain_along_accepted_path():
+    """Commit an accepted node with gdn_rollback (tree mode): state and conv state equal a chain
+    verify of the node's root path, bit for bit."""
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=3, n_batch=2, n_tok=48)
+    device, gdn = _mods()
+    inp = W.make_tree_inputs(shape, 7)
+    t = _tree_upload(shape, inp)
+    device.verify_tree(t)
+    torch.cuda.synchronize()
+    for b in range(shape.n_batch):
+        s = int(inp["slot_ids"][b])
+        a = int(inp["accepted"][b])
+        gdn.gdn_rollback(t["capture"], s, a)
+        path = []
+        n = a
+        while n >= 0:
+            path.append(n)
+            n = int(inp["parent"][b, n])
+        path.reverse()
+        say(f"  slot {s} accepted node {a}, path length {len(path)}")
+        sub = W.shape_with(shape, n_tok=len(path), n_batch=1)
+        sinp = dict(inp)
+        for k in ("qkv", "z", "alpha", "beta"):
+            sinp[k] = np.ascontiguousarray(inp[k][b:b + 1, path])
+        sinp["slot_ids"] = inp["slot_ids"][b:b + 1]
+        c = device.upload(sub, sinp)
+        device.verify(c)
+        torch.cuda.synchronize()
+        assert torch.equal(t["state"][s], c["state"][s])
+        assert torch.equal(t["conv_state"][s], c["conv_state"][s])
+
+
+def test_tree_multiple_roots_and_malformed_parents():
+    """Nodes with parent -1 start from the committed state; a malformed parent is treated as -1
+    (or rejected with GDN_F_CHECK_INDICES before anything runs)."""
+    shape = W.shape_with(W.TINY_VERIFY, n_tok=10, n_pool=2, n_batch=1)
+    device, gdn = _mods()
+    inp = W.make_tree_inputs(shape, 9)
+    par = np.array([[-1, 0, 1, -1, 3, 0, 9, 2, -7, 4]], dtype=np.int32)  # node 6 -> 9, node 8 -> -7
+    inp["parent"] = par
+    d = _tree_upload(shape, inp)
+    device.verify_tree(d)
+    torch.cuda.synchronize()
+    fixed = dict(inp)
+    fixed["parent"] = np.array([[-1, 0, 1, -1, 3, 0, -1, 2, -1, 4]], dtype=np.int32)
+    _check_tree(shape, fixed, d)
+    e = _tree_upload(shape, inp, flags=gdn.GDN_F_CHECK_INDICES)
+    with pytest.raises(gdn.GdnError) as ei:
+        device.verify_tree(e)
+    assert ei.value.code == gdn.GDN_ERR_RANGE
+
+
+def test_tree_too_many_nodes_rejected():
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=1, n_batch=1, n_tok=65)
+    device, gdn = _mods()
+    inp = W.make_tree_inputs(shape, 1)
+    d = _tree_upload(shape, inp)
+    with pytest.raises(gdn.GdnError) as ei:
+        device.verify_tree(d)
+    assert ei.value.code == gdn.GDN_ERR_SHAPE
