@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "GDN verify tokens/s (64 slots, K+1=16) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_FLOPS = 2.5e15  # dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_multi_slot_verify.json")
 VERIFY_SRC = os.path.join(ROOT, "gated_deltanet_linear_verify_amd", "csrc", "gdn_verify.hip")
 
@@ -118,6 +119,17 @@ def components(args) -> dict:
     out["single_slot_verify"] = {"workload": "1 slot x 16 tokens, 16/32 heads, d=128, bf16", "us": us,
                                  "tokens_per_s": s.n_tok / (us * 1e-6),
                                  "hbm_gbps": bytemodel.verify_bytes(s) / (us * 1e-6) / 1e9}
+    del d
+    # chunked prefill: one 8192-token sequence
+    s = W.CHUNKED_PREFILL
+    d = device.upload(s, W.make_inputs(s, 0), capture=False)
+    us = time_launches(lambda: device.prefill(d), 10)
+    fl = bytemodel.prefill_flops(s)
+    out["chunked_prefill"] = {"workload": "1 slot x 8192 tokens, 16/32 heads, d=128, bf16, chunk 64",
+                              "us": us, "tokens_per_s": s.n_tok / (us * 1e-6),
+                              "hbm_gbps": bytemodel.prefill_bytes(s) / (us * 1e-6) / 1e9,
+                              "algorithmic_flops": fl, "tflops": fl / (us * 1e-6) / 1e12,
+                              "mfma_util_vs_bf16_peak": fl / (us * 1e-6) / PEAK_BF16_FLOPS}
     del d
     torch.cuda.empty_cache()
     return out

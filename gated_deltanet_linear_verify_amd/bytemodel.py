@@ -62,3 +62,15 @@ def verify_flops(s: Shape) -> int:
     """~7 d^2 flops per (slot, head, token) for the recurrence (S k, S q, rank-1 update with the
     decay) plus 8 per channel per token for the conv."""
     return s.n_batch * s.n_tok * (s.n_vh * 7 * s.d_v * s.d_k + 8 * s.conv_channels)
+
+
+PREFILL_CHUNK = 64
+
+
+def prefill_flops(s: Shape, chunk: int = PREFILL_CHUNK) -> int:
+    """Dense products of the chunked (WY / UT) form, each counted once as 2 m n k, per token and
+    value head: K K^T and Q K^T (2 C d_k each), T Y and P U (2 C d_v each), K S^T, Q S^T and the
+    state update U^T K (2 d_k d_v each), plus the triangular inverse (C^2 / 3)."""
+    C, dk, dv = chunk, s.d_k, s.d_v
+    per_tok = 4 * C * dk + 4 * C * dv + 6 * dk * dv + (C * C) // 3
+    return s.n_tok * s.n_vh * per_tok

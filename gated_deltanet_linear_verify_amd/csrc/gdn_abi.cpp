@@ -137,6 +137,12 @@ gdn::VerifyArgs make_args(const gdn_dims &d, int n_tok, int n_batch)
 
 }  // namespace
 
+namespace gdn {
+int abi_fail(int code, const char *msg) { return fail(code, "%s", msg); }
+int abi_ok() { return ok(); }
+int abi_check_dims(const gdn_dims *d) { return check_dims(d); }
+}  // namespace gdn
+
 GDN_API int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, const void *qkv, const void *z,
                        const void *alpha, const void *beta, const float *A_log, const float *dt_bias,
                        const float *conv_w, const float *norm_w, const gdn_capture *capture, void *out,

@@ -53,4 +53,18 @@ hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream);
 
 hipError_t launch_fill_zero(float *p, size_t n, hipStream_t stream);
 
+struct PrefillArgs {
+    int32_t n_kh, n_vh, d, T, C, slot;
+    float eps;
+    float *state, *conv_state;
+    const void *qkv, *z, *alpha, *beta;
+    const float *A_log, *dt_bias, *conv_w, *norm_w;
+    void *out;
+    float *o_ws;  // workspace: [T][H_v][d_v] fp32 readout before the norm
+};
+// Chunked prefill: a chunk-scan kernel over H_v * (d / 16) workgroups, then the norm epilogue.
+hipError_t launch_prefill(const PrefillArgs &a, const LaunchCfg &c, hipStream_t stream);
+size_t prefill_workspace_bytes(int d, int n_vh, int T);
+size_t prefill_lds_bytes(int d, bool act_bf16);
+
 }  // namespace gdn

@@ -72,3 +72,17 @@ def verify_tree(d: dict, stream=None) -> None:
     gdn.gdn_verify_tree(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"],
                         d["beta"], d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], d["parent"],
                         d["capture"], d["out"], T, d["slot_ids"], B, stream)
+
+
+def prefill(d: dict, stream=None) -> None:
+    """gdn_prefill of every token of the uploaded single-entry inputs into slot slot_ids[0]."""
+    T = d["qkv"].shape[1]
+    need = gdn.gdn_prefill_workspace_bytes(d["dims"], T)
+    ws = d.get("workspace")
+    if ws is None or ws.numel() * 4 < need:
+        ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=d["qkv"].device)
+        d["workspace"] = ws
+    slot = int(d["slot_ids"][0].item()) if "slot" not in d else d["slot"]
+    gdn.gdn_prefill(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"], d["beta"],
+                    d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], d["out"], T, slot, ws,
+                    ws.numel() * 4, stream)

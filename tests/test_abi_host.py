@@ -108,3 +108,30 @@ def test_capture_bytes_match_layout():
     ssm_t, conv_t = gdn.capture_bytes(d, 64, gdn.GDN_TREE)
     assert conv_t == 4 * 64 * 64 * 3 * 8192
     assert gdn.capture_bytes(d, 0, gdn.GDN_CHAIN) == (0, 0)
+
+
+def test_prefill_validation():
+    """gdn_prefill rejects bad arguments before any launch; workspace size is T * H_v * d_v fp32."""
+    L = _lib_or_skip()
+    d = gdn.make_dims(W.CHUNKED_PREFILL)
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(d), 8192) == 4 * 8192 * 32 * 128
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(d), 0) == 0
+    big = 1 << 40
+    args = [FAKE] * 11  # state .. out
+
+    def call(dims, n_tok=64, slot=0, ws=FAKE, ws_bytes=big, a=args):
+        return L.gdn_prefill(ctypes.byref(dims), *a, n_tok, slot, ws, ws_bytes, None)
+
+    assert call(d, n_tok=0) == gdn.GDN_ERR_RANGE
+    assert call(d, slot=1) == gdn.GDN_ERR_RANGE
+    assert call(d, slot=-1) == gdn.GDN_ERR_RANGE
+    assert call(d, ws=None) == gdn.GDN_ERR_ARG
+    assert call(d, ws_bytes=4 * 64 * 32 * 128 - 4) == gdn.GDN_ERR_ARG
+    assert call(d, a=[ctypes.c_void_p(0x1004)] + args[1:]) == gdn.GDN_ERR_ARG
+    assert call(d, a=args[:3] + [None] + args[4:]) == gdn.GDN_ERR_ARG
+    f32 = gdn.make_dims(W.shape_with(W.CHUNKED_PREFILL, act_dtype=W.F32, out_dtype=W.F32))
+    assert call(f32) == gdn.GDN_ERR_SHAPE
+    assert "LDS" in gdn.last_error()
+    bad = gdn.make_dims(W.CHUNKED_PREFILL)
+    bad.d_k = 96
+    assert call(bad) == gdn.GDN_ERR_SHAPE
