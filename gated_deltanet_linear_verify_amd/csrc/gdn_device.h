@@ -74,6 +74,16 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds)
 #endif
 }
 
+// Workgroup barrier that orders LDS only: no wait on the vector-memory counter, so outstanding
+// global stores (and prefetch loads) stay in flight across it.  Only valid where threads of the
+// workgroup exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Depthwise causal conv tap sum, oldest input first; tap 3 multiplies the current token.  One
 // fixed rounding order so every kernel produces identical bits for identical windows.
 __device__ __forceinline__ float conv4(f4 w, float x0, float x1, float x2, float x3)

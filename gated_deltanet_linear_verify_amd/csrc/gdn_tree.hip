@@ -8,9 +8,10 @@
 // accepted node; the committed state and conv state are left untouched.
 //
 // One workgroup per (batch entry, value head).  A prologue stages the raw q|k|v rows of all nodes
-// in LDS (global_load_lds), computes every node's conv output, gate, beta and k.q into LDS, and
+// in LDS (global_load_lds), computes every node's conv output, gate and beta into LDS, and
 // builds a depth-first processing schedule.  The node loop then runs in DFS order: a node whose
-// parent is the node just processed continues from the state in registers; any other node
+// parent is the node just processed continues from the state in registers (each step is
+// Geo::step, the same arithmetic as the chain kernel); any other node
 // restarts from a register copy of the committed state and re-runs its parent's root path
 // (compute only, nothing stored) before its own step.  No state is ever re-read from memory, so
 // the loop never waits on the memory counter that the capture stores occupy.
@@ -227,42 +228,6 @@ __global__ __launch_bounds__(256) void verify_tree_kernel(VerifyArgs a)
         *nsched = cnt;
     }
     __syncthreads();
-    // ---- optional q/k scaling and k . q of every node (one wave per node)
-    for (int n = wave; n < T; n += NW) {
-        constexpr int E = D / 64;
-        float qv[E], kv[E];
-        float dq = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            qv[e] = qs[n * D + lane + 64 * e];
-            kv[e] = ks[n * D + lane + 64 * e];
-        }
-        if constexpr (QKN) {
-            float nq = 0.f, nk = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                nq += qv[e] * qv[e];
-                nk += kv[e] * kv[e];
-            }
-            nq = wave_sum(nq);
-            nk = wave_sum(nk);
-            const float sq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)D);
-            const float sk = 1.0f / sqrtf(nk + 1e-6f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                qv[e] *= sq;
-                kv[e] *= sk;
-                qs[n * D + lane + 64 * e] = qv[e];
-                ks[n * D + lane + 64 * e] = kv[e];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) dq += qv[e] * kv[e];
-        dq = wave_sum(dq);
-        if (lane == 0) rbk[n * 4 + 2] = dq;
-    }
-    __syncthreads();
-
     // ================= the node loop in schedule order =================
     float S[G::RPL][G::CPL];
 #pragma unroll
@@ -283,49 +248,14 @@ __global__ __launch_bounds__(256) void verify_tree_kernel(VerifyArgs a)
 #pragma unroll
                 for (int c = 0; c < G::CPL; ++c) S[i][c] = R0[i][c];
         }
-        float pk[G::RPL], pq[G::RPL];
-#pragma unroll
-        for (int i = 0; i < G::RPL; ++i) pk[i] = pq[i] = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < G::NC4; ++c4) {
-            const f4 kk = *reinterpret_cast<const f4 *>(ks + n * D + 64 * c4 + 4 * cg);
-            const f4 qq = *reinterpret_cast<const f4 *>(qs + n * D + 64 * c4 + 4 * cg);
-#pragma unroll
-            for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    pk[i] += S[i][4 * c4 + e2] * kk[e2];
-                    pq[i] += S[i][4 * c4 + e2] * qq[e2];
-                }
-        }
-#pragma unroll
-        for (int i = 0; i < G::RPL; ++i) {
-            pk[i] = row16_sum(pk[i]);
-            pq[i] = row16_sum(pq[i]);
-        }
         const f4 sc = *reinterpret_cast<const f4 *>(rbk + n * 4);
-        const float rho = sc[0], bet = sc[1], kq = sc[2];
-        const float *vsrc = vs + n * D + wih * G::RPW + rg * G::RPL;
-#pragma unroll
-        for (int i = 0; i < G::RPL; ++i) {
-            const float u = bet * (vsrc[i] - rho * pk[i]);
-            pq[i] = rho * pq[i] + kq * u;
-            pk[i] = u;
-        }
-#pragma unroll
-        for (int c4 = 0; c4 < G::NC4; ++c4) {
-            const f4 kk = *reinterpret_cast<const f4 *>(ks + n * D + 64 * c4 + 4 * cg);
-#pragma unroll
-            for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2)
-                    S[i][4 * c4 + e2] = __builtin_fmaf(pk[i], kk[e2], S[i][4 * c4 + e2] * rho);
-        }
+        float o[G::RPL];
+        G::template step<QKN>(S, ks + n * D, qs + n * D, vs + n * D + wih * G::RPW + rg * G::RPL, sc[0], sc[1], cg, o);
         if (e & kSchedEmit) {
             if (cg == 0) {
                 float *od = os + n * D + wih * G::RPW + rg * G::RPL;
 #pragma unroll
-                for (int i = 0; i < G::RPL; ++i) od[i] = pq[i];
+                for (int i = 0; i < G::RPL; ++i) od[i] = o[i];
             }
             float *cp = cap_base + (size_t)n * cap_nstride;
 #pragma unroll

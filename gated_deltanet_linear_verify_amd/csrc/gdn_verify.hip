@@ -11,9 +11,9 @@
 //   cols  of chunk c4   : 64*c4 + 4*cg + e,  e in [0,4)             (CPL = d/16 columns)
 // so one float4 store instruction covers 4 consecutive rows x 64 contiguous columns: every
 // 128-byte line of the per-token capture is written whole by a single instruction.  Both
-// contractions over the key index (S k and S q) finish with a 16-lane DPP sum.
+// contractions over the key index (S k, S q and k . q) finish with a 16-lane DPP sum.
 //
-// Per token (Yang, Kautz & Hatamizadeh 2024, gated delta rule):
+// Per token (Yang, Kautz & Hatamizadeh 2024, gated delta rule; Geo::step, shared with the tree kernel):
 //   p = S k,  u = beta (v - rho p),  S <- rho S + u k^T,  o = rho (S_old q) + (k.q) u  (= S_new q)
 // The capture of S after every token (lucebox-hub internal.h, struct TargetCache,
 // ssm_intermediate) streams out while the next token is computed; the RMS norm + SiLU(z)
@@ -57,7 +57,7 @@ struct VerifyLds {
         return sizeof(float) * (2 * TT * D + (size_t)R * TT * D)  // ks, qs, vs
                + region(R)                                          // os, aliased by the raw rows
                + (size_t)R * TT * D * sizeof(act_t)                 // zs
-               + sizeof(float) * (2 * (size_t)R * TT + TT + D);      // rb, kqs, norm_w
+               + sizeof(float) * (2 * (size_t)R * TT + TT + D);      // rb, (pad), norm_w
     }
 };
 
@@ -92,8 +92,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     act_t *raw = reinterpret_cast<act_t *>(os);         // [TT][nch]    staged qkv rows (prologue only)
     act_t *zs = reinterpret_cast<act_t *>(reinterpret_cast<unsigned char *>(os) + L::region(R));  // [TT][R*D]
     float *rb = reinterpret_cast<float *>(zs + R * TT * D);  // [R][TT][2]   (rho, beta)
-    float *kqs = rb + R * TT * 2;                              // [TT]         k . q
-    float *nws = kqs + TT;                                     // [D]          norm_w
+    float *nws = rb + R * TT * 2 + TT;                         // [D]          norm_w
 
     const int C = a.C;
     const int T = a.T;    // tokens of the whole call: the row stride of qkv, z, alpha, beta, out
@@ -211,42 +210,6 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
         }
     }
     __syncthreads();
-    // ---- optional q/k scaling, and k . q (one wave per token)
-    for (int t = wave; t < nt; t += nwaves) {
-        constexpr int E = D / 64;
-        float qv[E], kv[E];
-        float dq = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            qv[e] = qs[t * D + lane + 64 * e];
-            kv[e] = ks[t * D + lane + 64 * e];
-        }
-        if constexpr (QKN) {
-            float nq = 0.f, nk = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                nq += qv[e] * qv[e];
-                nk += kv[e] * kv[e];
-            }
-            nq = wave_sum(nq);
-            nk = wave_sum(nk);
-            const float sq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)D);
-            const float sk = 1.0f / sqrtf(nk + 1e-6f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                qv[e] *= sq;
-                kv[e] *= sk;
-                qs[t * D + lane + 64 * e] = qv[e];
-                ks[t * D + lane + 64 * e] = kv[e];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) dq += qv[e] * kv[e];
-        dq = wave_sum(dq);
-        if (lane == 0) kqs[t] = dq;
-    }
-    __syncthreads();
-
     // ================= the recurrence, state in registers =================
     // Only LDS reads and capture stores from here on: no wait on the memory counter, which the
     // capture stores occupy.
@@ -258,50 +221,14 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     }
 #pragma unroll 1
     for (int t = 0; t < nt; ++t) {
-        // p = S k and S q, accumulated chunk by chunk to keep few values live
-        float pk[G::RPL], pq[G::RPL];
-#pragma unroll
-        for (int i = 0; i < G::RPL; ++i) pk[i] = pq[i] = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < G::NC4; ++c4) {
-            const f4 kk = *reinterpret_cast<const f4 *>(ks + t * D + 64 * c4 + 4 * cg);
-            const f4 qq = *reinterpret_cast<const f4 *>(qs + t * D + 64 * c4 + 4 * cg);
-#pragma unroll
-            for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pk[i] += S[i][4 * c4 + e] * kk[e];
-                    pq[i] += S[i][4 * c4 + e] * qq[e];
-                }
-        }
-#pragma unroll
-        for (int i = 0; i < G::RPL; ++i) {
-            pk[i] = row16_sum(pk[i]);
-            pq[i] = row16_sum(pq[i]);
-        }
         const f2 rbv = *reinterpret_cast<const f2 *>(rb + (hl * TT + t) * 2);
-        const float rho = rbv[0], be = rbv[1];
-        const float kq = kqs[t];
-        const float *vsrc = vs + (hl * TT + t) * D + wih * G::RPW + rg * G::RPL;
-#pragma unroll
-        for (int i = 0; i < G::RPL; ++i) {
-            const float u = be * (vsrc[i] - rho * pk[i]);
-            pq[i] = rho * pq[i] + kq * u;  // o = S_new q for row i
-            pk[i] = u;
-        }
+        float o[G::RPL];
+        G::template step<QKN>(S, ks + t * D, qs + t * D, vs + (hl * TT + t) * D + wih * G::RPW + rg * G::RPL, rbv[0],
+                              rbv[1], cg, o);
         if (cg == 0) {
             float *od = os + (hl * TT + t) * D + wih * G::RPW + rg * G::RPL;
 #pragma unroll
-            for (int i = 0; i < G::RPL; ++i) od[i] = pq[i];
-        }
-#pragma unroll
-        for (int c4 = 0; c4 < G::NC4; ++c4) {
-            const f4 kk = *reinterpret_cast<const f4 *>(ks + t * D + 64 * c4 + 4 * cg);
-#pragma unroll
-            for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)  // S <- rho S + u k^T, scaled in place then accumulated
-                    S[i][4 * c4 + e] = __builtin_fmaf(pk[i], kk[e], S[i][4 * c4 + e] * rho);
+            for (int i = 0; i < G::RPL; ++i) od[i] = o[i];
         }
         if constexpr (CAP) {
             float *cp = cap_ptr + (size_t)t * cap_tstride;
@@ -327,7 +254,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
                 *reinterpret_cast<f4 *>(sp + off + (uint32_t)(4 * i * D + 64 * c4)) = v;
             }
     }
-    __syncthreads();
+    lds_barrier();  // o of every head is in LDS; the capture stores stay in flight
 
     // ================= epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) =================
     constexpr int EPL = D / 16;  // 16 lanes per (head, token) row
