@@ -74,14 +74,28 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds)
 #endif
 }
 
-// Workgroup barrier that orders LDS only: no wait on the vector-memory counter, so outstanding
-// global stores (and prefetch loads) stay in flight across it.  Only valid where threads of the
-// workgroup exchange data through LDS alone.
+// Workgroup barrier for data exchanged through LDS by ds_read / ds_write: waits for this wave's
+// own LDS operations, then meets the other waves.  No wait on the vector-memory counter, so
+// outstanding global stores and global_load_lds prefetches stay in flight across it; LDS filled
+// by global_load_lds must be waited for explicitly (s_waitcnt vmcnt) before the barrier that
+// publishes it.  The memory clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier()
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+}
+
+// Same, 4 bytes per lane: lane i lands at lds + 4 i of the first active lane.  The global address
+// must be 4-byte aligned.
+__device__ __forceinline__ void lds_dma4(const void *g, void *lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+#else
+    (void)g;
+    (void)lds;
+#endif
 }
 
 // Depthwise causal conv tap sum, oldest input first; tap 3 multiplies the current token.  One

@@ -33,6 +33,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kChunk = 64;  // tokens per chunk
 constexpr int kDB = 16;     // value rows per workgroup
 constexpr int kPThreads = 256;
+constexpr int kCP = kChunk + 4;  // padded row stride of the chunk x chunk matrices
 
 __device__ __forceinline__ f4 mfma16(bf16x8 a, bf16x8 b, f4 c)
 {
@@ -102,36 +103,48 @@ __device__ __forceinline__ f4 mma8(const float (&a)[8], const float (&b)[8], f4 
     return acc;
 }
 
-// acc += A(16x32 at row r0, col k0 of a row-major [.][lda] matrix) * B, where B (32x16) is given
-// transposed: Bt row-major [n][ldb], block at row n0, col k0.
-template <bool F32>
-__device__ __forceinline__ f4 mma_tile(const float *A, int lda, int r0, const float *Bt, int ldb, int n0, int k0,
-                                       f4 acc, int lane)
+// Row-major [rows][D] fp32 matrix with its 8-float groups XOR-swizzled by the row index, so the
+// 16 rows that one MFMA operand load touches fall on different LDS banks.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c)
 {
-    float av[8], bv[8];
-    load8(A + (r0 + (lane & 15)) * lda + k0 + (lane >> 4) * 8, av);
-    load8(Bt + (n0 + (lane & 15)) * ldb + k0 + (lane >> 4) * 8, bv);
-    return mma8<F32>(av, bv, acc);
+    constexpr int NG = D / 8;
+    return r * D + ((((c >> 3) ^ r) & (NG - 1)) << 3) + (c & 7);
+}
+
+// 16x16 fp32 block product on the fp32 MFMA: acc += X(16x16 at ld, rows r0, cols c0) *
+// Y(16x16, rows k0.., cols n0..), both in kCP-padded LDS matrices.  Lane l supplies X[l%16][4s + l/16]
+// and Y[4s + l/16][l%16] for step s; the result is in the usual layout (rows 4 (l/16) + i, col l%16).
+__device__ __forceinline__ f4 blk16(const float *X, int xr0, int xc0, const float *Y, int yr0, int yc0, f4 acc,
+                                    int lane)
+{
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int kk = 4 * st + (lane >> 4);
+        acc = mfma4f32(X[(xr0 + (lane & 15)) * kCP + xc0 + kk], Y[(yr0 + kk) * kCP + yc0 + (lane & 15)], acc);
+    }
+    return acc;
 }
 
 template <int D, typename act_t>
 struct PrefillLds {
     static constexpr int C = kChunk;
     static constexpr int NCH = 2 * D + kDB;  // q | k | v-block channels
-    static constexpr size_t q = 0;                                   // [C][D]
-    static constexpr size_t k = q + sizeof(float) * C * D;           // [C][D]
-    static constexpr size_t kt = k + sizeof(float) * C * D;          // [D][C]
-    static constexpr size_t vb = kt + sizeof(float) * D * C;         // [C][DB]
-    static constexpr size_t s = vb + sizeof(float) * C * kDB;        // [DB][D]   the state block
-    static constexpr size_t tm = s + sizeof(float) * kDB * D;        // [C][C]    A, then T
-    static constexpr size_t pm = tm + sizeof(float) * C * C;         // [C][C]    scratch, then P
-    static constexpr size_t yt = pm + sizeof(float) * C * C;         // [DB][C]
-    static constexpr size_t ut = yt + sizeof(float) * kDB * C;       // [DB][C]
-    static constexpr size_t work_end = ut + sizeof(float) * kDB * C;
-    static constexpr size_t raw_bytes = sizeof(act_t) * (C + 3) * NCH;  // staged rows, aliases tm..
-    static constexpr size_t sc = (tm + raw_bytes > work_end ? tm + raw_bytes : work_end);
-    static constexpr size_t total = sc + sizeof(float) * 4 * C;      // Gamma, gamma, beta, decay-to-end
+    static constexpr size_t q = 0;                                    // [C][D]    swizzled
+    static constexpr size_t k = q + sizeof(float) * C * D;            // [C][D]    swizzled
+    static constexpr size_t vb = k + sizeof(float) * C * D;           // [C][DB]
+    static constexpr size_t s = vb + sizeof(float) * C * kDB;         // [DB][D]   the state block, swizzled
+    static constexpr size_t tm = s + sizeof(float) * kDB * D;         // [C][kCP]  A, then T
+    static constexpr size_t pm = tm + sizeof(float) * C * kCP;        // [C][kCP]  P
+    static constexpr size_t yt = pm + sizeof(float) * C * kCP;        // [DB][kCP] Y^T
+    static constexpr size_t ut = yt + sizeof(float) * kDB * kCP;      // [DB][kCP] U^T; scratch of the inverse
+    static constexpr size_t hist = ut + sizeof(float) * kDB * kCP;    // [3][NCH]  raw rows before the chunk
+    static constexpr size_t gate = hist + sizeof(float) * 3 * NCH;    // Gamma, gamma, beta, decay [4][C]
+    static constexpr size_t ab = gate + sizeof(float) * 4 * C;        // alpha, beta words [2][C]
+    static constexpr size_t raw = ab + sizeof(uint32_t) * 2 * C;      // [C][NCH]  the chunk's raw rows
+    static constexpr size_t total = raw + sizeof(act_t) * C * NCH;
 };
+static_assert(PrefillLds<128, uint16_t>::total <= 160 * 1024, "bf16 d=128 prefill must fit one CU's LDS");
 
 template <int D, bool ACT_BF16, bool QKN>
 __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
@@ -143,6 +156,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
     constexpr int NCH = L::NCH;
     constexpr int VEC = 16 / (int)sizeof(act_t);
     constexpr int NB = D / kDB;
+    constexpr int QKG = 2 * D / 4;  // q | k channel groups of 4 (one per lane of a conv wave)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int R = a.n_vh / a.n_kh;
 
@@ -155,18 +169,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *Q = reinterpret_cast<float *>(smem + L::q);
     float *K = reinterpret_cast<float *>(smem + L::k);
-    float *Kt = reinterpret_cast<float *>(smem + L::kt);
     float *Vb = reinterpret_cast<float *>(smem + L::vb);
     float *S = reinterpret_cast<float *>(smem + L::s);
     float *Tm = reinterpret_cast<float *>(smem + L::tm);
     float *Pm = reinterpret_cast<float *>(smem + L::pm);
     float *Yt = reinterpret_cast<float *>(smem + L::yt);
     float *Ut = reinterpret_cast<float *>(smem + L::ut);
-    act_t *raw = reinterpret_cast<act_t *>(smem + L::tm);
-    float *Gam = reinterpret_cast<float *>(smem + L::sc);  // Gamma_t
-    float *gam = Gam + C;                                  // gamma_t = exp(Gamma_t)
-    float *bet = gam + C;                                  // beta_t
-    float *dec = bet + C;                                  // exp(Gamma_C - Gamma_t)
+    float *hist = reinterpret_cast<float *>(smem + L::hist);
+    float *Gam = reinterpret_cast<float *>(smem + L::gate);  // Gamma_t
+    float *gam = Gam + C;                                    // gamma_t = exp(Gamma_t)
+    float *bet = gam + C;                                    // beta_t (0 past the end)
+    float *dec = bet + C;                                    // exp(Gamma_C - Gamma_t)
+    uint32_t *abw = reinterpret_cast<uint32_t *>(smem + L::ab);  // the words holding alpha_t, beta_t
+    act_t *raw = reinterpret_cast<act_t *>(smem + L::raw);
 
     const act_t *qkv = static_cast<const act_t *>(a.qkv);
     auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
@@ -176,53 +191,87 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
         else
             return x;
     };
+    // alpha / beta of (token t, head h) sit in the 32-bit word at element (t H_v + h) & ~1 (bf16) or
+    // t H_v + h (fp32); the word never leaves the row because H_v is even for bf16
+    constexpr int EPW = ACT_BF16 ? 2 : 1;  // elements per word
+    const int ab_half = ACT_BF16 ? (h & 1) : 0;
+    auto word_val = [&](uint32_t w) -> float {
+        if constexpr (ACT_BF16)
+            return bf16_to_f32((uint16_t)(ab_half ? (w >> 16) : (w & 0xffffu)));
+        else
+            return __builtin_bit_cast(float, w);
+    };
+    // stage chunk c: raw rows via global_load_lds (lane i lands at the wave's base + 16 i, rows
+    // past the end are skipped) and the alpha / beta words (4-byte global_load_lds, lane t -> word t)
+    auto stage = [&](int c) {
+        const int t0 = c * C, Lc = min(C, T - t0);
+        constexpr int nvr = NCH / VEC;
+        for (int it = tid; it < Lc * nvr; it += kPThreads) {
+            const int r = it / nvr, lc = (it % nvr) * VEC;
+            lds_dma16(qkv + ((size_t)t0 + r) * Cc + gchan(lc), raw + it * VEC);
+        }
+        if (wave < 2 && lane < Lc) {
+            const size_t e = ((size_t)t0 + lane) * a.n_vh + (h & ~(EPW - 1));
+            const void *src = wave == 0 ? a.alpha : a.beta;
+            lds_dma4(static_cast<const unsigned char *>(src) + e * sizeof(act_t), abw + wave * C + lane);
+        }
+    };
 
-    // ---- the state block (rows blk*16 .. +16 of value head h) and the conv taps / conv state
-    const float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
-    for (int i = tid; i < kDB * D / 4; i += kPThreads) reinterpret_cast<f4 *>(S)[i] = reinterpret_cast<const f4 *>(st)[i];
-    constexpr int CPT = (NCH + kPThreads - 1) / kPThreads;
-    f4 wv[CPT];
-    float hist[CPT][3];  // conv window rows before the chunk (conv state for the first chunk)
-    const float *cs = a.conv_state + (size_t)a.slot * 3 * Cc;
+    // ---- prologue: state block, conv taps of this thread's channel groups, conv state
+    // conv taps of this thread's channel groups: q | k (lane -> channels 4 lane .. 4 lane + 3) and v
+    f4 wqk[4], wv[4];
+    {
+        const int lq = lane < QKG ? 4 * lane : 0;
+        const int lv = 2 * D + 4 * (tid & 3);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int lc = tid + j * kPThreads;
-        if (lc < NCH) {
-            const int gc = gchan(lc);
-            wv[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
-#pragma unroll
-            for (int r = 0; r < 3; ++r) hist[j][r] = cs[(size_t)r * Cc + gc];
+        for (int j = 0; j < 4; ++j) {
+            wqk[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lq + j) * 4);
+            wv[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lv + j) * 4);
         }
     }
+    const float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
+    for (int i = tid; i < kDB * D / 4; i += kPThreads) {
+        const int r = (4 * i) / D, c = (4 * i) % D;
+        *reinterpret_cast<f4 *>(S + swz<D>(r, c)) = reinterpret_cast<const f4 *>(st)[i];
+    }
+    const float *cs = a.conv_state + (size_t)a.slot * 3 * Cc;
+    for (int i = tid; i < 3 * NCH; i += kPThreads) hist[i] = cs[(size_t)(i / NCH) * Cc + gchan(i % NCH)];
+    // the upper blocks of A / T and P stay zero for the whole call
+    for (int i = tid; i < C * kCP; i += kPThreads) {
+        Tm[i] = 0.f;
+        Pm[i] = 0.f;
+    }
     const float negA = -expf(a.A_log[h]), dtb = a.dt_bias[h];
+    stage(0);
 
+    // readout tile of wave w: rows t = 16 w + 4 (lane / 16) + r, value row blk*16 + lane % 16
+    f4 o_prev = {0.f, 0.f, 0.f, 0.f};
+    auto store_o = [&](int cc, f4 o) {
+        const int tb = cc * C, Lb = min(C, T - tb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * wave + (lane >> 4) * 4 + r;
+            if (t < Lb) a.o_ws[(((size_t)tb + t) * a.n_vh + h) * D + blk * kDB + (lane & 15)] = o[r];
+        }
+    };
     const int nchunks = (T + C - 1) / C;
 #pragma unroll 1
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C;
         const int Lc = min(C, T - t0);  // valid tokens in this chunk
-        // ================= stage the chunk's raw rows (tokens t0 .. t0+Lc-1) into LDS ============
-        {
-            constexpr int nvr = NCH / VEC;
-            for (int it = tid; it < C * nvr; it += kPThreads) {
-                const int r = it / nvr, lc = (it % nvr) * VEC;
-                if (r < Lc)
-                    lds_dma16(qkv + ((size_t)t0 + r) * Cc + gchan(lc), raw + it * VEC);
-                else
-                    *reinterpret_cast<f4 *>(raw + it * VEC) = f4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        float gl = 0.f, bl = 0.f;
-        if (tid < Lc) {
-            const size_t tok = ((size_t)t0 + tid) * a.n_vh + h;
-            const float al = load_act<ACT_BF16>(a.alpha, tok);
-            bl = load_act<ACT_BF16>(a.beta, tok);
-            gl = negA * softplus_f(al + dtb);
-        }
+        // the loop's memory ops: the previous chunk's readout stores, then this chunk's stage
+        // (both issued a chunk ago), so waiting for everything waits for nothing recent
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
-        // Gamma = inclusive prefix sum of g over the chunk (wave 0); padded tokens have g = 0, beta = 0
+        lds_barrier();
+
+        // ================= gates: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
         if (wave == 0) {
-            float x = gl;
+            float g = 0.f, b = 0.f;
+            if (lane < Lc) {
+                g = negA * softplus_f(word_val(abw[lane]) + dtb);
+                b = word_val(abw[C + lane]);
+            }
+            float x = g;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off);
@@ -230,89 +279,133 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
             }
             Gam[lane] = x;
             gam[lane] = expf(x);
-            bet[lane] = bl;
-            const float gC = __shfl(x, 63);
-            dec[lane] = expf(gC - x);
-        }
-        __syncthreads();
-
-        // ================= conv (one thread per channel) =================
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int lc = tid + j * kPThreads;
-            if (lc < NCH) {
-                const f4 w = wv[j];
-                float x0 = hist[j][0], x1 = hist[j][1], x2 = hist[j][2];
-                for (int t = 0; t < C; ++t) {
-                    const float x3 = to_f32(raw[t * NCH + lc]);
-                    float y = conv4(w, x0, x1, x2, x3);
-                    if constexpr (QKN) y = y * sigmoid_f(y);
-                    if (t >= Lc) y = 0.f;  // padded tokens contribute nothing
-                    if (lc < D) {
-                        Q[t * D + lc] = y;
-                    } else if (lc < 2 * D) {
-                        K[t * D + (lc - D)] = y;
-                        Kt[(lc - D) * C + t] = y;
-                    } else {
-                        Vb[t * kDB + (lc - 2 * D)] = y;
-                    }
-                    // the window of the next chunk starts with this chunk's last three rows
-                    if (t < Lc) {
-                        x0 = x1;
-                        x1 = x2;
-                        x2 = x3;
-                    }
-                }
-                hist[j][0] = x0;
-                hist[j][1] = x1;
-                hist[j][2] = x2;
-            }
-        }
-        __syncthreads();
-        if constexpr (QKN) {  // q, k scaled to unit length (+1e-6), q by d_k^-1/2; one wave per token
-            for (int t = wave; t < Lc; t += kPThreads / 64) {
-                constexpr int E = D / 64;
-                float qv[E], kv[E], nq = 0.f, nk = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    qv[e] = Q[t * D + lane + 64 * e];
-                    kv[e] = K[t * D + lane + 64 * e];
-                    nq += qv[e] * qv[e];
-                    nk += kv[e] * kv[e];
-                }
-                nq = wave_sum(nq);
-                nk = wave_sum(nk);
-                const float sq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)D);
-                const float sk = 1.0f / sqrtf(nk + 1e-6f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    Q[t * D + lane + 64 * e] = qv[e] * sq;
-                    K[t * D + lane + 64 * e] = kv[e] * sk;
-                    Kt[(lane + 64 * e) * C + t] = kv[e] * sk;
-                }
-            }
-            __syncthreads();
+            bet[lane] = b;
+            dec[lane] = expf(__shfl(x, 63) - x);
         }
 
-        // ================= A = strictly-lower(beta_t e^{G_t-G_s} K K^T) into Tm  (MFMA) ===========
-        // wave w: row tile w, column tiles 0..w; upper tiles are zero
+        // ================= conv: q | k (wave w: tokens 16w .. 16w+15, lane: 4 channels), v block
+        auto xrow = [&](int t, int lc) -> f4 {  // 4 raw channels of chunk row t (t < 0: history)
+            f4 x;
+            if (t < 0) {
+                x = *reinterpret_cast<const f4 *>(hist + (3 + t) * NCH + lc);
+            } else if constexpr (ACT_BF16) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(raw + t * NCH + lc);
+                x = f4{bf16_to_f32((uint16_t)(u.x & 0xffffu)), bf16_to_f32((uint16_t)(u.x >> 16)),
+                       bf16_to_f32((uint16_t)(u.y & 0xffffu)), bf16_to_f32((uint16_t)(u.y >> 16))};
+            } else {
+                x = *reinterpret_cast<const f4 *>(raw + t * NCH + lc);
+            }
+            return x;
+        };
+        f4 hq[3], hv;
+        if (lane < QKG) {
+            const int lc = 4 * lane;
+            const bool isq = lc < D;
+            float *M = isq ? Q : K;
+            const int mc = isq ? lc : lc - D;
+            f4 x0 = xrow(16 * wave - 3, lc), x1 = xrow(16 * wave - 2, lc), x2 = xrow(16 * wave - 1, lc);
+#pragma unroll 1
+            for (int t = 16 * wave; t < 16 * wave + 16; ++t) {
+                const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
+                f4 y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v = conv4(wqk[j], x0[j], x1[j], x2[j], x3[j]);
+                    if constexpr (QKN) v = v * sigmoid_f(v);
+                    y[j] = t < Lc ? v : 0.f;
+                }
+                if constexpr (QKN) {  // unit length (+1e-6) over the head's 128 channels; q also / sqrt(d)
+                    float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+                    ss = row16_sum(ss);
+                    if constexpr (D == 128) ss += __shfl_xor(ss, 16);
+                    const float sc = 1.0f / sqrtf(ss + 1e-6f) / (isq ? sqrtf((float)D) : 1.0f);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y[j] *= sc;
+                }
+                *reinterpret_cast<f4 *>(M + swz<D>(t, mc)) = y;
+                x0 = x1;
+                x1 = x2;
+                x2 = x3;
+            }
+            hq[0] = x0;  // rows 61, 62, 63 for the last wave: the next chunk's history
+            hq[1] = x1;
+            hq[2] = x2;
+        }
         {
-            const int w = wave;
-            for (int ct = 0; ct < 4; ++ct) {
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (ct <= w)
-                    for (int k0 = 0; k0 < D; k0 += 32) acc = mma_tile<F32>(K, D, 16 * w, K, D, 16 * ct, k0, acc, lane);
-                const int s_ = 16 * ct + (lane & 15);
+            const int t = tid >> 2, lc = 2 * D + 4 * (tid & 3);
+            const f4 x0 = xrow(t - 3, lc), x1 = xrow(t - 2, lc), x2 = xrow(t - 1, lc);
+            const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
+            f4 y;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * w + (lane >> 4) * 4 + r;
-                    Tm[t * C + s_] = (s_ < t) ? bet[t] * expf(Gam[t] - Gam[s_]) * acc[r] : 0.f;
+            for (int j = 0; j < 4; ++j) {
+                float v = conv4(wv[j], x0[j], x1[j], x2[j], x3[j]);
+                if constexpr (QKN) v = v * sigmoid_f(v);
+                y[j] = t < Lc ? v : 0.f;
+            }
+            *reinterpret_cast<f4 *>(Vb + t * kDB + 4 * (tid & 3)) = y;
+            hv = x3;
+        }
+        lds_barrier();
+        // the raw rows and the history are consumed: the next chunk's history rows (this chunk's
+        // last three) are written, and the next chunk's stage travels while this one computes
+        if (Lc == C) {
+            if (wave == 3 && lane < QKG)
+#pragma unroll
+                for (int r = 0; r < 3; ++r) *reinterpret_cast<f4 *>(hist + r * NCH + 4 * lane) = hq[r];
+            if ((tid >> 2) >= C - 3) *reinterpret_cast<f4 *>(hist + ((tid >> 2) - (C - 3)) * NCH + 2 * D + 4 * (tid & 3)) = hv;
+        }
+        // the previous chunk's readout, held in registers until now so that its stores go out
+        // before this chunk's stage loads, never behind them
+        if (c > 0) store_o(c - 1, o_prev);
+        if (c + 1 < nchunks) stage(c + 1);
+
+        // ================= A = strictly-lower(beta e^{G_t-G_s} K K^T), P = lower(e^{G_t-G_s} Q K^T),
+        //                   Y = beta V - beta gamma K S^T  (MFMA; A / P row tiles {0,3} and {1,2})
+        {
+            const float *Am = wave < 2 ? K : Q;
+            float *Dm = wave < 2 ? Tm : Pm;
+            const int pair = wave & 1;  // row tiles {0, 3} or {1, 2}
+#pragma unroll 1
+            for (int jj = 0; jj < 2; ++jj) {
+                const int rt = jj == 0 ? pair : 3 - pair;
+#pragma unroll 1
+                for (int ct = 0; ct <= rt; ++ct) {
+                    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < D; kk += 32) {
+                        float av[8], bv[8];
+                        load8(Am + swz<D>(16 * rt + (lane & 15), kk + (lane >> 4) * 8), av);
+                        load8(K + swz<D>(16 * ct + (lane & 15), kk + (lane >> 4) * 8), bv);
+                        acc = mma8<F32>(av, bv, acc);
+                    }
+                    const int s_ = 16 * ct + (lane & 15);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * rt + (lane >> 4) * 4 + r;
+                        const float ratio = expf(Gam[t] - Gam[s_]);
+                        Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * acc[r] : 0.f)
+                                                    : (s_ <= t ? ratio * acc[r] : 0.f);
+                    }
                 }
             }
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D; kk += 32) {
+                float av[8], bv[8];
+                load8(K + swz<D>(16 * wave + (lane & 15), kk + (lane >> 4) * 8), av);
+                load8(S + swz<D>(lane & 15, kk + (lane >> 4) * 8), bv);
+                acc = mma8<F32>(av, bv, acc);
+            }
+            const int i = lane & 15;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * wave + (lane >> 4) * 4 + r;
+                Yt[i * kCP + t] = bet[t] * (Vb[t * kDB + i] - gam[t] * acc[r]);
+            }
         }
-        __syncthreads();
-        // ================= T = (I + A)^-1, blocked fp32 substitution =================
-        // diagonal 16x16 blocks: wave w, lane c < 16 solves column c of (I + A_ww)^-1
+        lds_barrier();
+        // ================= T = (I + A)^-1: 16x16 diagonal blocks by forward substitution (wave w,
+        //                   lane c < 16 solves column c of block w), then the blocks below them
         if (lane < 16) {
             const int w = wave, cc = lane;
             float x[16];
@@ -320,123 +413,128 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
             for (int r = 0; r < 16; ++r) {
                 float acc = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-                for (int s_ = 0; s_ < r; ++s_) acc -= Tm[(16 * w + r) * C + 16 * w + s_] * x[s_];
+                for (int s_ = 0; s_ < r; ++s_) acc -= Tm[(16 * w + r) * kCP + 16 * w + s_] * x[s_];
                 x[r] = (r < cc) ? 0.f : acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Tm[(16 * w + r) * C + 16 * w + cc] = x[r];
+            for (int r = 0; r < 16; ++r) Tm[(16 * w + r) * kCP + 16 * w + cc] = x[r];
         }
-        __syncthreads();
-        // off-diagonal blocks, block row i = 1..3: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-        for (int i = 1; i < 4; ++i) {
-            // X_ij (j < i) into the scratch Pm, one element per thread per pass
-            for (int e = tid; e < i * 256; e += kPThreads) {
-                const int j = e / 256, r = (e % 256) / 16, cc = e % 16;
-                float acc = 0.f;
-                for (int kb = j; kb < i; ++kb)
+        lds_barrier();
+        // T_10 = -T_11 A_10 T_00 (wave 0) and T_32 = -T_33 A_32 T_22 (wave 1), the product A T
+        // parked in the U area; T_ij = -T_ii (sum_k A_ik T_kj) for the 32 x 32 block below
+        float *scr = Ut + wave * 256;  // [16][16] per wave
+        auto park = [&](f4 v) {
 #pragma unroll
-                    for (int m = 0; m < 16; ++m) acc += Tm[(16 * i + r) * C + 16 * kb + m] * Tm[(16 * kb + m) * C + 16 * j + cc];
-                Pm[(16 * i + r) * C + 16 * j + cc] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < i * 256; e += kPThreads) {
-                const int j = e / 256, r = (e % 256) / 16, cc = e % 16;
-                float acc = 0.f;
+            for (int r = 0; r < 4; ++r) scr[((lane >> 4) * 4 + r) * 16 + (lane & 15)] = v[r];
+        };
+        auto blk16s = [&](const float *X, int xr0, int xc0, const float *Y, f4 acc) {  // acc += X(block) Y
 #pragma unroll
-                for (int m = 0; m < 16; ++m) acc += Tm[(16 * i + r) * C + 16 * i + m] * Pm[(16 * i + m) * C + 16 * j + cc];
-                Tm[(16 * i + r) * C + 16 * j + cc] = -acc;
+            for (int st2 = 0; st2 < 4; ++st2) {
+                const int kk = 4 * st2 + (lane >> 4);
+                acc = mfma4f32(X[(xr0 + (lane & 15)) * kCP + xc0 + kk], Y[kk * 16 + (lane & 15)], acc);
             }
-            __syncthreads();
+            return acc;
+        };
+        auto put_neg = [&](int r0, int c0, f4 v) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Tm[(r0 + (lane >> 4) * 4 + r) * kCP + c0 + (lane & 15)] = -v[r];
+        };
+        if (wave < 2) {
+            const int i = wave == 0 ? 1 : 3, j = i - 1;
+            park(blk16(Tm, 16 * i, 16 * j, Tm, 16 * j, 16 * j, f4{0.f, 0.f, 0.f, 0.f}, lane));
+            put_neg(16 * i, 16 * j, blk16s(Tm, 16 * i, 16 * i, scr, f4{0.f, 0.f, 0.f, 0.f}));
         }
-
-        // ================= P = lower(e^{G_t-G_s} Q K^T) (MFMA), Y = beta V - beta gamma K S^T ======
-        {
-            const int w = wave;
-            for (int ct = 0; ct < 4; ++ct) {
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (ct <= w)
-                    for (int k0 = 0; k0 < D; k0 += 32) acc = mma_tile<F32>(Q, D, 16 * w, K, D, 16 * ct, k0, acc, lane);
-                const int s_ = 16 * ct + (lane & 15);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * w + (lane >> 4) * 4 + r;
-                    Pm[t * C + s_] = (s_ <= t) ? expf(Gam[t] - Gam[s_]) * acc[r] : 0.f;
-                }
-            }
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < D; k0 += 32) acc = mma_tile<F32>(K, D, 16 * w, S, D, 0, k0, acc, lane);
-            const int i = lane & 15;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + (lane >> 4) * 4 + r;
-                Yt[i * C + t] = bet[t] * (Vb[t * kDB + i] - gam[t] * acc[r]);
-            }
+        lds_barrier();
+        const int r3 = 2 + (wave >> 1), c3 = wave & 1;  // block (r3, c3) of the lower-left 32 x 32
+        {  // X_rc = A_r0 T_0c + A_r1 T_1c
+            f4 x = blk16(Tm, 16 * r3, 16, Tm, 16, 16 * c3, f4{0.f, 0.f, 0.f, 0.f}, lane);
+            if (c3 == 0) x = blk16(Tm, 16 * r3, 0, Tm, 0, 0, x, lane);
+            park(x);
         }
-        __syncthreads();
+        lds_barrier();
+        {  // T_2c = -T_22 X_2c ;  T_3c = -(T_32 X_2c + T_33 X_3c)  (X_2c parked by wave c, X_3c by wave 2 + c)
+            f4 acc = blk16s(Tm, 16 * r3, 32, Ut + c3 * 256, f4{0.f, 0.f, 0.f, 0.f});
+            if (r3 == 3) acc = blk16s(Tm, 48, 48, scr, acc);
+            put_neg(16 * r3, 16 * c3, acc);
+        }
+        lds_barrier();
         // ================= U = T Y (MFMA) =================
         {
             const int w = wave;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < C; k0 += 32) acc = mma_tile<F32>(Tm, C, 16 * w, Yt, C, 0, k0, acc, lane);
+#pragma unroll
+            for (int kk = 0; kk < C; kk += 32) {
+                float av[8], bv[8];
+                load8(Tm + (16 * w + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
+                load8(Yt + (lane & 15) * kCP + kk + (lane >> 4) * 8, bv);
+                acc = mma8<F32>(av, bv, acc);
+            }
             const int i = lane & 15;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Ut[i * C + 16 * w + (lane >> 4) * 4 + r] = acc[r];
+            for (int r = 0; r < 4; ++r) Ut[i * kCP + 16 * w + (lane >> 4) * 4 + r] = acc[r];
         }
-        __syncthreads();
+        lds_barrier();
         // ================= O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K ==========
-        f4 snew[2];
+        constexpr int SCT = D / 16 / 4;  // S' column tiles per wave
+        f4 snew[SCT > 0 ? SCT : 1];
         {
             const int w = wave;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < D; k0 += 32) acc = mma_tile<F32>(Q, D, 16 * w, S, D, 0, k0, acc, lane);
+#pragma unroll
+            for (int kk = 0; kk < D; kk += 32) {
+                float av[8], bv[8];
+                load8(Q + swz<D>(16 * w + (lane & 15), kk + (lane >> 4) * 8), av);
+                load8(S + swz<D>(lane & 15, kk + (lane >> 4) * 8), bv);
+                acc = mma8<F32>(av, bv, acc);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] *= gam[16 * w + (lane >> 4) * 4 + r];
-            for (int k0 = 0; k0 < C; k0 += 32) acc = mma_tile<F32>(Pm, C, 16 * w, Ut, C, 0, k0, acc, lane);
-            const int i = lane & 15;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + (lane >> 4) * 4 + r;
-                if (t < Lc) a.o_ws[(((size_t)t0 + t) * a.n_vh + h) * D + blk * kDB + i] = acc[r];
+            for (int kk = 0; kk < C; kk += 32) {
+                float av[8], bv[8];
+                load8(Pm + (16 * w + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
+                load8(Ut + (lane & 15) * kCP + kk + (lane >> 4) * 8, bv);
+                acc = mma8<F32>(av, bv, acc);
             }
-            // S' block: rows i = 4*(lane>>4)+r, columns j = 16*ct + (lane&15), ct = 2w, 2w+1
-            const float gC = gam[Lc - 1];
+            o_prev = acc;  // stored during the next chunk (or after the loop)
+            // S' block: rows i = 4 (lane / 16) + r, columns j = 16 ct + lane % 16
+            const float gC = gam[C - 1];
 #pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                const int ct = 2 * w + q2;
-                if (ct * 16 >= D) {
-                    snew[q2] = f4{0.f, 0.f, 0.f, 0.f};
-                    continue;
-                }
+            for (int q2 = 0; q2 < SCT; ++q2) {
+                const int ct = SCT * w + q2;
                 f4 sa;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sa[r] = gC * S[((lane >> 4) * 4 + r) * D + 16 * ct + (lane & 15)];
-                for (int k0 = 0; k0 < C; k0 += 32) {
-                    float av[8], bv[8];
-                    load8(Ut + (lane & 15) * C + k0 + (lane >> 4) * 8, av);
-                    load8(Kt + (16 * ct + (lane & 15)) * C + k0 + (lane >> 4) * 8, bv);
+                for (int r = 0; r < 4; ++r) sa[r] = gC * S[swz<D>((lane >> 4) * 4 + r, 16 * ct + (lane & 15))];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bv[e] *= dec[k0 + (lane >> 4) * 8 + e];
+                for (int kk = 0; kk < C; kk += 32) {
+                    float av[8], bv[8];
+                    load8(Ut + (lane & 15) * kCP + kk + (lane >> 4) * 8, av);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int s_ = kk + (lane >> 4) * 8 + e;
+                        bv[e] = K[swz<D>(s_, 16 * ct + (lane & 15))] * dec[s_];
+                    }
                     sa = mma8<F32>(av, bv, sa);
                 }
                 snew[q2] = sa;
             }
         }
-        __syncthreads();
-        {
-            const int w = wave;
+        lds_barrier();
 #pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                const int ct = 2 * w + q2;
-                if (ct * 16 < D)
+        for (int q2 = 0; q2 < SCT; ++q2) {
+            const int ct = SCT * wave + q2;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[((lane >> 4) * 4 + r) * D + 16 * ct + (lane & 15)] = snew[q2][r];
-            }
+            for (int r = 0; r < 4; ++r) S[swz<D>((lane >> 4) * 4 + r, 16 * ct + (lane & 15))] = snew[q2][r];
         }
-        __syncthreads();
     }
+    if (nchunks > 0) store_o(nchunks - 1, o_prev);
+    __syncthreads();
     // ---- the state block after the last token
     float *sd = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
-    for (int i = tid; i < kDB * D / 4; i += kPThreads) reinterpret_cast<f4 *>(sd)[i] = reinterpret_cast<const f4 *>(S)[i];
+    for (int i = tid; i < kDB * D / 4; i += kPThreads) {
+        const int r = (4 * i) / D, c = (4 * i) % D;
+        reinterpret_cast<f4 *>(sd)[i] = *reinterpret_cast<const f4 *>(S + swz<D>(r, c));
+    }
 }
 
 // out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) per (token, head); 16 lanes per row.  The

@@ -42,6 +42,8 @@ GDN_API int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, c
     if (slot < 0 || slot >= d.n_pool) return gdn::abi_fail(GDN_ERR_RANGE, "gdn_prefill: slot outside [0, n_pool)");
     if (ws_bytes < gdn::prefill_workspace_bytes(d.d_v, d.n_vh, n_tok))
         return gdn::abi_fail(GDN_ERR_ARG, "gdn_prefill: workspace smaller than gdn_prefill_workspace_bytes()");
+    if (d.act_dtype == GDN_BF16 && (d.n_vh & 1))
+        return gdn::abi_fail(GDN_ERR_SHAPE, "gdn_prefill: bf16 activations need an even number of value heads");
     if (gdn::prefill_lds_bytes(d.d_k, d.act_dtype == GDN_BF16) > kMaxLds)
         return gdn::abi_fail(GDN_ERR_SHAPE, "gdn_prefill: fp32 activations with d = 128 exceed one workgroup's LDS");
     gdn::PrefillArgs a{};
