@@ -30,27 +30,30 @@ METRIC = "GDN verify tokens/s (64 slots, K+1=16) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_FLOPS = 2.5e15  # dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_multi_slot_verify.json")
-VERIFY_SRC = os.path.join(ROOT, "gated_deltanet_linear_verify_amd", "csrc", "gdn_verify.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(n_units: int):
-    """HBM bytes per verify launch from the committed rocprofv3 counter summary, or None when
-    the summary is missing or was taken from a different kernel source."""
+def measured_traffic():
+    """HBM bytes per verify launch from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what it reads for the rollback copy kernel of known size), or None
+    when the summary is missing or was taken on different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256_16") != source_digest(VERIFY_SRC):
+        if t.get("kernel_source_sha256_16") != source_digest(t["kernel_sources"]):
+            return None
+    except (OSError, ValueError, KeyError):
         return None
     return t.get("bytes_per_launch")
 
@@ -218,7 +221,7 @@ def main() -> int:
     vb = bytemodel.verify_bytes(shape)
     rb = bytemodel.rollback_bytes(shape, B)
     achieved = vb / (v_avg * 1e-3) / 1e9
-    traffic = measured_traffic(B * shape.n_vh)
+    traffic = measured_traffic()
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us), "
         f"verify {v_avg * 1e3:.1f} us avg (p10 {np.percentile(verify_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(verify_ms, 90) * 1e3:.1f}) -> {achieved:.0f} GB/s; "
