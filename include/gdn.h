@@ -122,7 +122,7 @@ int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, const void
  * Tree verify: n_tok draft-tree nodes per batch entry, node i hanging off parent[b][i]
  * (device int32 [n_batch][n_tok]; -1 = starts from the committed state, else 0 <= parent < i;
  * node 0 is the root and must have parent -1).  lucebox-hub internal.h, QwenGraphInputs::
- * parent_ids ("tree mode when non-null"); create_target_cache sizes the capture for
+ * parent_ids (a non-null parent array selects tree verification); create_target_cache sizes the capture for
  * 1 + tree budget positions.  Node i's state is its parent's state advanced by node i's token;
  * its conv window runs along the ancestor path, filled from conv_state above the root.  Writes
  * out for every node, capture->ssm[slot][i] (state after node i) and capture->conv[slot][i]

@@ -11,7 +11,7 @@
  *
  *   conv    Depthwise causal conv1d, kernel 4, over concat(old conv state, new qkv rows)
  *           (lucebox-hub internal.h, struct TargetCache: conv_state and conv_input_cache
- *           comments; struct TargetLayer: ssm_conv1d "depthwise causal conv").
+ *           comments; struct TargetLayer: ssm_conv1d, a depthwise causal conv weight).
  *           xhat[t][c] = sum_j w[c][j] * xext[t+j][c], tap 3 multiplies the current token.
  *   gate    g = -exp(A_log) * softplus(alpha + dt_bias), rho = exp(g)  (gated delta rule of
  *           Yang, Kautz & Hatamizadeh, "Gated Delta Networks", 2024; per-head A and dt_bias
@@ -23,10 +23,11 @@
  *   norm    y = o / sqrt(mean(o^2) + eps) * norm_w * z * sigmoid(z)  (ssm_norm [head_v_dim],
  *           rms_eps and the z projection in lucebox-hub internal.h, TargetLayer/TargetWeights).
  *   capture cap[t] = S_t for every verify position t (lucebox-hub internal.h, TargetCache:
- *           ssm_intermediate "state after processing verify token t").
+ *           ssm_intermediate, whose element t is the state after verify token t).
  *   tree    the state of node i is the chain evaluated along the root path of i, starting
  *           from the committed state; the conv window is taken along the same path
- *           (lucebox-hub internal.h, QwenGraphInputs::parent_ids "tree mode").
+ *           (lucebox-hub internal.h, QwenGraphInputs::parent_ids, which switches the forward to
+ *           tree verification).
  *
  * Layouts (row-major, last index fastest):
  *   qkv [B][T][C] with C = 2*H_k*d_k + H_v*d_v, channel blocks q | k | v, head-major;
