@@ -89,7 +89,8 @@ typedef struct gdn_dims {
 
 /* Persistent per-position capture written by a verify and read by rollback.  `state` and
  * `conv_state` name the buffers that rollback restores into.  lucebox-hub internal.h, struct
- * DeltaNetCapture ("persistent cache buffers ... not managed by the per-call allocator"). */
+ * DeltaNetCapture: the capture lives in persistent cache buffers that outlive a call, not in
+ * per-call scratch memory. */
 typedef struct gdn_capture {
     gdn_dims dims;
     float *ssm;        /* [P][t_cap][H_v][d_v][d_k] */
