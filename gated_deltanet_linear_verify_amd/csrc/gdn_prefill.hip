@@ -304,8 +304,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
             float *M = isq ? Q : K;
             const int mc = isq ? lc : lc - D;
             f4 x0 = xrow(16 * wave - 3, lc), x1 = xrow(16 * wave - 2, lc), x2 = xrow(16 * wave - 1, lc);
-#pragma unroll 1
-            for (int t = 16 * wave; t < 16 * wave + 16; ++t) {
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                const int t = 16 * wave + tt;
                 const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
                 f4 y;
 #pragma unroll
@@ -364,12 +365,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
         {
             const float *Am = wave < 2 ? K : Q;
             float *Dm = wave < 2 ? Tm : Pm;
-            const int pair = wave & 1;  // row tiles {0, 3} or {1, 2}
-#pragma unroll 1
-            for (int jj = 0; jj < 2; ++jj) {
-                const int rt = jj == 0 ? pair : 3 - pair;
-#pragma unroll 1
-                for (int ct = 0; ct <= rt; ++ct) {
+            const int pair = wave & 1;  // row tiles {0, 3} or {1, 2}: 5 tiles, listed so the loop unrolls
+#pragma unroll
+            for (int jt = 0; jt < 5; ++jt) {
+                // pair 0: (0,0) (3,0) (3,1) (3,2) (3,3);  pair 1: (1,0) (1,1) (2,0) (2,1) (2,2)
+                const int rt = pair == 0 ? (jt == 0 ? 0 : 3) : (jt < 2 ? 1 : 2);
+                const int ct = pair == 0 ? (jt == 0 ? 0 : jt - 1) : (jt < 2 ? jt : jt - 2);
+                {
                     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < D; kk += 32) {
