@@ -31,7 +31,7 @@ struct LaunchCfg {
 
 // Chain verify: grid B * H_k workgroups of (H_v/H_k) * waves_per_head(d) waves.
 hipError_t launch_verify_chain(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream);
-// Tree verify: grid B * H_v workgroups of waves_per_head(d) waves; at most 64 nodes.
+// Tree verify: grid B * H_v workgroups of 2 * waves_per_head(d) waves; at most 64 nodes.
 hipError_t launch_verify_tree(const VerifyArgs &a, const LaunchCfg &c, hipStream_t stream);
 
 int verify_waves_per_head(int d);

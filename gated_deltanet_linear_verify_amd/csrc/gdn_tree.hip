@@ -29,6 +29,16 @@ constexpr int kSchedRestart = 0x100;
 constexpr int kSchedEmit = 0x200;
 constexpr int kSchedMax = kTreeMaxNodes * (kTreeMaxNodes + 1) / 2 + kTreeMaxNodes;
 
+// Waves per head: twice the chain kernel's.  A tree's node steps form one dependent chain per
+// (slot, head) (64 nodes plus the root-path recomputations of DFS restarts), so the step latency,
+// not bytes, bounds the kernel; spreading the state's rows over more waves halves each lane's work
+// per step.  Each lane still holds whole 16-lane column groups, so the per-row sums, and the
+// results, are the same bits as in the chain kernel.
+template <int D>
+struct TreeWaves {
+    static constexpr int value = 2 * WavesPerHead<D>::value;
+};
+
 template <int D, typename act_t>
 struct TreeLds {
     __host__ __device__ static size_t raw_bytes(int T) { return (size_t)T * 3 * D * sizeof(act_t); }
@@ -50,11 +60,11 @@ struct TreeLds {
 };
 
 template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN>
-__global__ __launch_bounds__(256) void verify_tree_kernel(VerifyArgs a)
+__global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(VerifyArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
     using L = TreeLds<D, act_t>;
-    constexpr int NW = WavesPerHead<D>::value;
+    constexpr int NW = TreeWaves<D>::value;
     using G = Geo<D, NW>;
     constexpr int VEC = 16 / (int)sizeof(act_t);
     constexpr int NCH = 3 * D;  // q | k | v channels of this value head
@@ -308,7 +318,7 @@ template <int D, bool AB, bool OB, bool QKN>
 static hipError_t launch_tree_t(const VerifyArgs &a, hipStream_t stream)
 {
     const size_t lds = verify_tree_lds_bytes(D, a.T, AB);
-    hipLaunchKernelGGL((verify_tree_kernel<D, AB, OB, QKN>), dim3(a.n_batch * a.n_vh), dim3(WavesPerHead<D>::value * 64),
+    hipLaunchKernelGGL((verify_tree_kernel<D, AB, OB, QKN>), dim3(a.n_batch * a.n_vh), dim3(TreeWaves<D>::value * 64),
                        lds, stream, a);
     return hipGetLastError();
 }
