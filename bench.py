@@ -123,6 +123,18 @@ def components(args) -> dict:
                                  "tokens_per_s": s.n_tok / (us * 1e-6),
                                  "hbm_gbps": bytemodel.verify_bytes(s) / (us * 1e-6) / 1e9}
     del d
+    # snapshot-and-replay rollback on the 64-slot workload (no per-position capture): a round is
+    # snapshot + verify, plus restore + replay of the accepted tokens when some are rejected
+    s = W.MULTI_SLOT_VERIFY
+    d = device.upload(s, W.make_inputs(s, 0), capture=False)
+    snap = {"state": torch.empty_like(d["state"]), "conv_state": torch.empty_like(d["conv_state"])}
+    us_acc = time_launches(lambda: device.snapshot_replay_round(d, snap, s.n_tok), 50)
+    us_rej = time_launches(lambda: device.snapshot_replay_round(d, snap, 1), 50)
+    out["snapshot_replay"] = {"workload": "64 slots x 16 tokens, 16/32 heads, d=128, bf16, no capture",
+                              "us_all_accepted": us_acc, "us_reject_after_first": us_rej,
+                              "tokens_per_s_all_accepted": s.n_batch * s.n_tok / (us_acc * 1e-6),
+                              "tokens_per_s_reject_after_first": s.n_batch * s.n_tok / (us_rej * 1e-6)}
+    del d, snap
     # chunked prefill: one 8192-token sequence
     s = W.CHUNKED_PREFILL
     d = device.upload(s, W.make_inputs(s, 0), capture=False)

@@ -74,3 +74,9 @@ def prefill_flops(s: Shape, chunk: int = PREFILL_CHUNK) -> int:
     C, dk, dv = chunk, s.d_k, s.d_v
     per_tok = 4 * C * dk + 4 * C * dv + 6 * dk * dv + (C * C) // 3
     return s.n_tok * s.n_vh * per_tok
+
+
+def snapshot_bytes(s: Shape, n: int) -> int:
+    """Snapshot or restore of n slots: state and conv state read from one buffer pair and written
+    to the other."""
+    return n * 2 * 4 * (s.n_vh * s.d_v * s.d_k + 3 * s.conv_channels)

@@ -345,6 +345,47 @@ GDN_API int gdn_reset(const gdn_dims *dims, float *state, float *conv_state, int
     return ok();
 }
 
+namespace {
+int slot_copy(const char *who, const gdn_dims *dims, float *dst_s, float *dst_c, const float *src_s, const float *src_c,
+              const int32_t *slots, int32_t n, void *stream)
+{
+    if (int r = check_dims(dims)) return r;
+    if (n < 0 || n > dims->n_pool || n > 65535)
+        return fail(GDN_ERR_RANGE, "%s: n = %d outside [0, min(n_pool = %d, 65535)]", who, n, dims->n_pool);
+    if (n == 0) return ok();
+    if (!dst_s || !dst_c || !src_s || !src_c || !slots) return fail(GDN_ERR_ARG, "%s: NULL buffer or slot array", who);
+    if (!aligned16(dst_s) || !aligned16(dst_c) || !aligned16(src_s) || !aligned16(src_c))
+        return fail(GDN_ERR_ARG, "%s: state buffers must be 16-byte aligned", who);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dims->flags & GDN_F_CHECK_INDICES)
+        if (int r = check_slots(slots, n, dims->n_pool, st)) return r;
+    gdn::SlotCopyArgs a{};
+    a.dst_state = dst_s;
+    a.dst_conv = dst_c;
+    a.src_state = src_s;
+    a.src_conv = src_c;
+    a.slots = slots;
+    a.n = n;
+    a.n_pool = dims->n_pool;
+    a.ssm_elems = (size_t)dims->n_vh * dims->d_v * dims->d_k;
+    a.conv_elems = 3 * channels(*dims);
+    if (hipError_t e = gdn::launch_slot_copy(a, st)) return hip_fail(e, who);
+    return ok();
+}
+}  // namespace
+
+GDN_API int gdn_snapshot(const gdn_dims *dims, const float *state, const float *conv_state, float *snap_state,
+                         float *snap_conv, const int32_t *slots, int32_t n, void *stream)
+{
+    return slot_copy("gdn_snapshot", dims, snap_state, snap_conv, state, conv_state, slots, n, stream);
+}
+
+GDN_API int gdn_restore(const gdn_dims *dims, float *state, float *conv_state, const float *snap_state,
+                        const float *snap_conv, const int32_t *slots, int32_t n, void *stream)
+{
+    return slot_copy("gdn_restore", dims, state, conv_state, snap_state, snap_conv, slots, n, stream);
+}
+
 GDN_API const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
 GDN_API const char *gdn_version(void) { return "gdn 0.1 (gfx950)"; }

@@ -53,6 +53,18 @@ hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream);
 
 hipError_t launch_fill_zero(float *p, size_t n, hipStream_t stream);
 
+// Snapshot / restore: for each listed slot, copy its state and conv state from one pool-shaped
+// pair of buffers to another.
+struct SlotCopyArgs {
+    float *dst_state, *dst_conv;
+    const float *src_state, *src_conv;
+    const int32_t *slots;  // device array of n slots; entries outside [0, n_pool) are skipped
+    int32_t n, n_pool;
+    size_t ssm_elems;   // H_v * d_v * d_k floats per slot
+    size_t conv_elems;  // 3 * C floats per slot
+};
+hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream);
+
 struct PrefillArgs {
     int32_t n_kh, n_vh, d, T, C, slot;
     float eps;

@@ -50,6 +50,42 @@ hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Snapshot and restore of whole slots (lucebox-hub internal.h: snapshot_ssm_state and
+// restore_ssm_state copy the recurrent and conv state to and from TargetCache's ssm_state_snap /
+// conv_state_snap).  Same flat float4 stream as the rollback, between two pool-shaped buffers.
+__global__ __launch_bounds__(256) void slot_copy_kernel(SlotCopyArgs a)
+{
+    const int slot = a.slots[blockIdx.y];
+    if (slot < 0 || slot >= a.n_pool) return;  // uniform per block
+    const f4 *src_s = reinterpret_cast<const f4 *>(a.src_state + (size_t)slot * a.ssm_elems);
+    f4 *dst_s = reinterpret_cast<f4 *>(a.dst_state + (size_t)slot * a.ssm_elems);
+    const f4 *src_c = reinterpret_cast<const f4 *>(a.src_conv + (size_t)slot * a.conv_elems);
+    f4 *dst_c = reinterpret_cast<f4 *>(a.dst_conv + (size_t)slot * a.conv_elems);
+    const size_t ns = a.ssm_elems / 4, nc = a.conv_elems / 4;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < ns; i += 4 * stride) {
+        const f4 v0 = src_s[i], v1 = src_s[i + stride], v2 = src_s[i + 2 * stride], v3 = src_s[i + 3 * stride];
+        dst_s[i] = v0;
+        dst_s[i + stride] = v1;
+        dst_s[i + 2 * stride] = v2;
+        dst_s[i + 3 * stride] = v3;
+    }
+    for (; i < ns; i += stride) dst_s[i] = src_s[i];
+    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < nc; j += stride) dst_c[j] = src_c[j];
+}
+
+hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream)
+{
+    if (a.n <= 0) return hipSuccess;
+    const size_t vec = (a.ssm_elems + a.conv_elems) / 4;
+    size_t blocks = (vec + 256 * 4 - 1) / (256 * 4);
+    if (blocks > 512) blocks = 512;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(slot_copy_kernel, dim3((unsigned)blocks, (unsigned)a.n), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(f4 *p, size_t n4)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;

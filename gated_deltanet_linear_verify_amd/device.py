@@ -86,3 +86,26 @@ def prefill(d: dict, stream=None) -> None:
     gdn.gdn_prefill(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"], d["beta"],
                     d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], d["out"], T, slot, ws,
                     ws.numel() * 4, stream)
+
+
+def snapshot_replay_round(d: dict, snap: dict, n_accept: int, stream=None) -> None:
+    """One spec-decode round with snapshot-and-replay rollback on uploaded inputs (no capture):
+    snapshot the batch's slots, verify all T tokens, and when n_accept < T restore the snapshot
+    and verify the first n_accept tokens again.  snap holds pool-shaped "state" / "conv_state"."""
+    B, T = d["qkv"].shape[0], d["qkv"].shape[1]
+    gdn.gdn_snapshot(d["dims"], d["state"], d["conv_state"], snap["state"], snap["conv_state"], d["slot_ids"], B,
+                     stream)
+    verify(d, stream=stream, with_capture=False)
+    if n_accept < T:
+        gdn.gdn_restore(d["dims"], d["state"], d["conv_state"], snap["state"], snap["conv_state"], d["slot_ids"], B,
+                        stream)
+        rep = snap.get("replay")
+        if rep is None or rep["n"] != n_accept:  # the accepted prefix of every input, contiguous
+            rep = {"n": n_accept}
+            for k in ("qkv", "z", "alpha", "beta"):
+                rep[k] = d[k][:, :n_accept].contiguous()
+            rep["out"] = d["out"][:, :n_accept].contiguous()
+            snap["replay"] = rep
+        gdn.gdn_verify(d["dims"], d["state"], d["conv_state"], rep["qkv"], rep["z"], rep["alpha"], rep["beta"],
+                       d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], None, rep["out"], n_accept,
+                       d["slot_ids"], B, stream)

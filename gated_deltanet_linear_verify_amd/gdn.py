@@ -22,7 +22,7 @@ GDN_F_CHECK_INDICES = 0x2
 
 EXPORTS = ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch", "gdn_rollback_trim",
            "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_capture_bytes", "gdn_reset",
-           "gdn_last_error", "gdn_version")
+           "gdn_snapshot", "gdn_restore", "gdn_last_error", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -69,8 +69,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_capture_bytes.argtypes = [D, I, I, ctypes.POINTER(S)]
         L.gdn_capture_bytes.restype = S
         L.gdn_reset.argtypes = [D, P, P, I, P]
+        L.gdn_snapshot.argtypes = [D, P, P, P, P, P, I, P]
+        L.gdn_restore.argtypes = [D, P, P, P, P, P, I, P]
         for f in ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch",
-                  "gdn_rollback_trim", "gdn_prefill", "gdn_reset"):
+                  "gdn_rollback_trim", "gdn_prefill", "gdn_reset", "gdn_snapshot", "gdn_restore"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_version.restype = ctypes.c_char_p
@@ -172,3 +174,13 @@ def gdn_prefill(dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, co
 
 def gdn_reset(dims, state, conv_state, slot: int, stream=None) -> None:
     _check(lib().gdn_reset(ctypes.byref(dims), _p(state), _p(conv_state), slot, _stream(stream)))
+
+
+def gdn_snapshot(dims, state, conv_state, snap_state, snap_conv, slots, n: int, stream=None) -> None:
+    _check(lib().gdn_snapshot(ctypes.byref(dims), _p(state), _p(conv_state), _p(snap_state), _p(snap_conv),
+                              _p(slots), n, _stream(stream)))
+
+
+def gdn_restore(dims, state, conv_state, snap_state, snap_conv, slots, n: int, stream=None) -> None:
+    _check(lib().gdn_restore(ctypes.byref(dims), _p(state), _p(conv_state), _p(snap_state), _p(snap_conv),
+                             _p(slots), n, _stream(stream)))

@@ -192,6 +192,29 @@ size_t gdn_capture_bytes(const gdn_dims *dims, int32_t t_cap, int32_t mode, size
 int gdn_reset(const gdn_dims *dims, float *state, float *conv_state, int32_t slot,
               void *stream);
 
+/*
+ * Snapshot-and-replay rollback, the alternative to the per-position capture.  lucebox-hub
+ * internal.h, snapshot_ssm_state / restore_ssm_state: the recurrent and conv state are copied to
+ * and from snapshot tensors (TargetCache ssm_state_snap, conv_state_snap) shaped like the live
+ * ones.  A spec-decode round then runs: gdn_snapshot, gdn_verify with capture == NULL over the
+ * K+1 drafted tokens, and only if some are rejected gdn_restore followed by gdn_verify (again
+ * without capture) over the accepted tokens.  It moves the state about three times instead of
+ * writing K+1 captures, at the price of a second pass on rejection.
+ *
+ * gdn_snapshot copies, for each of the n slots in `slots` (device int32 [n], distinct), the slot's
+ * state [H_v][d_v][d_k] and conv state [3][C] from state / conv_state into snap_state / snap_conv;
+ * gdn_restore copies them back.  The snapshot buffers have the pool layout of state and conv_state
+ * ([P][H_v][d_v][d_k] and [P][3][C] fp32, caller-owned, 16-byte aligned); only the listed slots
+ * are read or written.  Bitwise copies, stream-ordered.  n == 0 is a no-op; n outside
+ * [0, min(n_pool, 65535)] is GDN_ERR_RANGE; NULL or misaligned buffers GDN_ERR_ARG.  Slots outside
+ * [0, n_pool) are skipped, or rejected with GDN_ERR_RANGE under GDN_F_CHECK_INDICES (which also
+ * rejects repeated slots).
+ */
+int gdn_snapshot(const gdn_dims *dims, const float *state, const float *conv_state, float *snap_state,
+                 float *snap_conv, const int32_t *slots, int32_t n, void *stream);
+int gdn_restore(const gdn_dims *dims, float *state, float *conv_state, const float *snap_state,
+                const float *snap_conv, const int32_t *slots, int32_t n, void *stream);
+
 /* Thread-local description of the last error of this thread ("" after success). */
 const char *gdn_last_error(void);
 

@@ -135,3 +135,20 @@ def test_prefill_validation():
     bad = gdn.make_dims(W.CHUNKED_PREFILL)
     bad.d_k = 96
     assert call(bad) == gdn.GDN_ERR_SHAPE
+
+
+def test_snapshot_restore_validation():
+    """gdn_snapshot / gdn_restore reject bad arguments before any launch; n == 0 is a no-op."""
+    L = _lib_or_skip()
+    d = _dims(n_pool=4)
+    bufs = [FAKE] * 4
+    for fn in (L.gdn_snapshot, L.gdn_restore):
+        assert fn(ctypes.byref(d), *bufs, None, 0, None) == gdn.GDN_OK
+        assert fn(ctypes.byref(d), *bufs, FAKE, -1, None) == gdn.GDN_ERR_RANGE
+        assert fn(ctypes.byref(d), *bufs, FAKE, 5, None) == gdn.GDN_ERR_RANGE
+        assert fn(ctypes.byref(d), *bufs, None, 2, None) == gdn.GDN_ERR_ARG
+        assert fn(ctypes.byref(d), None, *bufs[1:], FAKE, 2, None) == gdn.GDN_ERR_ARG
+        mis = ctypes.c_void_p(0x1008)
+        assert fn(ctypes.byref(d), *bufs[:3], mis, FAKE, 2, None) == gdn.GDN_ERR_ARG
+        bad = _dims(n_pool=4, d_conv=3)
+        assert fn(ctypes.byref(bad), *bufs, FAKE, 1, None) == gdn.GDN_ERR_SHAPE
