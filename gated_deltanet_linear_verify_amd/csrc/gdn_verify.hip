@@ -305,7 +305,7 @@ static hipError_t launch_t(const VerifyArgs &a0, hipStream_t stream)
     const int waves = R * WavesPerHead<D>::value;
     const int wgs_per_cu = waves >= kTargetWavesPerCu ? 1 : kTargetWavesPerCu / waves;
     const size_t lds_cap = kLdsPerCu / (wgs_per_cu + 1) + 16;  // wgs_per_cu + 1 workgroups no longer fit
-    if (lds < lds_cap) lds = lds_cap;
+    if (CAP && lds < lds_cap) lds = lds_cap;  // without capture stores more resident waves only help
     for (int t0 = 0; t0 < a0.T; t0 += kTokenTile) {
         VerifyArgs a = a0;
         a.t0 = t0;
