@@ -135,6 +135,53 @@ def components(args) -> dict:
                               "tokens_per_s_all_accepted": s.n_batch * s.n_tok / (us_acc * 1e-6),
                               "tokens_per_s_reject_after_first": s.n_batch * s.n_tok / (us_rej * 1e-6)}
     del d, snap
+    # a spec-decode step over 48 GDN layers (the pages' model has 48 delta-net layers), 1 slot, 16
+    # drafted tokens and plain 1-token decode: eager launches from the binding vs one replay of the
+    # recorded HIP graph
+    n_layers = 48
+    for name, n_tok in (("graph_step_48_layers", 16), ("graph_step_48_layers_1_token", 1)):
+        s = W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=n_tok)
+        layers = [device.upload(s, W.make_inputs(s, 1000 + l), fill_capture=0.0) for l in range(n_layers)]
+        slots = layers[0]["slot_ids"].clone()
+        acc = torch.full((s.n_batch,), s.n_tok // 2, dtype=torch.int32, device="cuda")
+        us_eager = time_launches(lambda: device.layers_step(layers, slots, acc), 20)
+        g = device.layers_graph(layers, slots, acc)
+        us_graph = time_launches(lambda: g.launch(), 20)
+        g.close()
+        step_bytes = n_layers * (bytemodel.verify_bytes(s) + bytemodel.rollback_bytes(s, s.n_batch))
+        out[name] = {
+            "workload": f"48 layers x (1 slot x {n_tok} token verify with capture) + one cross-layer rollback",
+            "us_eager": us_eager, "us_graph": us_graph,
+            "tokens_per_s_graph": s.n_tok / (us_graph * 1e-6),
+            "hbm_gbps_graph": step_bytes / (us_graph * 1e-6) / 1e9}
+        del layers, g
+    # rollback of 48 layers x 64 slots: one cross-layer launch vs one batched launch per layer
+    s = W.MULTI_SLOT_VERIFY
+    dims = gdn.make_dims(s)
+    C = s.conv_channels
+    caps = []
+    for _ in range(n_layers):
+        st = torch.empty((s.n_pool, s.n_vh, s.d_v, s.d_k), dtype=torch.float32, device="cuda")
+        cs = torch.empty((s.n_pool, 3, C), dtype=torch.float32, device="cuda")
+        cap = torch.empty((s.n_pool, s.n_tok, s.n_vh, s.d_v, s.d_k), dtype=torch.float32, device="cuda")
+        cc = torch.empty((s.n_pool, 3 + s.n_tok, C), dtype=torch.float32, device="cuda")
+        caps.append(gdn.Capture(dims, cap, cc, st, cs, s.n_tok, gdn.GDN_CHAIN))
+    slots = torch.randperm(s.n_pool, dtype=torch.int32).cuda()
+    acc = torch.from_numpy((s.n_tok - 1 - W.make_inputs(s, 0)["trims"]).astype(np.int32)).cuda()
+    us_one = time_launches(lambda: gdn.gdn_rollback_layers(caps, slots, acc, s.n_batch), 10)
+    us_per_layer = time_launches(lambda: [gdn.gdn_rollback_batch(c, slots, acc, s.n_batch) for c in caps], 10)
+    rb = n_layers * bytemodel.rollback_bytes(s, s.n_batch)
+    n1 = 1  # the same rollback for one slot
+    us_one_1 = time_launches(lambda: gdn.gdn_rollback_layers(caps, slots, acc, n1), 20)
+    us_per_layer_1 = time_launches(lambda: [gdn.gdn_rollback_batch(c, slots, acc, n1) for c in caps], 20)
+    out["rollback_48_layers"] = {"workload": "48 layers x 64 slots, 16/32 heads, d=128",
+                                 "us_one_launch": us_one, "us_launch_per_layer": us_per_layer,
+                                 "hbm_gbps_one_launch": rb / (us_one * 1e-6) / 1e9,
+                                 "algorithmic_bytes": rb,
+                                 "one_slot_us_one_launch": us_one_1,
+                                 "one_slot_us_launch_per_layer": us_per_layer_1}
+    del caps
+    torch.cuda.empty_cache()
     # chunked prefill: one 8192-token sequence
     s = W.CHUNKED_PREFILL
     d = device.upload(s, W.make_inputs(s, 0), capture=False)

@@ -5,6 +5,7 @@
 // error sink of lucebox-hub internal.h, set_last_error).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -20,14 +21,20 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char *fmt, ...)
+int vfail(int code, const char *fmt, va_list ap)
 {
     char buf[512];
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    g_last_error = buf;
+    return code;
+}
+
+int fail(int code, const char *fmt, ...)
+{
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vfail(code, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return code;
 }
 
@@ -138,8 +145,6 @@ gdn::VerifyArgs make_args(const gdn_dims &d, int n_tok, int n_batch)
 }  // namespace
 
 namespace gdn {
-int abi_fail(int code, const char *msg) { return fail(code, "%s", msg); }
-int abi_ok() { return ok(); }
 int abi_check_dims(const gdn_dims *d) { return check_dims(d); }
 }  // namespace gdn
 
@@ -307,6 +312,66 @@ GDN_API int gdn_rollback_batch(const gdn_capture *capture, const int32_t *slots,
     return ok();
 }
 
+namespace {
+bool same_geometry(const gdn_capture &a, const gdn_capture &b)
+{
+    const gdn_dims &x = a.dims, &y = b.dims;
+    return x.n_kh == y.n_kh && x.n_vh == y.n_vh && x.d_k == y.d_k && x.d_v == y.d_v && x.d_conv == y.d_conv &&
+           x.n_pool == y.n_pool && a.t_cap == b.t_cap && a.mode == b.mode;
+}
+}  // namespace
+
+GDN_API int gdn_rollback_layers(const gdn_capture *layers, int32_t n_layers, const int32_t *slots,
+                                const int32_t *accepted_idx, int32_t n, void *stream)
+{
+    if (!layers) return fail(GDN_ERR_ARG, "gdn_rollback_layers: layers is NULL");
+    if (n_layers < 1) return fail(GDN_ERR_RANGE, "gdn_rollback_layers: n_layers = %d < 1", n_layers);
+    const gdn_capture &l0 = layers[0];
+    std::vector<const float *> owned;
+    owned.reserve(2 * (size_t)n_layers);
+    for (int l = 0; l < n_layers; ++l) {
+        if (int r = check_rollback_capture(&layers[l])) return fail(r, "gdn_rollback_layers: layer %d: %s", l, gdn_last_error());
+        if (!same_geometry(l0, layers[l]))
+            return fail(GDN_ERR_ARG, "gdn_rollback_layers: layer %d differs from layer 0 in dims, t_cap or mode", l);
+        owned.push_back(layers[l].state);
+        owned.push_back(layers[l].conv_state);
+    }
+    std::sort(owned.begin(), owned.end());
+    if (std::adjacent_find(owned.begin(), owned.end()) != owned.end())
+        return fail(GDN_ERR_ARG, "gdn_rollback_layers: two layers share a state or conv_state buffer");
+    if (n < 0 || n > l0.dims.n_pool || n > 65535)
+        return fail(GDN_ERR_RANGE, "gdn_rollback_layers: n = %d outside [0, min(n_pool = %d, 65535)]", n, l0.dims.n_pool);
+    if (n == 0) return ok();
+    if (!slots || !accepted_idx) return fail(GDN_ERR_ARG, "gdn_rollback_layers: index arrays are NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (l0.dims.flags & GDN_F_CHECK_INDICES) {
+        if (int r = check_slots(slots, n, l0.dims.n_pool, st)) return r;
+        std::vector<int32_t> h;
+        if (int r = fetch_i32(accepted_idx, n, st, h)) return r;
+        for (int i = 0; i < n; ++i)
+            if (h[i] < 0 || h[i] >= l0.t_cap)
+                return fail(GDN_ERR_RANGE, "accepted_idx[%d] = %d outside [0, %d)", i, h[i], l0.t_cap);
+    }
+    gdn::RollbackLayersArgs a{};
+    a.geo = rollback_args(&l0);
+    a.geo.state = nullptr;
+    a.geo.conv_state = nullptr;
+    a.geo.cap_ssm = nullptr;
+    a.geo.cap_conv = nullptr;
+    a.geo.slots = slots;
+    a.geo.idx = accepted_idx;
+    a.geo.n = n;
+    for (int l0i = 0; l0i < n_layers; l0i += gdn::kMaxLayersPerLaunch) {
+        a.n_layers = n_layers - l0i < gdn::kMaxLayersPerLaunch ? n_layers - l0i : gdn::kMaxLayersPerLaunch;
+        for (int j = 0; j < a.n_layers; ++j) {
+            const gdn_capture &c = layers[l0i + j];
+            a.layer[j] = gdn::LayerBuffers{c.state, c.conv_state, c.ssm, c.conv};
+        }
+        if (hipError_t e = gdn::launch_rollback_layers(a, st)) return hip_fail(e, "gdn_rollback_layers launch");
+    }
+    return ok();
+}
+
 GDN_API int gdn_rollback_trim(const gdn_capture *capture, int32_t slot, int32_t trim, int32_t n_tok, void *stream)
 {
     if (int r = check_rollback_capture(capture)) return r;
@@ -385,6 +450,18 @@ GDN_API int gdn_restore(const gdn_dims *dims, float *state, float *conv_state, c
 {
     return slot_copy("gdn_restore", dims, state, conv_state, snap_state, snap_conv, slots, n, stream);
 }
+
+namespace gdn {
+int abi_fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vfail(code, fmt, ap);
+    va_end(ap);
+    return code;
+}
+int abi_ok() { return ok(); }
+}  // namespace gdn
 
 GDN_API const char *gdn_last_error(void) { return g_last_error.c_str(); }
 

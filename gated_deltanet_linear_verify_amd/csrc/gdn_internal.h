@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct gdn_dims;  // include/gdn.h
+
 namespace gdn {
 
 constexpr int kTokenTile = 16;  // tokens per LDS tile in the verify kernels
@@ -51,6 +53,20 @@ struct RollbackArgs {
 };
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream);
 
+// Rollback of several layers' captures in one launch: the shapes, slots and indices are shared
+// (geo; its buffer pointers are unused), each layer brings its own four buffers.
+constexpr int kMaxLayersPerLaunch = 64;
+struct LayerBuffers {
+    float *state, *conv_state;
+    const float *cap_ssm, *cap_conv;
+};
+struct RollbackLayersArgs {
+    RollbackArgs geo;
+    int32_t n_layers;  // 1 .. kMaxLayersPerLaunch
+    LayerBuffers layer[kMaxLayersPerLaunch];
+};
+hipError_t launch_rollback_layers(const RollbackLayersArgs &a, hipStream_t stream);
+
 hipError_t launch_fill_zero(float *p, size_t n, hipStream_t stream);
 
 // Snapshot / restore: for each listed slot, copy its state and conv state from one pool-shaped
@@ -64,6 +80,13 @@ struct SlotCopyArgs {
     size_t conv_elems;  // 3 * C floats per slot
 };
 hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream);
+
+// The C ABI's thread-local last error (gdn_last_error): set it and return code, or clear it and
+// return GDN_OK.
+int abi_fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int abi_ok();
+// Validation of gdn_dims as every entry point does it (sets the last error; GDN_OK if valid).
+int abi_check_dims(const gdn_dims *d);
 
 struct PrefillArgs {
     int32_t n_kh, n_vh, d, T, C, slot;

@@ -9,12 +9,6 @@
 
 #define GDN_API extern "C" __attribute__((visibility("default")))
 
-namespace gdn {
-int abi_fail(int code, const char *msg);  // gdn_abi.cpp: records the thread-local last error
-int abi_ok();
-int abi_check_dims(const gdn_dims *d);
-}  // namespace gdn
-
 namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 constexpr size_t kMaxLds = 160 * 1024;
@@ -68,6 +62,6 @@ GDN_API int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, c
     a.o_ws = static_cast<float *>(workspace);
     gdn::LaunchCfg c{d.act_dtype == GDN_BF16, d.out_dtype == GDN_BF16, (d.flags & GDN_F_QK_NORM_SILU) != 0};
     if (hipError_t e = gdn::launch_prefill(a, c, static_cast<hipStream_t>(stream)))
-        return gdn::abi_fail(GDN_ERR_HIP, hipGetErrorString(e));
+        return gdn::abi_fail(GDN_ERR_HIP, "gdn_prefill launch: %s", hipGetErrorString(e));
     return gdn::abi_ok();
 }

@@ -11,21 +11,10 @@
 
 namespace gdn {
 
-__global__ __launch_bounds__(256) void rollback_kernel(RollbackArgs a)
+// One entry's copy: ns float4 of recurrent state and nc float4 of conv state, spread over the
+// gridDim.x blocks that share the entry, four loads in flight per thread.
+__device__ __forceinline__ void copy_entry(const f4 *src_s, f4 *dst_s, size_t ns, const f4 *src_c, f4 *dst_c, size_t nc)
 {
-    const int n = blockIdx.y;
-    const int slot = a.slots ? a.slots[n] : a.slot0;
-    const int idx = a.idx ? a.idx[n] : a.idx0;
-    if (slot < 0 || slot >= a.n_pool || idx < 0 || idx >= a.t_cap) return;  // uniform per block
-
-    const f4 *src_s = reinterpret_cast<const f4 *>(a.cap_ssm + ((size_t)slot * a.t_cap + idx) * a.ssm_elems);
-    f4 *dst_s = reinterpret_cast<f4 *>(a.state + (size_t)slot * a.ssm_elems);
-    const float *csrc = a.mode == 0 ? a.cap_conv + ((size_t)slot * (3 + a.t_cap) + idx + 1) * a.C
-                                    : a.cap_conv + ((size_t)slot * a.t_cap + idx) * a.conv_elems;
-    const f4 *src_c = reinterpret_cast<const f4 *>(csrc);
-    f4 *dst_c = reinterpret_cast<f4 *>(a.conv_state + (size_t)slot * a.conv_elems);
-
-    const size_t ns = a.ssm_elems / 4, nc = a.conv_elems / 4;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < ns; i += 4 * stride) {
@@ -39,14 +28,65 @@ __global__ __launch_bounds__(256) void rollback_kernel(RollbackArgs a)
     for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < nc; j += stride) dst_c[j] = src_c[j];
 }
 
-hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream)
+// Sources of entry (slot, idx) in one layer's capture: the state after position idx, and the conv
+// state that follows it (chain window rows idx+1 .. idx+3, or the tree node's 3-row record).
+__device__ __forceinline__ void rollback_entry(const RollbackArgs &a, const float *cap_ssm, const float *cap_conv,
+                                               float *state, float *conv_state, int slot, int idx)
 {
-    if (a.n <= 0) return hipSuccess;
-    const size_t vec = (a.ssm_elems + a.conv_elems) / 4;
+    const f4 *src_s = reinterpret_cast<const f4 *>(cap_ssm + ((size_t)slot * a.t_cap + idx) * a.ssm_elems);
+    f4 *dst_s = reinterpret_cast<f4 *>(state + (size_t)slot * a.ssm_elems);
+    const float *csrc = a.mode == 0 ? cap_conv + ((size_t)slot * (3 + a.t_cap) + idx + 1) * a.C
+                                    : cap_conv + ((size_t)slot * a.t_cap + idx) * a.conv_elems;
+    copy_entry(src_s, dst_s, a.ssm_elems / 4, reinterpret_cast<const f4 *>(csrc),
+               reinterpret_cast<f4 *>(conv_state + (size_t)slot * a.conv_elems), a.conv_elems / 4);
+}
+
+__global__ __launch_bounds__(256) void rollback_kernel(RollbackArgs a)
+{
+    const int n = blockIdx.y;
+    const int slot = a.slots ? a.slots[n] : a.slot0;
+    const int idx = a.idx ? a.idx[n] : a.idx0;
+    if (slot < 0 || slot >= a.n_pool || idx < 0 || idx >= a.t_cap) return;  // uniform per block
+    rollback_entry(a, a.cap_ssm, a.cap_conv, a.state, a.conv_state, slot, idx);
+}
+
+// Every layer of a model at once (hf2q qwen35_target.rs, rollback_kv walks the captures of all
+// linear-attention layers for the slot): blockIdx.z picks the layer, blockIdx.y the entry.  The
+// per-layer buffers travel in the kernel arguments, so no device-side table is needed.
+__global__ __launch_bounds__(256) void rollback_layers_kernel(RollbackLayersArgs a)
+{
+    const int n = blockIdx.y;
+    const int slot = a.geo.slots[n];
+    const int idx = a.geo.idx[n];
+    if (slot < 0 || slot >= a.geo.n_pool || idx < 0 || idx >= a.geo.t_cap) return;  // uniform per block
+    const LayerBuffers &L = a.layer[blockIdx.z];
+    rollback_entry(a.geo, L.cap_ssm, L.cap_conv, L.state, L.conv_state, slot, idx);
+}
+
+static unsigned copy_blocks(size_t ssm_elems, size_t conv_elems)
+{
+    const size_t vec = (ssm_elems + conv_elems) / 4;
     size_t blocks = (vec + 256 * 4 - 1) / (256 * 4);
     if (blocks > 512) blocks = 512;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(rollback_kernel, dim3((unsigned)blocks, (unsigned)a.n), dim3(256), 0, stream, a);
+    return (unsigned)blocks;
+}
+
+hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream)
+{
+    if (a.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rollback_kernel, dim3(copy_blocks(a.ssm_elems, a.conv_elems), (unsigned)a.n), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rollback_layers(const RollbackLayersArgs &a, hipStream_t stream)
+{
+    if (a.geo.n <= 0 || a.n_layers <= 0) return hipSuccess;
+    if (a.n_layers > kMaxLayersPerLaunch) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rollback_layers_kernel,
+                       dim3(copy_blocks(a.geo.ssm_elems, a.geo.conv_elems), (unsigned)a.geo.n, (unsigned)a.n_layers),
+                       dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -57,32 +97,17 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(SlotCopyArgs a)
 {
     const int slot = a.slots[blockIdx.y];
     if (slot < 0 || slot >= a.n_pool) return;  // uniform per block
-    const f4 *src_s = reinterpret_cast<const f4 *>(a.src_state + (size_t)slot * a.ssm_elems);
-    f4 *dst_s = reinterpret_cast<f4 *>(a.dst_state + (size_t)slot * a.ssm_elems);
-    const f4 *src_c = reinterpret_cast<const f4 *>(a.src_conv + (size_t)slot * a.conv_elems);
-    f4 *dst_c = reinterpret_cast<f4 *>(a.dst_conv + (size_t)slot * a.conv_elems);
-    const size_t ns = a.ssm_elems / 4, nc = a.conv_elems / 4;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < ns; i += 4 * stride) {
-        const f4 v0 = src_s[i], v1 = src_s[i + stride], v2 = src_s[i + 2 * stride], v3 = src_s[i + 3 * stride];
-        dst_s[i] = v0;
-        dst_s[i + stride] = v1;
-        dst_s[i + 2 * stride] = v2;
-        dst_s[i + 3 * stride] = v3;
-    }
-    for (; i < ns; i += stride) dst_s[i] = src_s[i];
-    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < nc; j += stride) dst_c[j] = src_c[j];
+    copy_entry(reinterpret_cast<const f4 *>(a.src_state + (size_t)slot * a.ssm_elems),
+               reinterpret_cast<f4 *>(a.dst_state + (size_t)slot * a.ssm_elems), a.ssm_elems / 4,
+               reinterpret_cast<const f4 *>(a.src_conv + (size_t)slot * a.conv_elems),
+               reinterpret_cast<f4 *>(a.dst_conv + (size_t)slot * a.conv_elems), a.conv_elems / 4);
 }
 
 hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream)
 {
     if (a.n <= 0) return hipSuccess;
-    const size_t vec = (a.ssm_elems + a.conv_elems) / 4;
-    size_t blocks = (vec + 256 * 4 - 1) / (256 * 4);
-    if (blocks > 512) blocks = 512;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(slot_copy_kernel, dim3((unsigned)blocks, (unsigned)a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(slot_copy_kernel, dim3(copy_blocks(a.ssm_elems, a.conv_elems), (unsigned)a.n), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

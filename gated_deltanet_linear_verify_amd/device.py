@@ -109,3 +109,22 @@ def snapshot_replay_round(d: dict, snap: dict, n_accept: int, stream=None) -> No
         gdn.gdn_verify(d["dims"], d["state"], d["conv_state"], rep["qkv"], rep["z"], rep["alpha"], rep["beta"],
                        d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], None, rep["out"], n_accept,
                        d["slot_ids"], B, stream)
+
+
+def layers_step(layers: list, slot_ids, accepted_idx, stream=None) -> None:
+    """One spec-decode step over several layers, eagerly: gdn_verify of every layer (capture on,
+    all uploaded tokens, every batch entry) with the shared slot_ids, then one
+    gdn_rollback_layers to accepted_idx.  The launches a recorded gdn.Graph replays."""
+    B, T = layers[0]["qkv"].shape[0], layers[0]["qkv"].shape[1]
+    for d in layers:
+        gdn.gdn_verify(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"], d["beta"],
+                       d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], d["capture"], d["out"], T, slot_ids,
+                       B, stream)
+    gdn.gdn_rollback_layers([d["capture"] for d in layers], slot_ids, accepted_idx, B, stream)
+
+
+def layers_graph(layers: list, slot_ids, accepted_idx,
+                 phases: int = gdn.GDN_GRAPH_VERIFY | gdn.GDN_GRAPH_ROLLBACK) -> "gdn.Graph":
+    """The same step recorded once (gdn_graph_create) over the uploaded layers' buffers."""
+    B, T = layers[0]["qkv"].shape[0], layers[0]["qkv"].shape[1]
+    return gdn.Graph(layers[0]["dims"], layers, layers[0]["capture"].t_cap, T, slot_ids, B, accepted_idx, phases)

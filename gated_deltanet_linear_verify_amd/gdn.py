@@ -22,7 +22,8 @@ GDN_F_CHECK_INDICES = 0x2
 
 EXPORTS = ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch", "gdn_rollback_trim",
            "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_capture_bytes", "gdn_reset",
-           "gdn_snapshot", "gdn_restore", "gdn_last_error", "gdn_version")
+           "gdn_snapshot", "gdn_restore", "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch",
+           "gdn_graph_destroy", "gdn_last_error", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -43,6 +44,14 @@ class gdn_capture(ctypes.Structure):
                 ("state", ctypes.c_void_p), ("conv_state", ctypes.c_void_p),
                 ("t_cap", ctypes.c_int32), ("mode", ctypes.c_int32)]
 
+
+class gdn_layer(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("state", "conv_state", "qkv", "z", "alpha", "beta", "A_log",
+                                                "dt_bias", "conv_w", "norm_w", "cap_ssm", "cap_conv", "out")]
+
+
+GDN_GRAPH_VERIFY = 0x1
+GDN_GRAPH_ROLLBACK = 0x2
 
 _lib = None
 
@@ -71,8 +80,14 @@ def lib() -> ctypes.CDLL:
         L.gdn_reset.argtypes = [D, P, P, I, P]
         L.gdn_snapshot.argtypes = [D, P, P, P, P, P, I, P]
         L.gdn_restore.argtypes = [D, P, P, P, P, P, I, P]
+        L.gdn_rollback_layers.argtypes = [Cp, I, P, P, I, P]
+        L.gdn_graph_create.argtypes = [D, ctypes.POINTER(gdn_layer), I, I, I, P, I, P, ctypes.c_uint32,
+                                       ctypes.POINTER(ctypes.c_void_p)]
+        L.gdn_graph_launch.argtypes = [P, P]
+        L.gdn_graph_destroy.argtypes = [P]
         for f in ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch",
-                  "gdn_rollback_trim", "gdn_prefill", "gdn_reset", "gdn_snapshot", "gdn_restore"):
+                  "gdn_rollback_trim", "gdn_prefill", "gdn_reset", "gdn_snapshot", "gdn_restore",
+                  "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch", "gdn_graph_destroy"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_version.restype = ctypes.c_char_p
@@ -155,6 +170,40 @@ def gdn_rollback(capture: Capture, slot: int, accepted_idx: int, stream=None) ->
 
 def gdn_rollback_batch(capture: Capture, slots, accepted_idx, n: int, stream=None) -> None:
     _check(lib().gdn_rollback_batch(capture.ref, _p(slots), _p(accepted_idx), n, _stream(stream)))
+
+
+def gdn_rollback_layers(layers, slots, accepted_idx, n: int, stream=None) -> None:
+    """One launch (per 64 layers) restoring every layer's capture for the listed slots."""
+    arr = (gdn_capture * len(layers))(*[c.c for c in layers])
+    _check(lib().gdn_rollback_layers(arr, len(layers), _p(slots), _p(accepted_idx), n, _stream(stream)))
+
+
+class Graph:
+    """A recorded spec-decode step (gdn_graph_create) over layers given as dicts of torch tensors
+    with the gdn_layer field names; replay with launch(), freed by close() or on collection."""
+
+    def __init__(self, dims, layers, t_cap: int, n_tok: int, slot_ids, n_batch: int, accepted_idx,
+                 phases: int = GDN_GRAPH_VERIFY | GDN_GRAPH_ROLLBACK):
+        arr = (gdn_layer * len(layers))(*[gdn_layer(*[_p(L[n]) for n, _ in gdn_layer._fields_])
+                                          for L in layers])
+        self._h = ctypes.c_void_p(None)
+        self._keep = (layers, slot_ids, accepted_idx)  # the graph holds raw pointers into these
+        _check(lib().gdn_graph_create(ctypes.byref(dims), arr, len(layers), t_cap, n_tok, _p(slot_ids),
+                                      n_batch, _p(accepted_idx), phases, ctypes.byref(self._h)))
+
+    def launch(self, stream=None) -> None:
+        _check(lib().gdn_graph_launch(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if self._h:
+            _check(lib().gdn_graph_destroy(self._h))
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def gdn_rollback_trim(capture: Capture, slot: int, trim: int, n_tok: int, stream=None) -> None:

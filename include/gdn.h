@@ -215,6 +215,70 @@ int gdn_snapshot(const gdn_dims *dims, const float *state, const float *conv_sta
 int gdn_restore(const gdn_dims *dims, float *state, float *conv_state, const float *snap_state,
                 const float *snap_conv, const int32_t *slots, int32_t n, void *stream);
 
+/*
+ * Rollback of every GDN layer of a model in one launch.  The pages keep one capture per
+ * delta-net layer (lucebox-hub internal.h, struct TargetCache: ssm_intermediate and
+ * conv_input_cache, one each per layer) and a slot's rollback restores all of them (hf2q
+ * qwen35_target.rs, rollback_kv: the LA-state rollback covers the model's linear-attention
+ * layers for that slot).
+ *   layers: host array of n_layers capture descriptors, one per layer, all with equal dims,
+ *     t_cap and mode; no two may share a state or conv_state buffer.  Read during the call only.
+ *   slots, accepted_idx: device int32 [n], shared by every layer (a slot accepts the same
+ *     drafted tokens in every layer).
+ * For every layer l the result is that of gdn_rollback_batch(&layers[l], slots, accepted_idx,
+ * n): bitwise copies, stream-ordered, entries with an out-of-range slot or index skipped (under
+ * GDN_F_CHECK_INDICES in layers[0].dims.flags: GDN_ERR_RANGE).  Up to 64 layers go into one
+ * launch; more take one launch per 64.  n == 0 is a no-op; n outside [0, min(n_pool, 65535)] or
+ * n_layers < 1 is GDN_ERR_RANGE; NULL layers, a bad descriptor, descriptors that differ in dims,
+ * t_cap or mode, or a shared state buffer are GDN_ERR_ARG.
+ */
+int gdn_rollback_layers(const gdn_capture *layers, int32_t n_layers, const int32_t *slots,
+                        const int32_t *accepted_idx, int32_t n, void *stream);
+
+/*
+ * A whole GDN spec-decode step recorded once as a HIP graph and replayed with one launch.  The
+ * pages replay a recorded graph per step to cut launch overhead (lucebox dflash_draft_kv.h: the
+ * draft's CUDA graph is replayed each step; lucebox-hub internal.h, the note on the number of
+ * graph launches per step) and keep one capture per delta-net layer (struct TargetCache).
+ *
+ * gdn_layer names one layer's buffers, with the meaning and layout of the gdn_verify arguments of
+ * the same names; cap_ssm / cap_conv form that layer's chain capture of t_cap positions, restored
+ * into state / conv_state.
+ */
+typedef struct gdn_layer {
+    float *state;
+    float *conv_state;
+    const void *qkv, *z, *alpha, *beta;
+    const float *A_log, *dt_bias, *conv_w, *norm_w;
+    float *cap_ssm;
+    float *cap_conv;
+    void *out;
+} gdn_layer;
+
+#define GDN_GRAPH_VERIFY 0x1u   /* gdn_verify of every layer, in layer order, capture on */
+#define GDN_GRAPH_ROLLBACK 0x2u /* then gdn_rollback_layers of every layer */
+
+typedef struct gdn_graph gdn_graph; /* opaque; owned by the caller between create and destroy */
+
+/*
+ * Record the phases in `phases` (GDN_GRAPH_* bits, at least one) for n_layers layers, n_tok
+ * tokens and the n_batch slots in slot_ids (device int32 [n_batch]); the rollback phase restores
+ * the slots of slot_ids to accepted_idx (device int32 [n_batch]).  Every argument is checked as
+ * the corresponding gdn_verify / gdn_rollback_layers call checks it, once, here.  The graph keeps
+ * the pointers and sizes given now and reads what they point at when it runs, so between
+ * launches the caller rewrites activations, slot ids and accepted indices in place.  The layer
+ * array is read during the call only.  GDN_F_CHECK_INDICES is rejected (GDN_ERR_ARG): its host
+ * copy cannot be recorded.  Recording uses a private stream and allocates the graph; on error
+ * *graph is NULL and nothing is left allocated.
+ */
+int gdn_graph_create(const gdn_dims *dims, const gdn_layer *layers, int32_t n_layers, int32_t t_cap,
+                     int32_t n_tok, const int32_t *slot_ids, int32_t n_batch,
+                     const int32_t *accepted_idx, uint32_t phases, gdn_graph **graph);
+/* Enqueue one replay of the recorded step on `stream`.  Replays on one graph must not overlap. */
+int gdn_graph_launch(const gdn_graph *graph, void *stream);
+/* Free the graph (NULL is a no-op).  Pending replays finish first. */
+int gdn_graph_destroy(gdn_graph *graph);
+
 /* Thread-local description of the last error of this thread ("" after success). */
 const char *gdn_last_error(void);
 

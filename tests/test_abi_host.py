@@ -152,3 +152,73 @@ def test_snapshot_restore_validation():
         assert fn(ctypes.byref(d), *bufs[:3], mis, FAKE, 2, None) == gdn.GDN_ERR_ARG
         bad = _dims(n_pool=4, d_conv=3)
         assert fn(ctypes.byref(bad), *bufs, FAKE, 1, None) == gdn.GDN_ERR_SHAPE
+
+
+def test_rollback_layers_validation():
+    """gdn_rollback_layers checks every descriptor, their agreement and buffer ownership before
+    any launch; n == 0 is a no-op."""
+    L = _lib_or_skip()
+    d = _dims(n_pool=4)
+
+    def cap(base, t_cap=16, mode=gdn.GDN_CHAIN, dims=d):
+        return gdn.gdn_capture(dims, base, base + 0x100, base + 0x200, base + 0x300, t_cap, mode)
+
+    def arr(*caps):
+        return (gdn.gdn_capture * len(caps))(*caps)
+
+    two = arr(cap(0x1000), cap(0x2000))
+    assert L.gdn_rollback_layers(two, 2, None, None, 0, None) == gdn.GDN_OK
+    assert L.gdn_rollback_layers(None, 2, FAKE, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    assert L.gdn_rollback_layers(two, 0, FAKE, FAKE, 1, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback_layers(two, 2, None, None, 2, None) == gdn.GDN_ERR_ARG
+    assert L.gdn_rollback_layers(two, 2, FAKE, FAKE, 5, None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_rollback_layers(two, 2, FAKE, FAKE, -1, None) == gdn.GDN_ERR_RANGE
+    # layers that disagree in t_cap, mode or dims
+    assert L.gdn_rollback_layers(arr(cap(0x1000), cap(0x2000, t_cap=8)), 2, FAKE, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    assert L.gdn_rollback_layers(arr(cap(0x1000), cap(0x2000, mode=gdn.GDN_TREE)), 2, FAKE, FAKE, 1,
+                                 None) == gdn.GDN_ERR_ARG
+    assert L.gdn_rollback_layers(arr(cap(0x1000), cap(0x2000, dims=_dims(n_pool=5))), 2, FAKE, FAKE, 1,
+                                 None) == gdn.GDN_ERR_ARG
+    # two layers restoring into the same state buffer
+    assert L.gdn_rollback_layers(arr(cap(0x1000), cap(0x1000)), 2, FAKE, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    # a bad descriptor anywhere: its own check's code, naming the layer
+    bad = gdn.gdn_capture(d, 0x3000, 0x3100, 0x3200, 0x3308, 16, gdn.GDN_CHAIN)
+    assert L.gdn_rollback_layers(arr(cap(0x1000), bad), 2, FAKE, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    assert "layer 1" in gdn.last_error()
+    bad_shape = cap(0x3000, dims=_dims(n_pool=4, d_conv=3))
+    assert L.gdn_rollback_layers(arr(bad_shape), 1, FAKE, FAKE, 1, None) == gdn.GDN_ERR_SHAPE
+
+
+def test_graph_validation():
+    """gdn_graph_create rejects bad arguments before it records anything (no HIP call is made
+    for these); launch of a NULL graph fails, destroy of NULL is a no-op."""
+    L = _lib_or_skip()
+    d = _dims(n_pool=4)
+    lay = gdn.gdn_layer(*([0x1000] * 13))
+    arr = (gdn.gdn_layer * 2)(lay, lay)
+    h = ctypes.c_void_p(None)
+    VR = gdn.GDN_GRAPH_VERIFY | gdn.GDN_GRAPH_ROLLBACK
+
+    def create(dims=d, layers=arr, n_layers=2, t_cap=16, n_tok=16, slots=FAKE, n_batch=1, acc=FAKE,
+               phases=VR, out=ctypes.byref(h)):
+        return L.gdn_graph_create(ctypes.byref(dims) if dims is not None else None, layers, n_layers,
+                                  t_cap, n_tok, slots, n_batch, acc, phases, out)
+
+    assert create(out=None) == gdn.GDN_ERR_ARG
+    assert create(dims=None) == gdn.GDN_ERR_ARG
+    assert create(layers=None) == gdn.GDN_ERR_ARG
+    assert create(dims=_dims(n_pool=4, flags=gdn.GDN_F_CHECK_INDICES)) == gdn.GDN_ERR_ARG
+    assert "cannot be recorded" in gdn.last_error()
+    assert create(phases=0) == gdn.GDN_ERR_ARG
+    assert create(phases=0x4) == gdn.GDN_ERR_ARG
+    assert create(n_layers=0) == gdn.GDN_ERR_RANGE
+    assert create(t_cap=8) == gdn.GDN_ERR_RANGE
+    assert create(n_tok=0) == gdn.GDN_ERR_RANGE
+    assert create(acc=None) == gdn.GDN_ERR_ARG
+    assert create(slots=None) == gdn.GDN_ERR_ARG
+    bad = gdn.gdn_layer(*([0x1000] * 12 + [0]))
+    assert create(layers=(gdn.gdn_layer * 2)(lay, bad)) == gdn.GDN_ERR_ARG
+    assert "layer 1" in gdn.last_error()
+    assert h.value is None
+    assert L.gdn_graph_launch(None, None) == gdn.GDN_ERR_ARG
+    assert L.gdn_graph_destroy(None) == gdn.GDN_OK
