@@ -95,11 +95,12 @@ struct PrefillArgs {
     const void *qkv, *z, *alpha, *beta;
     const float *A_log, *dt_bias, *conv_w, *norm_w;
     void *out;
-    float *o_ws;  // workspace: [T][H_v][d_v] fp32 readout before the norm
+    float *ws;  // workspace of prefill_workspace_bytes(): per-chunk operands and the fp32 readout
 };
-// Chunked prefill: a chunk-scan kernel over H_v * (d / 16) workgroups, then the norm epilogue.
+// Chunked prefill: a chunk-parallel prep kernel (conv, gates, T = (I + A)^-1 and P per chunk and
+// value head), a sequential scan over H_v * (d / 16) workgroups, then the norm epilogue.
 hipError_t launch_prefill(const PrefillArgs &a, const LaunchCfg &c, hipStream_t stream);
-size_t prefill_workspace_bytes(int d, int n_vh, int T);
-size_t prefill_lds_bytes(int d, bool act_bf16);
+size_t prefill_workspace_bytes(int d, int n_kh, int n_vh, int T);
+size_t prefill_lds_bytes(int d, bool act_bf16);  // the larger of the two kernels' LDS
 
 }  // namespace gdn

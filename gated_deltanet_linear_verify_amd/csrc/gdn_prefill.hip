@@ -14,12 +14,20 @@
 // which is the token recurrence unrolled (u_t = beta_t (v_t - rho_t S_{t-1} k_t)); only ratios
 // exp(Gamma_t - Gamma_s) with s <= t and gamma_t <= 1 are ever formed.
 //
-// Kernel 1 (chunk scan): one workgroup per (value head, block of 16 value rows).  Rows of S are
+// Everything that does not depend on S (conv, gates, A -> T, P) is the same for every value-row
+// block and every chunk can compute it at once, so it runs first, chunk-parallel; only Y, U, O
+// and S' remain on the sequential chain of chunks.
+// Kernel 1 (prep): one workgroup per (chunk, value head): conv of the chunk's q | k | v channels,
+// the gates, A and P on MFMA, T by blocked fp32 forward substitution.  It writes the operands of
+// the scan to the workspace as LDS images (the layouts the scan reads), so the scan copies them
+// with flat global_load_lds transfers.
+// Kernel 2 (scan): one workgroup per (value head, block of 16 value rows).  Rows of S are
 // independent given the keys, so the blocks never communicate; each walks the chunks in order with
-// its S block in LDS.  Dense products run on v_mfma_f32_16x16x32_bf16 with each fp32 operand
-// split into bf16 hi + lo parts (a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi, ~2^-16 relative), so the
-// fp32 state is not rounded to bf16; with fp32 activations the products run on the fp32 MFMA.  T comes from a blocked fp32 forward substitution.
-// Kernel 2 (epilogue): RMS norm over d_v + SiLU(z) gate of every token (the d_v blocks of kernel 1
+// its S block in LDS while the next chunk's operands travel in.  Dense products run on
+// v_mfma_f32_16x16x32_bf16 with each fp32 operand split into bf16 hi + lo parts (a b ~ a_hi b_hi +
+// a_hi b_lo + a_lo b_hi, ~2^-16 relative), so the fp32 state is not rounded to bf16; with fp32
+// activations the products run on the fp32 MFMA.
+// Kernel 3 (epilogue): RMS norm over d_v + SiLU(z) gate of every token (the d_v blocks of kernel 2
 // meet here through an fp32 workspace), and the conv state after the last token.
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -126,32 +134,87 @@ __device__ __forceinline__ f4 blk16(const float *X, int xr0, int xc0, const floa
     return acc;
 }
 
-template <int D, typename act_t>
-struct PrefillLds {
-    static constexpr int C = kChunk;
-    static constexpr int NCH = 2 * D + kDB;  // q | k | v-block channels
-    static constexpr size_t q = 0;                                    // [C][D]    swizzled
-    static constexpr size_t k = q + sizeof(float) * C * D;            // [C][D]    swizzled
-    static constexpr size_t vb = k + sizeof(float) * C * D;           // [C][DB]
-    static constexpr size_t s = vb + sizeof(float) * C * kDB;         // [DB][D]   the state block, swizzled
-    static constexpr size_t tm = s + sizeof(float) * kDB * D;         // [C][kCP]  A, then T
-    static constexpr size_t pm = tm + sizeof(float) * C * kCP;        // [C][kCP]  P
-    static constexpr size_t yt = pm + sizeof(float) * C * kCP;        // [DB][kCP] Y^T
-    static constexpr size_t ut = yt + sizeof(float) * kDB * kCP;      // [DB][kCP] U^T; scratch of the inverse
-    static constexpr size_t hist = ut + sizeof(float) * kDB * kCP;    // [3][NCH]  raw rows before the chunk
-    static constexpr size_t gate = hist + sizeof(float) * 3 * NCH;    // Gamma, gamma, beta, decay [4][C]
-    static constexpr size_t ab = gate + sizeof(float) * 4 * C;        // alpha, beta words [2][C]
-    static constexpr size_t raw = ab + sizeof(uint32_t) * 2 * C;      // [C][NCH]  the chunk's raw rows
-    static constexpr size_t total = raw + sizeof(act_t) * C * NCH;
-};
-static_assert(PrefillLds<128, uint16_t>::total <= 160 * 1024, "bf16 d=128 prefill must fit one CU's LDS");
 
+// Workspace (floats), nc = number of chunks:
+//   o  [nc * 64][H_v][d]         fp32 readout before the norm (whole chunks: the tail is scratch)
+//   qk [nc][H_k][2][64 * d]      conv'd q then k of the chunk, swizzled (swz<d>), per key head
+//   t  [nc][H_v][64 * kCP]       T = (I + A)^-1, padded rows
+//   p  [nc][H_v][64 * kCP]       P, padded rows
+//   v  [nc][H_v][d / 16][64][16] conv'd v, one block of 16 value rows per scan workgroup
+//   g  [nc][H_v][256]            gamma | beta | exp(Gamma_C - Gamma) | 0, 64 each
+constexpr int kGateRec = 4 * kChunk;
+struct PrefillWs {
+    size_t o, qk, t, p, v, g, total;
+};
+__host__ __device__ inline PrefillWs prefill_ws(int d, int n_kh, int n_vh, int T)
+{
+    const size_t nc = ((size_t)T + kChunk - 1) / kChunk;
+    PrefillWs w;
+    w.o = 0;
+    w.qk = w.o + nc * kChunk * n_vh * d;
+    w.t = w.qk + nc * n_kh * 2 * kChunk * d;
+    w.p = w.t + nc * n_vh * kChunk * kCP;
+    w.v = w.p + nc * n_vh * kChunk * kCP;
+    w.g = w.v + nc * n_vh * kChunk * d;
+    w.total = w.g + nc * n_vh * kGateRec;
+    return w;
+}
+
+// Copy n16 16-byte units from global memory to LDS with global_load_lds (lane i of a wave lands at
+// the wave's base + 16 i).  Thread tid issues units tid, tid + 256, ...: every wave issues
+// floor(n16 / 256) transfers, the first waves one more when n16 is not a multiple of 256.
+__device__ __forceinline__ void dma_image(const float *g, float *l, int n16, int tid)
+{
+    for (int i = tid; i < n16; i += kPThreads) lds_dma16(g + 4 * i, l + 4 * i);
+}
+
+template <int D, typename act_t>
+struct PrepLds {
+    static constexpr int C = kChunk;
+    static constexpr int NCH = 3 * D;  // q | k | v channels of (key head, value head)
+    static constexpr size_t raw_bytes = sizeof(act_t) * (3 + C) * NCH;
+    static constexpr size_t tp_bytes = sizeof(float) * (2 * C * kCP + 4 * 256);
+    static constexpr size_t q = 0;                                  // [C][D] swizzled
+    static constexpr size_t k = q + sizeof(float) * C * D;          // [C][D] swizzled
+    static constexpr size_t raw = k + sizeof(float) * C * D;        // [3 + C][NCH] raw rows t0-3 ..
+    static constexpr size_t tm = raw;                               // after the conv: [C][kCP] A, then T
+    static constexpr size_t pm = tm + sizeof(float) * C * kCP;      //                 [C][kCP] P
+    static constexpr size_t scr = pm + sizeof(float) * C * kCP;     //                 [4][16][16] scratch
+    static constexpr size_t hist = raw + (raw_bytes > tp_bytes ? raw_bytes : tp_bytes);  // [3][NCH] fp32
+    static constexpr size_t gate = hist + sizeof(float) * 3 * NCH;  // Gamma, gamma, beta, decay [4][C]
+    static constexpr size_t ab = gate + sizeof(float) * 4 * C;      // alpha, beta words [2][C]
+    static constexpr size_t total = ab + sizeof(uint32_t) * 2 * C;
+};
+static_assert(PrepLds<128, uint16_t>::total <= 160 * 1024, "bf16 d=128 prep must fit one CU's LDS");
+static_assert(PrepLds<64, float>::total <= 160 * 1024, "fp32 d=64 prep must fit one CU's LDS");
+
+template <int D>
+struct ScanLds {
+    static constexpr int C = kChunk;
+    static constexpr size_t kimg = sizeof(float) * C * D;    // a q or k image
+    static constexpr size_t timg = sizeof(float) * C * kCP;  // a T or P image
+    static constexpr size_t vimg = sizeof(float) * C * kDB;  // a v block image
+    static constexpr size_t gimg = sizeof(float) * kGateRec;
+    static constexpr size_t kb = 0;                          // [2] k images (this chunk, next chunk)
+    static constexpr size_t vb = kb + 2 * kimg;              // [2] v block images
+    static constexpr size_t gb = vb + 2 * vimg;              // [2] gate records
+    static constexpr size_t q = gb + 2 * gimg;               // q image
+    static constexpr size_t tm = q + kimg;                   // T
+    static constexpr size_t pm = tm + timg;                  // P
+    static constexpr size_t s = pm + timg;                   // [DB][D] the state block, swizzled
+    static constexpr size_t yt = s + sizeof(float) * kDB * D;   // [DB][kCP] Y^T
+    static constexpr size_t ut = yt + sizeof(float) * kDB * kCP;  // [DB][kCP] U^T
+    static constexpr size_t total = ut + sizeof(float) * kDB * kCP;
+};
+static_assert(ScanLds<128>::total <= 160 * 1024, "d=128 scan must fit one CU's LDS");
+
+// ============================== kernel 1: per (chunk, value head) ==============================
 template <int D, bool ACT_BF16, bool QKN>
-__global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
-    using L = PrefillLds<D, act_t>;
-    constexpr bool F32 = !ACT_BF16;  // fp32 activations: fp32 MFMA products
+    using L = PrepLds<D, act_t>;
+    constexpr bool F32 = !ACT_BF16;
     constexpr int C = kChunk;
     constexpr int NCH = L::NCH;
     constexpr int VEC = 16 / (int)sizeof(act_t);
@@ -160,236 +223,374 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int R = a.n_vh / a.n_kh;
 
-    const int h = blockIdx.x / NB, blk = blockIdx.x % NB;
+    const int c = blockIdx.x / a.n_vh, h = blockIdx.x % a.n_vh;
     const int hk = h / R;
     const int T = a.T;
     const int Cc = a.C;  // conv channels
-    const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + h * D + blk * kDB;
+    const int t0 = c * C, Lc = min(C, T - t0);
+    const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + h * D;
+    const PrefillWs w = prefill_ws(D, a.n_kh, a.n_vh, T);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *Q = reinterpret_cast<float *>(smem + L::q);
     float *K = reinterpret_cast<float *>(smem + L::k);
-    float *Vb = reinterpret_cast<float *>(smem + L::vb);
-    float *S = reinterpret_cast<float *>(smem + L::s);
+    act_t *raw = reinterpret_cast<act_t *>(smem + L::raw);
     float *Tm = reinterpret_cast<float *>(smem + L::tm);
     float *Pm = reinterpret_cast<float *>(smem + L::pm);
-    float *Yt = reinterpret_cast<float *>(smem + L::yt);
-    float *Ut = reinterpret_cast<float *>(smem + L::ut);
     float *hist = reinterpret_cast<float *>(smem + L::hist);
     float *Gam = reinterpret_cast<float *>(smem + L::gate);  // Gamma_t
     float *gam = Gam + C;                                    // gamma_t = exp(Gamma_t)
     float *bet = gam + C;                                    // beta_t (0 past the end)
     float *dec = bet + C;                                    // exp(Gamma_C - Gamma_t)
     uint32_t *abw = reinterpret_cast<uint32_t *>(smem + L::ab);  // the words holding alpha_t, beta_t
-    act_t *raw = reinterpret_cast<act_t *>(smem + L::raw);
 
     const act_t *qkv = static_cast<const act_t *>(a.qkv);
     auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
-    auto to_f32 = [](act_t x) -> float {
-        if constexpr (ACT_BF16)
-            return bf16_to_f32(x);
-        else
-            return x;
-    };
     // alpha / beta of (token t, head h) sit in the 32-bit word at element (t H_v + h) & ~1 (bf16) or
     // t H_v + h (fp32); the word never leaves the row because H_v is even for bf16
     constexpr int EPW = ACT_BF16 ? 2 : 1;  // elements per word
     const int ab_half = ACT_BF16 ? (h & 1) : 0;
-    auto word_val = [&](uint32_t w) -> float {
+    auto word_val = [&](uint32_t wd) -> float {
         if constexpr (ACT_BF16)
-            return bf16_to_f32((uint16_t)(ab_half ? (w >> 16) : (w & 0xffffu)));
+            return bf16_to_f32((uint16_t)(ab_half ? (wd >> 16) : (wd & 0xffffu)));
         else
-            return __builtin_bit_cast(float, w);
+            return __builtin_bit_cast(float, wd);
     };
-    // stage chunk c: raw rows via global_load_lds (lane i lands at the wave's base + 16 i, rows
-    // past the end are skipped) and the alpha / beta words (4-byte global_load_lds, lane t -> word t)
-    auto stage = [&](int c) {
-        const int t0 = c * C, Lc = min(C, T - t0);
+
+    // ---- stage: raw rows of tokens t0-3 .. t0+Lc-1 (row r holds token t0-3+r; before the first
+    // chunk the three rows come from the conv state instead), alpha / beta words
+    {
         constexpr int nvr = NCH / VEC;
-        for (int it = tid; it < Lc * nvr; it += kPThreads) {
-            const int r = it / nvr, lc = (it % nvr) * VEC;
-            lds_dma16(qkv + ((size_t)t0 + r) * Cc + gchan(lc), raw + it * VEC);
+        const int r0 = c == 0 ? 3 : 0;
+        for (int it = tid; it < (3 + Lc - r0) * nvr; it += kPThreads) {
+            const int r = r0 + it / nvr, lc = (it % nvr) * VEC;
+            lds_dma16(qkv + ((size_t)t0 - 3 + r) * Cc + gchan(lc), raw + r0 * NCH + it * VEC);
         }
         if (wave < 2 && lane < Lc) {
             const size_t e = ((size_t)t0 + lane) * a.n_vh + (h & ~(EPW - 1));
             const void *src = wave == 0 ? a.alpha : a.beta;
             lds_dma4(static_cast<const unsigned char *>(src) + e * sizeof(act_t), abw + wave * C + lane);
         }
-    };
-
-    // ---- prologue: state block, conv taps of this thread's channel groups, conv state
-    // conv taps of this thread's channel groups: q | k (lane -> channels 4 lane .. 4 lane + 3) and v
-    f4 wqk[4], wv[4];
-    {
-        const int lq = lane < QKG ? 4 * lane : 0;
-        const int lv = 2 * D + 4 * (tid & 3);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            wqk[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lq + j) * 4);
-            wv[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lv + j) * 4);
+        if (c == 0) {
+            const float *cs = a.conv_state + (size_t)a.slot * 3 * Cc;
+            for (int i = tid; i < 3 * NCH; i += kPThreads) hist[i] = cs[(size_t)(i / NCH) * Cc + gchan(i % NCH)];
         }
-    }
-    const float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
-    for (int i = tid; i < kDB * D / 4; i += kPThreads) {
-        const int r = (4 * i) / D, c = (4 * i) % D;
-        *reinterpret_cast<f4 *>(S + swz<D>(r, c)) = reinterpret_cast<const f4 *>(st)[i];
-    }
-    const float *cs = a.conv_state + (size_t)a.slot * 3 * Cc;
-    for (int i = tid; i < 3 * NCH; i += kPThreads) hist[i] = cs[(size_t)(i / NCH) * Cc + gchan(i % NCH)];
-    // the upper blocks of A / T and P stay zero for the whole call
-    for (int i = tid; i < C * kCP; i += kPThreads) {
-        Tm[i] = 0.f;
-        Pm[i] = 0.f;
     }
     const float negA = -expf(a.A_log[h]), dtb = a.dt_bias[h];
-    stage(0);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    lds_barrier();
 
-    // readout tile of wave w: rows t = 16 w + 4 (lane / 16) + r, value row blk*16 + lane % 16
-    f4 o_prev = {0.f, 0.f, 0.f, 0.f};
-    auto store_o = [&](int cc, f4 o) {
-        const int tb = cc * C, Lb = min(C, T - tb);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + (lane >> 4) * 4 + r;
-            if (t < Lb) a.o_ws[(((size_t)tb + t) * a.n_vh + h) * D + blk * kDB + (lane & 15)] = o[r];
+    // ---- gates: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
+    if (wave == 0) {
+        float g = 0.f, b = 0.f;
+        if (lane < Lc) {
+            g = negA * softplus_f(word_val(abw[lane]) + dtb);
+            b = word_val(abw[C + lane]);
         }
+        float x = g;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        Gam[lane] = x;
+        gam[lane] = expf(x);
+        bet[lane] = b;
+        dec[lane] = expf(__shfl(x, 63) - x);
+    }
+
+    // ---- conv: q | k (wave w: tokens 16w .. 16w+15, lane: 4 channels), v (thread: a token, 4
+    // channels of every 16-row block, written straight to the workspace)
+    auto xrow = [&](int t, int lc) -> f4 {  // 4 raw channels of token t0 + t (t >= -3)
+        f4 x;
+        if (t < 0 && c == 0) {
+            x = *reinterpret_cast<const f4 *>(hist + (3 + t) * NCH + lc);
+        } else if constexpr (ACT_BF16) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(raw + (3 + t) * NCH + lc);
+            x = f4{bf16_to_f32((uint16_t)(u.x & 0xffffu)), bf16_to_f32((uint16_t)(u.x >> 16)),
+                   bf16_to_f32((uint16_t)(u.y & 0xffffu)), bf16_to_f32((uint16_t)(u.y >> 16))};
+        } else {
+            x = *reinterpret_cast<const f4 *>(raw + (3 + t) * NCH + lc);
+        }
+        return x;
     };
-    const int nchunks = (T + C - 1) / C;
-#pragma unroll 1
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int Lc = min(C, T - t0);  // valid tokens in this chunk
-        // the loop's memory ops: the previous chunk's readout stores, then this chunk's stage
-        // (both issued a chunk ago), so waiting for everything waits for nothing recent
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
-        lds_barrier();
-
-        // ================= gates: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
-        if (wave == 0) {
-            float g = 0.f, b = 0.f;
-            if (lane < Lc) {
-                g = negA * softplus_f(word_val(abw[lane]) + dtb);
-                b = word_val(abw[C + lane]);
-            }
-            float x = g;
+    if (lane < QKG) {
+        const int lc = 4 * lane;
+        const bool isq = lc < D;
+        float *M = isq ? Q : K;
+        const int mc = isq ? lc : lc - D;
+        f4 wqk[4];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            Gam[lane] = x;
-            gam[lane] = expf(x);
-            bet[lane] = b;
-            dec[lane] = expf(__shfl(x, 63) - x);
-        }
-
-        // ================= conv: q | k (wave w: tokens 16w .. 16w+15, lane: 4 channels), v block
-        auto xrow = [&](int t, int lc) -> f4 {  // 4 raw channels of chunk row t (t < 0: history)
-            f4 x;
-            if (t < 0) {
-                x = *reinterpret_cast<const f4 *>(hist + (3 + t) * NCH + lc);
-            } else if constexpr (ACT_BF16) {
-                const uint2 u = *reinterpret_cast<const uint2 *>(raw + t * NCH + lc);
-                x = f4{bf16_to_f32((uint16_t)(u.x & 0xffffu)), bf16_to_f32((uint16_t)(u.x >> 16)),
-                       bf16_to_f32((uint16_t)(u.y & 0xffffu)), bf16_to_f32((uint16_t)(u.y >> 16))};
-            } else {
-                x = *reinterpret_cast<const f4 *>(raw + t * NCH + lc);
-            }
-            return x;
-        };
-        f4 hq[3], hv;
-        if (lane < QKG) {
-            const int lc = 4 * lane;
-            const bool isq = lc < D;
-            float *M = isq ? Q : K;
-            const int mc = isq ? lc : lc - D;
-            f4 x0 = xrow(16 * wave - 3, lc), x1 = xrow(16 * wave - 2, lc), x2 = xrow(16 * wave - 1, lc);
+        for (int j = 0; j < 4; ++j) wqk[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + j) * 4);
+        f4 x0 = xrow(16 * wave - 3, lc), x1 = xrow(16 * wave - 2, lc), x2 = xrow(16 * wave - 1, lc);
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt) {
-                const int t = 16 * wave + tt;
-                const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
-                f4 y;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float v = conv4(wqk[j], x0[j], x1[j], x2[j], x3[j]);
-                    if constexpr (QKN) v = v * sigmoid_f(v);
-                    y[j] = t < Lc ? v : 0.f;
-                }
-                if constexpr (QKN) {  // unit length (+1e-6) over the head's 128 channels; q also / sqrt(d)
-                    float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
-                    ss = row16_sum(ss);
-                    if constexpr (D == 128) ss += __shfl_xor(ss, 16);
-                    const float sc = 1.0f / sqrtf(ss + 1e-6f) / (isq ? sqrtf((float)D) : 1.0f);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) y[j] *= sc;
-                }
-                *reinterpret_cast<f4 *>(M + swz<D>(t, mc)) = y;
-                x0 = x1;
-                x1 = x2;
-                x2 = x3;
-            }
-            hq[0] = x0;  // rows 61, 62, 63 for the last wave: the next chunk's history
-            hq[1] = x1;
-            hq[2] = x2;
-        }
-        {
-            const int t = tid >> 2, lc = 2 * D + 4 * (tid & 3);
-            const f4 x0 = xrow(t - 3, lc), x1 = xrow(t - 2, lc), x2 = xrow(t - 1, lc);
+        for (int tt = 0; tt < 16; ++tt) {
+            const int t = 16 * wave + tt;
             const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
             f4 y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float v = conv4(wv[j], x0[j], x1[j], x2[j], x3[j]);
+                float v = conv4(wqk[j], x0[j], x1[j], x2[j], x3[j]);
                 if constexpr (QKN) v = v * sigmoid_f(v);
                 y[j] = t < Lc ? v : 0.f;
             }
-            *reinterpret_cast<f4 *>(Vb + t * kDB + 4 * (tid & 3)) = y;
-            hv = x3;
-        }
-        lds_barrier();
-        // the raw rows and the history are consumed: the next chunk's history rows (this chunk's
-        // last three) are written, and the next chunk's stage travels while this one computes
-        if (Lc == C) {
-            if (wave == 3 && lane < QKG)
+            if constexpr (QKN) {  // unit length (+1e-6) over the head's 128 channels; q also / sqrt(d)
+                float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+                ss = row16_sum(ss);
+                if constexpr (D == 128) ss += __shfl_xor(ss, 16);
+                const float sc = 1.0f / sqrtf(ss + 1e-6f) / (isq ? sqrtf((float)D) : 1.0f);
 #pragma unroll
-                for (int r = 0; r < 3; ++r) *reinterpret_cast<f4 *>(hist + r * NCH + 4 * lane) = hq[r];
-            if ((tid >> 2) >= C - 3) *reinterpret_cast<f4 *>(hist + ((tid >> 2) - (C - 3)) * NCH + 2 * D + 4 * (tid & 3)) = hv;
-        }
-        // the previous chunk's readout, held in registers until now so that its stores go out
-        // before this chunk's stage loads, never behind them
-        if (c > 0) store_o(c - 1, o_prev);
-        if (c + 1 < nchunks) stage(c + 1);
-
-        // ================= A = strictly-lower(beta e^{G_t-G_s} K K^T), P = lower(e^{G_t-G_s} Q K^T),
-        //                   Y = beta V - beta gamma K S^T  (MFMA; A / P row tiles {0,3} and {1,2})
-        {
-            const float *Am = wave < 2 ? K : Q;
-            float *Dm = wave < 2 ? Tm : Pm;
-            const int pair = wave & 1;  // row tiles {0, 3} or {1, 2}: 5 tiles, listed so the loop unrolls
-#pragma unroll
-            for (int jt = 0; jt < 5; ++jt) {
-                // pair 0: (0,0) (3,0) (3,1) (3,2) (3,3);  pair 1: (1,0) (1,1) (2,0) (2,1) (2,2)
-                const int rt = pair == 0 ? (jt == 0 ? 0 : 3) : (jt < 2 ? 1 : 2);
-                const int ct = pair == 0 ? (jt == 0 ? 0 : jt - 1) : (jt < 2 ? jt : jt - 2);
-                {
-                    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < D; kk += 32) {
-                        float av[8], bv[8];
-                        load8(Am + swz<D>(16 * rt + (lane & 15), kk + (lane >> 4) * 8), av);
-                        load8(K + swz<D>(16 * ct + (lane & 15), kk + (lane >> 4) * 8), bv);
-                        acc = mma8<F32>(av, bv, acc);
-                    }
-                    const int s_ = 16 * ct + (lane & 15);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = 16 * rt + (lane >> 4) * 4 + r;
-                        const float ratio = expf(Gam[t] - Gam[s_]);
-                        Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * acc[r] : 0.f)
-                                                    : (s_ <= t ? ratio * acc[r] : 0.f);
-                    }
-                }
+                for (int j = 0; j < 4; ++j) y[j] *= sc;
             }
+            *reinterpret_cast<f4 *>(M + swz<D>(t, mc)) = y;
+            x0 = x1;
+            x1 = x2;
+            x2 = x3;
+        }
+    }
+    {
+        const int t = tid >> 2, e4 = 4 * (tid & 3);
+        float *vdst = a.ws + w.v + (((size_t)c * a.n_vh + h) * NB) * C * kDB + t * kDB + e4;
+#pragma unroll 1
+        for (int j = 0; j < NB; ++j) {
+            const int lc = 2 * D + kDB * j + e4;
+            f4 wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + e) * 4);
+            const f4 x0 = xrow(t - 3, lc), x1 = xrow(t - 2, lc), x2 = xrow(t - 1, lc);
+            const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
+            f4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = conv4(wv[e], x0[e], x1[e], x2[e], x3[e]);
+                if constexpr (QKN) v = v * sigmoid_f(v);
+                y[e] = t < Lc ? v : 0.f;
+            }
+            *reinterpret_cast<f4 *>(vdst + (size_t)j * C * kDB) = y;
+        }
+    }
+    lds_barrier();  // q, k and the gates are in LDS; the raw rows are consumed
+    // the upper blocks of A / T and P are zero
+    for (int i = tid; i < C * kCP; i += kPThreads) {
+        Tm[i] = 0.f;
+        Pm[i] = 0.f;
+    }
+    lds_barrier();
+
+    // ---- A = strictly-lower(beta e^{G_t-G_s} K K^T), P = lower(e^{G_t-G_s} Q K^T) (MFMA; waves
+    // 0, 1 build A, waves 2, 3 build P, row tiles {0,3} or {1,2}: 5 tiles per wave)
+    {
+        const float *Am = wave < 2 ? K : Q;
+        float *Dm = wave < 2 ? Tm : Pm;
+        const int pair = wave & 1;
+#pragma unroll
+        for (int jt = 0; jt < 5; ++jt) {
+            // pair 0: (0,0) (3,0) (3,1) (3,2) (3,3);  pair 1: (1,0) (1,1) (2,0) (2,1) (2,2)
+            const int rt = pair == 0 ? (jt == 0 ? 0 : 3) : (jt < 2 ? 1 : 2);
+            const int ct = pair == 0 ? (jt == 0 ? 0 : jt - 1) : (jt < 2 ? jt : jt - 2);
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D; kk += 32) {
+                float av[8], bv[8];
+                load8(Am + swz<D>(16 * rt + (lane & 15), kk + (lane >> 4) * 8), av);
+                load8(K + swz<D>(16 * ct + (lane & 15), kk + (lane >> 4) * 8), bv);
+                acc = mma8<F32>(av, bv, acc);
+            }
+            const int s_ = 16 * ct + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * rt + (lane >> 4) * 4 + r;
+                const float ratio = expf(Gam[t] - Gam[s_]);
+                Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * acc[r] : 0.f) : (s_ <= t ? ratio * acc[r] : 0.f);
+            }
+        }
+    }
+    lds_barrier();
+    // ---- T = (I + A)^-1: 16x16 diagonal blocks by forward substitution (wave w, lane c < 16
+    // solves column c of block w), then the blocks below them
+    if (lane < 16) {
+        const int wv = wave, cc = lane;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+            for (int s_ = 0; s_ < r; ++s_) acc -= Tm[(16 * wv + r) * kCP + 16 * wv + s_] * x[s_];
+            x[r] = (r < cc) ? 0.f : acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Tm[(16 * wv + r) * kCP + 16 * wv + cc] = x[r];
+    }
+    lds_barrier();
+    // T_10 = -T_11 A_10 T_00 (wave 0) and T_32 = -T_33 A_32 T_22 (wave 1), the product A T
+    // parked in the scratch; T_ij = -T_ii (sum_k A_ik T_kj) for the 32 x 32 block below
+    float *scr_all = reinterpret_cast<float *>(smem + L::scr);
+    float *scr = scr_all + wave * 256;  // [16][16] per wave
+    auto park = [&](f4 v) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scr[((lane >> 4) * 4 + r) * 16 + (lane & 15)] = v[r];
+    };
+    auto blk16s = [&](const float *X, int xr0, int xc0, const float *Y, f4 acc) {  // acc += X(block) Y
+#pragma unroll
+        for (int st2 = 0; st2 < 4; ++st2) {
+            const int kk = 4 * st2 + (lane >> 4);
+            acc = mfma4f32(X[(xr0 + (lane & 15)) * kCP + xc0 + kk], Y[kk * 16 + (lane & 15)], acc);
+        }
+        return acc;
+    };
+    auto put_neg = [&](int r0, int c0, f4 v) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tm[(r0 + (lane >> 4) * 4 + r) * kCP + c0 + (lane & 15)] = -v[r];
+    };
+    if (wave < 2) {
+        const int i = wave == 0 ? 1 : 3, j = i - 1;
+        park(blk16(Tm, 16 * i, 16 * j, Tm, 16 * j, 16 * j, f4{0.f, 0.f, 0.f, 0.f}, lane));
+        put_neg(16 * i, 16 * j, blk16s(Tm, 16 * i, 16 * i, scr, f4{0.f, 0.f, 0.f, 0.f}));
+    }
+    lds_barrier();
+    const int r3 = 2 + (wave >> 1), c3 = wave & 1;  // block (r3, c3) of the lower-left 32 x 32
+    {  // X_rc = A_r0 T_0c + A_r1 T_1c
+        f4 x = blk16(Tm, 16 * r3, 16, Tm, 16, 16 * c3, f4{0.f, 0.f, 0.f, 0.f}, lane);
+        if (c3 == 0) x = blk16(Tm, 16 * r3, 0, Tm, 0, 0, x, lane);
+        park(x);
+    }
+    lds_barrier();
+    {  // T_2c = -T_22 X_2c ;  T_3c = -(T_32 X_2c + T_33 X_3c)  (X_2c parked by wave c, X_3c by wave 2 + c)
+        f4 acc = blk16s(Tm, 16 * r3, 32, scr_all + c3 * 256, f4{0.f, 0.f, 0.f, 0.f});
+        if (r3 == 3) acc = blk16s(Tm, 48, 48, scr, acc);
+        put_neg(16 * r3, 16 * c3, acc);
+    }
+    lds_barrier();
+
+    // ---- the scan's operands, as the LDS images it copies
+    {
+        const size_t ch = (size_t)c * a.n_vh + h;
+        f4 *tdst = reinterpret_cast<f4 *>(a.ws + w.t + ch * C * kCP);
+        f4 *pdst = reinterpret_cast<f4 *>(a.ws + w.p + ch * C * kCP);
+        for (int i = tid; i < C * kCP / 4; i += kPThreads) {
+            tdst[i] = reinterpret_cast<const f4 *>(Tm)[i];
+            pdst[i] = reinterpret_cast<const f4 *>(Pm)[i];
+        }
+        if (h % R == 0) {  // q and k belong to the key head: its first value head writes them
+            f4 *qdst = reinterpret_cast<f4 *>(a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D);
+            f4 *kdst = qdst + C * D / 4;
+            for (int i = tid; i < C * D / 4; i += kPThreads) {
+                qdst[i] = reinterpret_cast<const f4 *>(Q)[i];
+                kdst[i] = reinterpret_cast<const f4 *>(K)[i];
+            }
+        }
+        if (tid < C) {
+            float *g = a.ws + w.g + ch * kGateRec;
+            g[tid] = gam[tid];
+            g[C + tid] = bet[tid];
+            g[2 * C + tid] = dec[tid];
+            g[3 * C + tid] = 0.f;
+        }
+    }
+}
+
+// ============================== kernel 2: the chunk chain ==============================
+// Per chunk, for this workgroup's 16 value rows (S block 16 x d):
+//   A: Y^T = beta V^T - (S K^T) diag(beta gamma)        (wave w: tokens 16w .. 16w+15)
+//   B: U^T = Y^T T^T
+//   C: O   = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K
+// The next chunk's operands arrive by global_load_lds while this one computes.  Loads and stores
+// share gfx950's one vector-memory counter and a store may complete before an older load, so a
+// partial wait is only sound when no store was issued after the loads it waits for.  Order within
+// chunk c:
+//   wait: everything but q, P of chunk c  |  A  |  B  |  wait: everything
+//   stores of chunk c-1's readout, then issue T, k, v, gates of chunk c+1  |  C  |  issue q, P of c+1
+// so the one slot for stores follows a full wait, the k / v / gates / T transfers travel during C,
+// and q / P during A and B of the next chunk.  k, v and gates are double-buffered (the next chunk's
+// arrive while C still reads this chunk's).
+template <int D>
+struct ScanCounts {
+    static constexpr int per_wave(int n16) { return n16 / kPThreads; }  // the minimum over the waves
+    static constexpr int q = per_wave(kChunk * D / 4);
+    static constexpr int p = per_wave(kChunk * kCP / 4);
+    static constexpr int top = q + p;  // at the top of a chunk only its q and P may be in flight
+    static_assert(top < 64, "vmcnt holds at most 63");
+};
+// s_waitcnt immediate: wait until at most n vector-memory operations are outstanding (gfx9
+// encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+
+template <int D, bool F32>
+__global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
+{
+    using L = ScanLds<D>;
+    using N = ScanCounts<D>;
+    constexpr int C = kChunk;
+    constexpr int NB = D / kDB;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int R = a.n_vh / a.n_kh;
+    // workgroups are dealt to the 8 XCDs in turn: keep the row blocks of a key head's value heads on
+    // one XCD, so the operand images they all read are fetched into that XCD's L2 once
+    const int nwg = a.n_vh * NB;
+    const int idx = nwg % 8 == 0 ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int h = idx / NB, blk = idx % NB;
+    const int hk = h / R;
+    const int T = a.T;
+    const int nchunks = (T + C - 1) / C;
+    const PrefillWs w = prefill_ws(D, a.n_kh, a.n_vh, T);
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float *Kb = reinterpret_cast<float *>(smem + L::kb);
+    float *Vb = reinterpret_cast<float *>(smem + L::vb);
+    float *Gb = reinterpret_cast<float *>(smem + L::gb);
+    float *Q = reinterpret_cast<float *>(smem + L::q);
+    float *Tm = reinterpret_cast<float *>(smem + L::tm);
+    float *Pm = reinterpret_cast<float *>(smem + L::pm);
+    float *S = reinterpret_cast<float *>(smem + L::s);
+    float *Yt = reinterpret_cast<float *>(smem + L::yt);
+    float *Ut = reinterpret_cast<float *>(smem + L::ut);
+
+    auto qk_img = [&](int cc, int which) { return a.ws + w.qk + (((size_t)cc * a.n_kh + hk) * 2 + which) * C * D; };
+    auto issue_kvg = [&](int cc) {
+        const int b = cc & 1;
+        const size_t ch = (size_t)cc * a.n_vh + h;
+        dma_image(qk_img(cc, 1), Kb + b * C * D, C * D / 4, tid);
+        dma_image(a.ws + w.v + (ch * NB + blk) * C * kDB, Vb + b * C * kDB, C * kDB / 4, tid);
+        dma_image(a.ws + w.g + ch * kGateRec, Gb + b * kGateRec, kGateRec / 4, tid);
+    };
+    auto issue_t = [&](int cc) { dma_image(a.ws + w.t + ((size_t)cc * a.n_vh + h) * C * kCP, Tm, C * kCP / 4, tid); };
+    auto issue_qp = [&](int cc) {
+        dma_image(qk_img(cc, 0), Q, C * D / 4, tid);
+        dma_image(a.ws + w.p + ((size_t)cc * a.n_vh + h) * C * kCP, Pm, C * kCP / 4, tid);
+    };
+
+    // ---- prologue: the state block, then chunk 0's operands
+    float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
+    for (int i = tid; i < kDB * D / 4; i += kPThreads) {
+        const int r = (4 * i) / D, cl = (4 * i) % D;
+        *reinterpret_cast<f4 *>(S + swz<D>(r, cl)) = reinterpret_cast<const f4 *>(st)[i];
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): the state block is loaded
+    issue_kvg(0);
+    issue_t(0);
+    issue_qp(0);
+
+    f4 o_prev = {0.f, 0.f, 0.f, 0.f};
+    auto store_o = [&](int cc) {  // rows t = 16 w + 4 (lane / 16) + r of chunk cc; whole chunks fit
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = cc * C + 16 * wave + (lane >> 4) * 4 + r;
+            a.ws[w.o + ((size_t)t * a.n_vh + h) * D + blk * kDB + (lane & 15)] = o_prev[r];
+        }
+    };
+#pragma unroll 1
+    for (int c = 0; c < nchunks; ++c) {
+        const int b = c & 1;
+        const float *K = Kb + b * C * D;
+        const float *Vc = Vb + b * C * kDB;
+        const float *gam = Gb + b * kGateRec;
+        const float *bet = gam + C;
+        const float *dec = bet + C;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(N::top));  // k, v, gates, T of chunk c (q, P may travel)
+        lds_barrier();
+
+        // ---- A: Y^T[i][t] = beta_t (V[t][i] - gamma_t (K S^T)[t][i])
+        {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D; kk += 32) {
@@ -402,108 +603,58 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * wave + (lane >> 4) * 4 + r;
-                Yt[i * kCP + t] = bet[t] * (Vb[t * kDB + i] - gam[t] * acc[r]);
+                Yt[i * kCP + t] = bet[t] * (Vc[t * kDB + i] - gam[t] * acc[r]);
             }
         }
         lds_barrier();
-        // ================= T = (I + A)^-1: 16x16 diagonal blocks by forward substitution (wave w,
-        //                   lane c < 16 solves column c of block w), then the blocks below them
-        if (lane < 16) {
-            const int w = wave, cc = lane;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-                for (int s_ = 0; s_ < r; ++s_) acc -= Tm[(16 * w + r) * kCP + 16 * w + s_] * x[s_];
-                x[r] = (r < cc) ? 0.f : acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Tm[(16 * w + r) * kCP + 16 * w + cc] = x[r];
-        }
-        lds_barrier();
-        // T_10 = -T_11 A_10 T_00 (wave 0) and T_32 = -T_33 A_32 T_22 (wave 1), the product A T
-        // parked in the U area; T_ij = -T_ii (sum_k A_ik T_kj) for the 32 x 32 block below
-        float *scr = Ut + wave * 256;  // [16][16] per wave
-        auto park = [&](f4 v) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) scr[((lane >> 4) * 4 + r) * 16 + (lane & 15)] = v[r];
-        };
-        auto blk16s = [&](const float *X, int xr0, int xc0, const float *Y, f4 acc) {  // acc += X(block) Y
-#pragma unroll
-            for (int st2 = 0; st2 < 4; ++st2) {
-                const int kk = 4 * st2 + (lane >> 4);
-                acc = mfma4f32(X[(xr0 + (lane & 15)) * kCP + xc0 + kk], Y[kk * 16 + (lane & 15)], acc);
-            }
-            return acc;
-        };
-        auto put_neg = [&](int r0, int c0, f4 v) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Tm[(r0 + (lane >> 4) * 4 + r) * kCP + c0 + (lane & 15)] = -v[r];
-        };
-        if (wave < 2) {
-            const int i = wave == 0 ? 1 : 3, j = i - 1;
-            park(blk16(Tm, 16 * i, 16 * j, Tm, 16 * j, 16 * j, f4{0.f, 0.f, 0.f, 0.f}, lane));
-            put_neg(16 * i, 16 * j, blk16s(Tm, 16 * i, 16 * i, scr, f4{0.f, 0.f, 0.f, 0.f}));
-        }
-        lds_barrier();
-        const int r3 = 2 + (wave >> 1), c3 = wave & 1;  // block (r3, c3) of the lower-left 32 x 32
-        {  // X_rc = A_r0 T_0c + A_r1 T_1c
-            f4 x = blk16(Tm, 16 * r3, 16, Tm, 16, 16 * c3, f4{0.f, 0.f, 0.f, 0.f}, lane);
-            if (c3 == 0) x = blk16(Tm, 16 * r3, 0, Tm, 0, 0, x, lane);
-            park(x);
-        }
-        lds_barrier();
-        {  // T_2c = -T_22 X_2c ;  T_3c = -(T_32 X_2c + T_33 X_3c)  (X_2c parked by wave c, X_3c by wave 2 + c)
-            f4 acc = blk16s(Tm, 16 * r3, 32, Ut + c3 * 256, f4{0.f, 0.f, 0.f, 0.f});
-            if (r3 == 3) acc = blk16s(Tm, 48, 48, scr, acc);
-            put_neg(16 * r3, 16 * c3, acc);
-        }
-        lds_barrier();
-        // ================= U = T Y (MFMA) =================
+        // ---- B: U = T Y
         {
-            const int w = wave;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < C; kk += 32) {
                 float av[8], bv[8];
-                load8(Tm + (16 * w + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
+                load8(Tm + (16 * wave + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
                 load8(Yt + (lane & 15) * kCP + kk + (lane >> 4) * 8, bv);
                 acc = mma8<F32>(av, bv, acc);
             }
             const int i = lane & 15;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Ut[i * kCP + 16 * w + (lane >> 4) * 4 + r] = acc[r];
+            for (int r = 0; r < 4; ++r) Ut[i * kCP + 16 * wave + (lane >> 4) * 4 + r] = acc[r];
         }
-        lds_barrier();
-        // ================= O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K ==========
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): q and P of chunk c
+        lds_barrier();                      // also: every wave is done with T
+        if (c > 0) store_o(c - 1);
+        if (c + 1 < nchunks) {
+            issue_t(c + 1);
+            issue_kvg(c + 1);  // the buffer chunk c-1 used
+        }
+        // ---- C: O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K
         constexpr int SCT = D / 16 / 4;  // S' column tiles per wave
-        f4 snew[SCT > 0 ? SCT : 1];
+        f4 snew[SCT];
         {
-            const int w = wave;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D; kk += 32) {
                 float av[8], bv[8];
-                load8(Q + swz<D>(16 * w + (lane & 15), kk + (lane >> 4) * 8), av);
+                load8(Q + swz<D>(16 * wave + (lane & 15), kk + (lane >> 4) * 8), av);
                 load8(S + swz<D>(lane & 15, kk + (lane >> 4) * 8), bv);
                 acc = mma8<F32>(av, bv, acc);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= gam[16 * w + (lane >> 4) * 4 + r];
+            for (int r = 0; r < 4; ++r) acc[r] *= gam[16 * wave + (lane >> 4) * 4 + r];
 #pragma unroll
             for (int kk = 0; kk < C; kk += 32) {
                 float av[8], bv[8];
-                load8(Pm + (16 * w + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
+                load8(Pm + (16 * wave + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
                 load8(Ut + (lane & 15) * kCP + kk + (lane >> 4) * 8, bv);
                 acc = mma8<F32>(av, bv, acc);
             }
-            o_prev = acc;  // stored during the next chunk (or after the loop)
+            o_prev = acc;
             // S' block: rows i = 4 (lane / 16) + r, columns j = 16 ct + lane % 16
             const float gC = gam[C - 1];
 #pragma unroll
             for (int q2 = 0; q2 < SCT; ++q2) {
-                const int ct = SCT * w + q2;
+                const int ct = SCT * wave + q2;
                 f4 sa;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sa[r] = gC * S[swz<D>((lane >> 4) * 4 + r, 16 * ct + (lane & 15))];
@@ -528,14 +679,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_chunk_kernel(PrefillArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[swz<D>((lane >> 4) * 4 + r, 16 * ct + (lane & 15))] = snew[q2][r];
         }
+        if (c + 1 < nchunks) issue_qp(c + 1);
     }
-    if (nchunks > 0) store_o(nchunks - 1, o_prev);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): every transfer into LDS has landed
+    if (nchunks > 0) store_o(nchunks - 1);
     __syncthreads();
     // ---- the state block after the last token
-    float *sd = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
     for (int i = tid; i < kDB * D / 4; i += kPThreads) {
-        const int r = (4 * i) / D, c = (4 * i) % D;
-        reinterpret_cast<f4 *>(sd)[i] = *reinterpret_cast<const f4 *>(S + swz<D>(r, c));
+        const int r = (4 * i) / D, cl = (4 * i) % D;
+        reinterpret_cast<f4 *>(st)[i] = *reinterpret_cast<const f4 *>(S + swz<D>(r, cl));
     }
 }
 
@@ -549,7 +701,7 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillArgs a)
     const int cg = threadIdx.x & 15;
     const int nrows = a.T * a.n_vh;
     if (row < nrows) {
-        const float *o = a.o_ws + (size_t)row * D + cg * EPL;
+        const float *o = a.ws + (size_t)row * D + cg * EPL;  // the readout sits at the start of the workspace
         float ov[EPL], ss = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -586,19 +738,29 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillArgs a)
     }
 }
 
-size_t prefill_workspace_bytes(int d, int n_vh, int T) { return sizeof(float) * (size_t)T * n_vh * d; }
+size_t prefill_workspace_bytes(int d, int n_kh, int n_vh, int T)
+{
+    return sizeof(float) * prefill_ws(d, n_kh, n_vh, T).total;
+}
 
 size_t prefill_lds_bytes(int d, bool act_bf16)
 {
-    if (d == 128) return act_bf16 ? PrefillLds<128, uint16_t>::total : PrefillLds<128, float>::total;
-    return act_bf16 ? PrefillLds<64, uint16_t>::total : PrefillLds<64, float>::total;
+    const size_t prep = d == 128 ? (act_bf16 ? PrepLds<128, uint16_t>::total : PrepLds<128, float>::total)
+                                 : (act_bf16 ? PrepLds<64, uint16_t>::total : PrepLds<64, float>::total);
+    const size_t scan = d == 128 ? ScanLds<128>::total : ScanLds<64>::total;
+    return prep > scan ? prep : scan;
 }
 
 template <int D, bool AB, bool OB, bool QKN>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
-    const size_t lds = prefill_lds_bytes(D, AB);
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, AB, QKN>), dim3(a.n_vh * (D / kDB)), dim3(kPThreads), lds, stream, a);
+    using act_t = typename std::conditional<AB, uint16_t, float>::type;
+    const int nchunks = (a.T + kChunk - 1) / kChunk;
+    const size_t prep_lds = PrepLds<D, act_t>::total;
+    hipLaunchKernelGGL((prefill_prep_kernel<D, AB, QKN>), dim3(nchunks * a.n_vh), dim3(kPThreads), prep_lds, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL((prefill_scan_kernel<D, !AB>), dim3(a.n_vh * (D / kDB)), dim3(kPThreads), ScanLds<D>::total,
+                       stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     const long rows = (long)a.T * a.n_vh;
     const long conv_rows = (a.C + 15) / 16;  // 16 threads per row-group also cover the conv state

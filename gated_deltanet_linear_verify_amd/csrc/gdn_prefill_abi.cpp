@@ -17,7 +17,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 GDN_API size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t n_tok)
 {
     if (gdn::abi_check_dims(dims) || n_tok < 1) return 0;
-    return gdn::prefill_workspace_bytes(dims->d_v, dims->n_vh, n_tok);
+    return gdn::prefill_workspace_bytes(dims->d_v, dims->n_kh, dims->n_vh, n_tok);
 }
 
 GDN_API int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, const void *qkv, const void *z,
@@ -34,7 +34,7 @@ GDN_API int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, c
         return gdn::abi_fail(GDN_ERR_ARG, "gdn_prefill: state, conv_state, conv_w, qkv and workspace must be 16-byte aligned");
     if (n_tok < 1) return gdn::abi_fail(GDN_ERR_RANGE, "gdn_prefill: n_tok must be >= 1");
     if (slot < 0 || slot >= d.n_pool) return gdn::abi_fail(GDN_ERR_RANGE, "gdn_prefill: slot outside [0, n_pool)");
-    if (ws_bytes < gdn::prefill_workspace_bytes(d.d_v, d.n_vh, n_tok))
+    if (ws_bytes < gdn::prefill_workspace_bytes(d.d_v, d.n_kh, d.n_vh, n_tok))
         return gdn::abi_fail(GDN_ERR_ARG, "gdn_prefill: workspace smaller than gdn_prefill_workspace_bytes()");
     if (d.act_dtype == GDN_BF16 && (d.n_vh & 1))
         return gdn::abi_fail(GDN_ERR_SHAPE, "gdn_prefill: bf16 activations need an even number of value heads");
@@ -59,7 +59,7 @@ GDN_API int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, c
     a.conv_w = conv_w;
     a.norm_w = norm_w;
     a.out = out;
-    a.o_ws = static_cast<float *>(workspace);
+    a.ws = static_cast<float *>(workspace);
     gdn::LaunchCfg c{d.act_dtype == GDN_BF16, d.out_dtype == GDN_BF16, (d.flags & GDN_F_QK_NORM_SILU) != 0};
     if (hipError_t e = gdn::launch_prefill(a, c, static_cast<hipStream_t>(stream)))
         return gdn::abi_fail(GDN_ERR_HIP, "gdn_prefill launch: %s", hipGetErrorString(e));
