@@ -135,11 +135,100 @@ __device__ __forceinline__ f4 blk16(const float *X, int xr0, int xc0, const floa
 }
 
 
+// ---- MFMA operand matrices shared by the prep (as images it writes) and the scan (in LDS) ----
+// One lane's 8 consecutive k values of an MFMA operand: fp32 values for the fp32 MFMA, or the bf16
+// hi and lo parts of the fp32 values for the bf16 MFMA.
+template <bool F32>
+struct Frag;
+template <>
+struct Frag<true> {
+    float v[8];
+};
+template <>
+struct Frag<false> {
+    bf16x8 hi, lo;
+};
+
+template <bool F32>
+__device__ __forceinline__ f4 mma(const Frag<F32> &a, const Frag<F32> &b, f4 acc)
+{
+    if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = mfma4f32(a.v[e], b.v[e], acc);
+    } else {  // the same three products, in the same order, as mma8
+        acc = mfma16(a.lo, b.hi, acc);
+        acc = mfma16(a.hi, b.lo, acc);
+        acc = mfma16(a.hi, b.hi, acc);
+    }
+    return acc;
+}
+
+// A [ROWS][COLS] fp32 matrix kept ready for MFMA operand loads: fp32 (F32), or already split into a
+// bf16 hi plane followed by a bf16 lo plane (both the size of the fp32 matrix together).  Groups
+// of 8 consecutive columns are XOR-swizzled by the row, so the 16 rows one operand load touches
+// spread over the LDS banks.  The same layout serves as the prep's workspace image and the scan's
+// LDS copy, so moving it is a flat copy.
+template <bool F32, int ROWS, int COLS>
+struct Mat {
+    static constexpr int NG = COLS / 8;
+    static constexpr int floats = ROWS * COLS;  // size in floats either way
+    __device__ static int idx(int r, int c) { return r * COLS + ((((c >> 3) ^ r) & (NG - 1)) << 3) + (c & 7); }
+    // operand fragment: row r, columns c0 .. c0 + 7 (c0 a multiple of 8)
+    __device__ static Frag<F32> load(const float *m, int r, int c0)
+    {
+        Frag<F32> f;
+        if constexpr (F32) {
+            load8(m + idx(r, c0), f.v);
+        } else {
+            const __bf16 *hp = reinterpret_cast<const __bf16 *>(m);
+            f.hi = *reinterpret_cast<const bf16x8 *>(hp + idx(r, c0));
+            f.lo = *reinterpret_cast<const bf16x8 *>(hp + ROWS * COLS + idx(r, c0));
+        }
+        return f;
+    }
+    // element (r, c) into fragment slot e (gathers down a column)
+    __device__ static void get(const float *m, int r, int c, Frag<F32> &f, int e)
+    {
+        if constexpr (F32) {
+            f.v[e] = m[idx(r, c)];
+        } else {
+            const __bf16 *hp = reinterpret_cast<const __bf16 *>(m);
+            f.hi[e] = hp[idx(r, c)];
+            f.lo[e] = hp[ROWS * COLS + idx(r, c)];
+        }
+    }
+    __device__ static void put(float *m, int r, int c, float x)
+    {
+        if constexpr (F32) {
+            m[idx(r, c)] = x;
+        } else {
+            __bf16 *hp = reinterpret_cast<__bf16 *>(m);
+            const __bf16 h = (__bf16)x;
+            hp[idx(r, c)] = h;
+            hp[ROWS * COLS + idx(r, c)] = (__bf16)(x - (float)h);
+        }
+    }
+    __device__ static void put8(float *m, int r, int c0, const float (&x)[8])
+    {
+        if constexpr (F32) {
+            *reinterpret_cast<f4 *>(m + idx(r, c0)) = f4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f4 *>(m + idx(r, c0) + 4) = f4{x[4], x[5], x[6], x[7]};
+        } else {
+            bf16x8 hi, lo;
+            split8(x, hi, lo);
+            __bf16 *hp = reinterpret_cast<__bf16 *>(m);
+            *reinterpret_cast<bf16x8 *>(hp + idx(r, c0)) = hi;
+            *reinterpret_cast<bf16x8 *>(hp + ROWS * COLS + idx(r, c0)) = lo;
+        }
+    }
+};
+
 // Workspace (floats), nc = number of chunks:
 //   o  [nc * 64][H_v][d]         fp32 readout before the norm (whole chunks: the tail is scratch)
-//   qk [nc][H_k][2][64 * d]      conv'd q then k of the chunk, swizzled (swz<d>), per key head
-//   t  [nc][H_v][64 * kCP]       T = (I + A)^-1, padded rows
-//   p  [nc][H_v][64 * kCP]       P, padded rows
+//   qk [nc][H_k][2][64 * d]      conv'd q then k of the chunk, per key head
+// (q, k, T and P as Mat images: fp32, or split into bf16 hi / lo planes for bf16 activations)
+//   t  [nc][H_v][64 * 64]        T = (I + A)^-1
+//   p  [nc][H_v][64 * 64]        P
 //   v  [nc][H_v][d / 16][64][16] conv'd v, one block of 16 value rows per scan workgroup
 //   g  [nc][H_v][256]            gamma | beta | exp(Gamma_C - Gamma) | 0, 64 each
 constexpr int kGateRec = 4 * kChunk;
@@ -153,8 +242,8 @@ __host__ __device__ inline PrefillWs prefill_ws(int d, int n_kh, int n_vh, int T
     w.o = 0;
     w.qk = w.o + nc * kChunk * n_vh * d;
     w.t = w.qk + nc * n_kh * 2 * kChunk * d;
-    w.p = w.t + nc * n_vh * kChunk * kCP;
-    w.v = w.p + nc * n_vh * kChunk * kCP;
+    w.p = w.t + nc * n_vh * kChunk * kChunk;
+    w.v = w.p + nc * n_vh * kChunk * kChunk;
     w.g = w.v + nc * n_vh * kChunk * d;
     w.total = w.g + nc * n_vh * kGateRec;
     return w;
@@ -192,19 +281,20 @@ template <int D>
 struct ScanLds {
     static constexpr int C = kChunk;
     static constexpr size_t kimg = sizeof(float) * C * D;    // a q or k image
-    static constexpr size_t timg = sizeof(float) * C * kCP;  // a T or P image
+    static constexpr size_t timg = sizeof(float) * C * C;    // a T or P image
     static constexpr size_t vimg = sizeof(float) * C * kDB;  // a v block image
     static constexpr size_t gimg = sizeof(float) * kGateRec;
     static constexpr size_t kb = 0;                          // [2] k images (this chunk, next chunk)
     static constexpr size_t vb = kb + 2 * kimg;              // [2] v block images
     static constexpr size_t gb = vb + 2 * vimg;              // [2] gate records
     static constexpr size_t q = gb + 2 * gimg;               // q image
-    static constexpr size_t tm = q + kimg;                   // T
-    static constexpr size_t pm = tm + timg;                  // P
-    static constexpr size_t s = pm + timg;                   // [DB][D] the state block, swizzled
-    static constexpr size_t yt = s + sizeof(float) * kDB * D;   // [DB][kCP] Y^T
-    static constexpr size_t ut = yt + sizeof(float) * kDB * kCP;  // [DB][kCP] U^T
-    static constexpr size_t total = ut + sizeof(float) * kDB * kCP;
+    static constexpr size_t tm = q + kimg;                   // T image
+    static constexpr size_t pm = tm + timg;                  // P image
+    static constexpr size_t sp = pm + timg;                  // S block [DB][D]      (operand form)
+    static constexpr size_t yp = sp + sizeof(float) * kDB * D;  // Y^T [DB][C]        (operand form)
+    static constexpr size_t up = yp + sizeof(float) * kDB * C;  // U^T [DB][C]        (operand form)
+    static constexpr size_t dp = up + sizeof(float) * kDB * C;  // U^T diag(dec) [DB][C]
+    static constexpr size_t total = dp + sizeof(float) * kDB * C;
 };
 static_assert(ScanLds<128>::total <= 160 * 1024, "d=128 scan must fit one CU's LDS");
 
@@ -462,21 +552,31 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
     }
     lds_barrier();
 
-    // ---- the scan's operands, as the LDS images it copies
+    // ---- the scan's operands, as the Mat images it copies
     {
+        using MQ = Mat<F32, C, D>;
+        using MT = Mat<F32, C, C>;
         const size_t ch = (size_t)c * a.n_vh + h;
-        f4 *tdst = reinterpret_cast<f4 *>(a.ws + w.t + ch * C * kCP);
-        f4 *pdst = reinterpret_cast<f4 *>(a.ws + w.p + ch * C * kCP);
-        for (int i = tid; i < C * kCP / 4; i += kPThreads) {
-            tdst[i] = reinterpret_cast<const f4 *>(Tm)[i];
-            pdst[i] = reinterpret_cast<const f4 *>(Pm)[i];
+        float *tdst = a.ws + w.t + ch * C * C;
+        float *pdst = a.ws + w.p + ch * C * C;
+        for (int g = tid; g < C * C / 8; g += kPThreads) {
+            const int r = g / (C / 8), c0 = (g % (C / 8)) * 8;
+            float x[8];
+            load8(Tm + r * kCP + c0, x);
+            MT::put8(tdst, r, c0, x);
+            load8(Pm + r * kCP + c0, x);
+            MT::put8(pdst, r, c0, x);
         }
         if (h % R == 0) {  // q and k belong to the key head: its first value head writes them
-            f4 *qdst = reinterpret_cast<f4 *>(a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D);
-            f4 *kdst = qdst + C * D / 4;
-            for (int i = tid; i < C * D / 4; i += kPThreads) {
-                qdst[i] = reinterpret_cast<const f4 *>(Q)[i];
-                kdst[i] = reinterpret_cast<const f4 *>(K)[i];
+            float *qdst = a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D;
+            float *kdst = qdst + C * D;
+            for (int g = tid; g < C * D / 8; g += kPThreads) {
+                const int r = g / (D / 8), c0 = (g % (D / 8)) * 8;
+                float x[8];
+                load8(Q + swz<D>(r, c0), x);
+                MQ::put8(qdst, r, c0, x);
+                load8(K + swz<D>(r, c0), x);
+                MQ::put8(kdst, r, c0, x);
             }
         }
         if (tid < C) {
@@ -507,7 +607,7 @@ template <int D>
 struct ScanCounts {
     static constexpr int per_wave(int n16) { return n16 / kPThreads; }  // the minimum over the waves
     static constexpr int q = per_wave(kChunk * D / 4);
-    static constexpr int p = per_wave(kChunk * kCP / 4);
+    static constexpr int p = per_wave(kChunk * kChunk / 4);
     static constexpr int top = q + p;  // at the top of a chunk only its q and P may be in flight
     static_assert(top < 64, "vmcnt holds at most 63");
 };
@@ -522,6 +622,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
     using N = ScanCounts<D>;
     constexpr int C = kChunk;
     constexpr int NB = D / kDB;
+    using MK = Mat<F32, C, D>;    // q and k images
+    using MT = Mat<F32, C, C>;    // T and P images
+    using MS = Mat<F32, kDB, D>;  // the S block
+    using MU = Mat<F32, kDB, C>;  // Y^T, U^T, U^T diag(dec)
+    constexpr int SCT = D / 16 / 4;  // S column tiles per wave
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int R = a.n_vh / a.n_kh;
     // workgroups are dealt to the 8 XCDs in turn: keep the row blocks of a key head's value heads on
@@ -533,6 +638,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
     const int T = a.T;
     const int nchunks = (T + C - 1) / C;
     const PrefillWs w = prefill_ws(D, a.n_kh, a.n_vh, T);
+    const int li = lane & 15, lg = lane >> 4;  // fragment row / column, 8-wide k group
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *Kb = reinterpret_cast<float *>(smem + L::kb);
@@ -541,9 +647,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
     float *Q = reinterpret_cast<float *>(smem + L::q);
     float *Tm = reinterpret_cast<float *>(smem + L::tm);
     float *Pm = reinterpret_cast<float *>(smem + L::pm);
-    float *S = reinterpret_cast<float *>(smem + L::s);
-    float *Yt = reinterpret_cast<float *>(smem + L::yt);
-    float *Ut = reinterpret_cast<float *>(smem + L::ut);
+    float *Sp = reinterpret_cast<float *>(smem + L::sp);
+    float *Yp = reinterpret_cast<float *>(smem + L::yp);
+    float *Up = reinterpret_cast<float *>(smem + L::up);
+    float *Dp = reinterpret_cast<float *>(smem + L::dp);
 
     auto qk_img = [&](int cc, int which) { return a.ws + w.qk + (((size_t)cc * a.n_kh + hk) * 2 + which) * C * D; };
     auto issue_kvg = [&](int cc) {
@@ -553,29 +660,36 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
         dma_image(a.ws + w.v + (ch * NB + blk) * C * kDB, Vb + b * C * kDB, C * kDB / 4, tid);
         dma_image(a.ws + w.g + ch * kGateRec, Gb + b * kGateRec, kGateRec / 4, tid);
     };
-    auto issue_t = [&](int cc) { dma_image(a.ws + w.t + ((size_t)cc * a.n_vh + h) * C * kCP, Tm, C * kCP / 4, tid); };
+    auto issue_t = [&](int cc) { dma_image(a.ws + w.t + ((size_t)cc * a.n_vh + h) * C * C, Tm, C * C / 4, tid); };
     auto issue_qp = [&](int cc) {
         dma_image(qk_img(cc, 0), Q, C * D / 4, tid);
-        dma_image(a.ws + w.p + ((size_t)cc * a.n_vh + h) * C * kCP, Pm, C * kCP / 4, tid);
+        dma_image(a.ws + w.p + ((size_t)cc * a.n_vh + h) * C * C, Pm, C * C / 4, tid);
     };
 
-    // ---- prologue: the state block, then chunk 0's operands
+    // ---- prologue: the state block.  Each lane keeps the S elements its S' tiles produce, in fp32
+    // registers (rows i = 4 lg + r, columns j = 16 ct + li of its tiles ct); the LDS copy is only
+    // the operand form.
     float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
-    for (int i = tid; i < kDB * D / 4; i += kPThreads) {
-        const int r = (4 * i) / D, cl = (4 * i) % D;
-        *reinterpret_cast<f4 *>(S + swz<D>(r, cl)) = reinterpret_cast<const f4 *>(st)[i];
-    }
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): the state block is loaded
+    f4 sreg[SCT];
+#pragma unroll
+    for (int q2 = 0; q2 < SCT; ++q2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sreg[q2][r] = st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li];
+#pragma unroll
+    for (int q2 = 0; q2 < SCT; ++q2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): nothing but the prefetches below in flight
     issue_kvg(0);
     issue_t(0);
     issue_qp(0);
 
     f4 o_prev = {0.f, 0.f, 0.f, 0.f};
-    auto store_o = [&](int cc) {  // rows t = 16 w + 4 (lane / 16) + r of chunk cc; whole chunks fit
+    auto store_o = [&](int cc) {  // rows t = 16 w + 4 lg + r of chunk cc; whole chunks fit
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = cc * C + 16 * wave + (lane >> 4) * 4 + r;
-            a.ws[w.o + ((size_t)t * a.n_vh + h) * D + blk * kDB + (lane & 15)] = o_prev[r];
+            const int t = cc * C + 16 * wave + 4 * lg + r;
+            a.ws[w.o + ((size_t)t * a.n_vh + h) * D + blk * kDB + li] = o_prev[r];
         }
     };
 #pragma unroll 1
@@ -593,33 +707,27 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
         {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < D; kk += 32) {
-                float av[8], bv[8];
-                load8(K + swz<D>(16 * wave + (lane & 15), kk + (lane >> 4) * 8), av);
-                load8(S + swz<D>(lane & 15, kk + (lane >> 4) * 8), bv);
-                acc = mma8<F32>(av, bv, acc);
-            }
-            const int i = lane & 15;
+            for (int kk = 0; kk < D; kk += 32)
+                acc = mma<F32>(MK::load(K, 16 * wave + li, kk + 8 * lg), MS::load(Sp, li, kk + 8 * lg), acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + (lane >> 4) * 4 + r;
-                Yt[i * kCP + t] = bet[t] * (Vc[t * kDB + i] - gam[t] * acc[r]);
+                const int t = 16 * wave + 4 * lg + r;
+                MU::put(Yp, li, t, bet[t] * (Vc[t * kDB + li] - gam[t] * acc[r]));
             }
         }
         lds_barrier();
-        // ---- B: U = T Y
+        // ---- B: U = T Y; U^T and U^T diag(dec) in operand form
         {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < C; kk += 32) {
-                float av[8], bv[8];
-                load8(Tm + (16 * wave + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
-                load8(Yt + (lane & 15) * kCP + kk + (lane >> 4) * 8, bv);
-                acc = mma8<F32>(av, bv, acc);
-            }
-            const int i = lane & 15;
+            for (int kk = 0; kk < C; kk += 32)
+                acc = mma<F32>(MT::load(Tm, 16 * wave + li, kk + 8 * lg), MU::load(Yp, li, kk + 8 * lg), acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Ut[i * kCP + 16 * wave + (lane >> 4) * 4 + r] = acc[r];
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * wave + 4 * lg + r;
+                MU::put(Up, li, t, acc[r]);
+                MU::put(Dp, li, t, acc[r] * dec[t]);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): q and P of chunk c
         lds_barrier();                      // also: every wave is done with T
@@ -628,67 +736,49 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
             issue_t(c + 1);
             issue_kvg(c + 1);  // the buffer chunk c-1 used
         }
-        // ---- C: O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K
-        constexpr int SCT = D / 16 / 4;  // S' column tiles per wave
-        f4 snew[SCT];
+        // ---- C: O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + (U^T diag(dec)) K
         {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < D; kk += 32) {
-                float av[8], bv[8];
-                load8(Q + swz<D>(16 * wave + (lane & 15), kk + (lane >> 4) * 8), av);
-                load8(S + swz<D>(lane & 15, kk + (lane >> 4) * 8), bv);
-                acc = mma8<F32>(av, bv, acc);
-            }
+            for (int kk = 0; kk < D; kk += 32)
+                acc = mma<F32>(MK::load(Q, 16 * wave + li, kk + 8 * lg), MS::load(Sp, li, kk + 8 * lg), acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= gam[16 * wave + (lane >> 4) * 4 + r];
+            for (int r = 0; r < 4; ++r) acc[r] *= gam[16 * wave + 4 * lg + r];
 #pragma unroll
-            for (int kk = 0; kk < C; kk += 32) {
-                float av[8], bv[8];
-                load8(Pm + (16 * wave + (lane & 15)) * kCP + kk + (lane >> 4) * 8, av);
-                load8(Ut + (lane & 15) * kCP + kk + (lane >> 4) * 8, bv);
-                acc = mma8<F32>(av, bv, acc);
-            }
+            for (int kk = 0; kk < C; kk += 32)
+                acc = mma<F32>(MT::load(Pm, 16 * wave + li, kk + 8 * lg), MU::load(Up, li, kk + 8 * lg), acc);
             o_prev = acc;
-            // S' block: rows i = 4 (lane / 16) + r, columns j = 16 ct + lane % 16
             const float gC = gam[C - 1];
 #pragma unroll
             for (int q2 = 0; q2 < SCT; ++q2) {
-                const int ct = SCT * wave + q2;
+                const int j = 16 * (SCT * wave + q2) + li;
                 f4 sa;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sa[r] = gC * S[swz<D>((lane >> 4) * 4 + r, 16 * ct + (lane & 15))];
+                for (int r = 0; r < 4; ++r) sa[r] = gC * sreg[q2][r];
 #pragma unroll
                 for (int kk = 0; kk < C; kk += 32) {
-                    float av[8], bv[8];
-                    load8(Ut + (lane & 15) * kCP + kk + (lane >> 4) * 8, av);
+                    Frag<F32> kf;  // K[s][j] down the column, s = kk + 8 lg + e
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int s_ = kk + (lane >> 4) * 8 + e;
-                        bv[e] = K[swz<D>(s_, 16 * ct + (lane & 15))] * dec[s_];
-                    }
-                    sa = mma8<F32>(av, bv, sa);
+                    for (int e = 0; e < 8; ++e) MK::get(K, kk + 8 * lg + e, j, kf, e);
+                    sa = mma<F32>(MU::load(Dp, li, kk + 8 * lg), kf, sa);
                 }
-                snew[q2] = sa;
+                sreg[q2] = sa;
             }
         }
-        lds_barrier();
+        lds_barrier();  // every wave is done reading S, q, P and this chunk's k
 #pragma unroll
-        for (int q2 = 0; q2 < SCT; ++q2) {
-            const int ct = SCT * wave + q2;
+        for (int q2 = 0; q2 < SCT; ++q2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[swz<D>((lane >> 4) * 4 + r, 16 * ct + (lane & 15))] = snew[q2][r];
-        }
+            for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
         if (c + 1 < nchunks) issue_qp(c + 1);
     }
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): every transfer into LDS has landed
     if (nchunks > 0) store_o(nchunks - 1);
-    __syncthreads();
     // ---- the state block after the last token
-    for (int i = tid; i < kDB * D / 4; i += kPThreads) {
-        const int r = (4 * i) / D, cl = (4 * i) % D;
-        reinterpret_cast<f4 *>(st)[i] = *reinterpret_cast<const f4 *>(S + swz<D>(r, cl));
-    }
+#pragma unroll
+    for (int q2 = 0; q2 < SCT; ++q2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li] = sreg[q2][r];
 }
 
 // out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) per (token, head); 16 lanes per row.  The
@@ -747,7 +837,7 @@ size_t prefill_lds_bytes(int d, bool act_bf16)
 {
     const size_t prep = d == 128 ? (act_bf16 ? PrepLds<128, uint16_t>::total : PrepLds<128, float>::total)
                                  : (act_bf16 ? PrepLds<64, uint16_t>::total : PrepLds<64, float>::total);
-    const size_t scan = d == 128 ? ScanLds<128>::total : ScanLds<64>::total;
+    const size_t scan = d == 128 ? ScanLds<128>::total : ScanLds<64>::total;  // the same for both dtypes
     return prep > scan ? prep : scan;
 }
 
