@@ -257,25 +257,20 @@ __device__ __forceinline__ void dma_image(const float *g, float *l, int n16, int
     for (int i = tid; i < n16; i += kPThreads) lds_dma16(g + 4 * i, l + 4 * i);
 }
 
-template <int D, typename act_t>
+template <int D>
 struct PrepLds {
     static constexpr int C = kChunk;
-    static constexpr int NCH = 3 * D;  // q | k | v channels of (key head, value head)
-    static constexpr size_t raw_bytes = sizeof(act_t) * (3 + C) * NCH;
+    static constexpr size_t qk_bytes = sizeof(float) * 2 * C * D;
     static constexpr size_t tp_bytes = sizeof(float) * (2 * C * kCP + 4 * 256);
-    static constexpr size_t q = 0;                                  // [C][D] swizzled
-    static constexpr size_t k = q + sizeof(float) * C * D;          // [C][D] swizzled
-    static constexpr size_t raw = k + sizeof(float) * C * D;        // [3 + C][NCH] raw rows t0-3 ..
-    static constexpr size_t tm = raw;                               // after the conv: [C][kCP] A, then T
-    static constexpr size_t pm = tm + sizeof(float) * C * kCP;      //                 [C][kCP] P
-    static constexpr size_t scr = pm + sizeof(float) * C * kCP;     //                 [4][16][16] scratch
-    static constexpr size_t hist = raw + (raw_bytes > tp_bytes ? raw_bytes : tp_bytes);  // [3][NCH] fp32
-    static constexpr size_t gate = hist + sizeof(float) * 3 * NCH;  // Gamma, gamma, beta, decay [4][C]
-    static constexpr size_t ab = gate + sizeof(float) * 4 * C;      // alpha, beta words [2][C]
-    static constexpr size_t total = ab + sizeof(uint32_t) * 2 * C;
+    static constexpr size_t q = 0;                               // [C][D] swizzled
+    static constexpr size_t k = q + sizeof(float) * C * D;       // [C][D] swizzled
+    static constexpr size_t tm = 0;                              // once q, k are consumed: [C][kCP] A, then T
+    static constexpr size_t pm = tm + sizeof(float) * C * kCP;   //                         [C][kCP] P
+    static constexpr size_t scr = pm + sizeof(float) * C * kCP;  //                         [4][16][16] scratch
+    static constexpr size_t gate = qk_bytes > tp_bytes ? qk_bytes : tp_bytes;  // Gamma, gamma, beta, decay [4][C]
+    static constexpr size_t total = gate + sizeof(float) * 4 * C;
 };
-static_assert(PrepLds<128, uint16_t>::total <= 160 * 1024, "bf16 d=128 prep must fit one CU's LDS");
-static_assert(PrepLds<64, float>::total <= 160 * 1024, "fp32 d=64 prep must fit one CU's LDS");
+static_assert(2 * PrepLds<128>::total <= 160 * 1024, "two d=128 prep workgroups must fit one CU's LDS");
 
 template <int D>
 struct ScanLds {
@@ -303,11 +298,9 @@ template <int D, bool ACT_BF16, bool QKN>
 __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
-    using L = PrepLds<D, act_t>;
+    using L = PrepLds<D>;
     constexpr bool F32 = !ACT_BF16;
     constexpr int C = kChunk;
-    constexpr int NCH = L::NCH;
-    constexpr int VEC = 16 / (int)sizeof(act_t);
     constexpr int NB = D / kDB;
     constexpr int QKG = 2 * D / 4;  // q | k channel groups of 4 (one per lane of a conv wave)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -324,58 +317,37 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *Q = reinterpret_cast<float *>(smem + L::q);
     float *K = reinterpret_cast<float *>(smem + L::k);
-    act_t *raw = reinterpret_cast<act_t *>(smem + L::raw);
     float *Tm = reinterpret_cast<float *>(smem + L::tm);
     float *Pm = reinterpret_cast<float *>(smem + L::pm);
-    float *hist = reinterpret_cast<float *>(smem + L::hist);
     float *Gam = reinterpret_cast<float *>(smem + L::gate);  // Gamma_t
     float *gam = Gam + C;                                    // gamma_t = exp(Gamma_t)
     float *bet = gam + C;                                    // beta_t (0 past the end)
     float *dec = bet + C;                                    // exp(Gamma_C - Gamma_t)
-    uint32_t *abw = reinterpret_cast<uint32_t *>(smem + L::ab);  // the words holding alpha_t, beta_t
 
     const act_t *qkv = static_cast<const act_t *>(a.qkv);
     auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
-    // alpha / beta of (token t, head h) sit in the 32-bit word at element (t H_v + h) & ~1 (bf16) or
-    // t H_v + h (fp32); the word never leaves the row because H_v is even for bf16
-    constexpr int EPW = ACT_BF16 ? 2 : 1;  // elements per word
-    const int ab_half = ACT_BF16 ? (h & 1) : 0;
-    auto word_val = [&](uint32_t wd) -> float {
-        if constexpr (ACT_BF16)
-            return bf16_to_f32((uint16_t)(ab_half ? (wd >> 16) : (wd & 0xffffu)));
-        else
-            return __builtin_bit_cast(float, wd);
+    // raw channels lc .. lc+3 of token t0 + t, -3 <= t < Lc (callers clamp t past the chunk); before
+    // the first chunk the three rows come from the conv state
+    auto ld4 = [&](int t, int lc) -> f4 {
+        if (c == 0 && t < 0)
+            return *reinterpret_cast<const f4 *>(a.conv_state + ((size_t)a.slot * 3 + 3 + t) * Cc + gchan(lc));
+        const size_t off = ((size_t)t0 + t) * Cc + gchan(lc);
+        if constexpr (ACT_BF16) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(qkv + off);
+            return f4{bf16_to_f32((uint16_t)(u.x & 0xffffu)), bf16_to_f32((uint16_t)(u.x >> 16)),
+                      bf16_to_f32((uint16_t)(u.y & 0xffffu)), bf16_to_f32((uint16_t)(u.y >> 16))};
+        } else {
+            return *reinterpret_cast<const f4 *>(qkv + off);
+        }
     };
-
-    // ---- stage: raw rows of tokens t0-3 .. t0+Lc-1 (row r holds token t0-3+r; before the first
-    // chunk the three rows come from the conv state instead), alpha / beta words
-    {
-        constexpr int nvr = NCH / VEC;
-        const int r0 = c == 0 ? 3 : 0;
-        for (int it = tid; it < (3 + Lc - r0) * nvr; it += kPThreads) {
-            const int r = r0 + it / nvr, lc = (it % nvr) * VEC;
-            lds_dma16(qkv + ((size_t)t0 - 3 + r) * Cc + gchan(lc), raw + r0 * NCH + it * VEC);
-        }
-        if (wave < 2 && lane < Lc) {
-            const size_t e = ((size_t)t0 + lane) * a.n_vh + (h & ~(EPW - 1));
-            const void *src = wave == 0 ? a.alpha : a.beta;
-            lds_dma4(static_cast<const unsigned char *>(src) + e * sizeof(act_t), abw + wave * C + lane);
-        }
-        if (c == 0) {
-            const float *cs = a.conv_state + (size_t)a.slot * 3 * Cc;
-            for (int i = tid; i < 3 * NCH; i += kPThreads) hist[i] = cs[(size_t)(i / NCH) * Cc + gchan(i % NCH)];
-        }
-    }
-    const float negA = -expf(a.A_log[h]), dtb = a.dt_bias[h];
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
-    lds_barrier();
 
     // ---- gates: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
     if (wave == 0) {
         float g = 0.f, b = 0.f;
         if (lane < Lc) {
-            g = negA * softplus_f(word_val(abw[lane]) + dtb);
-            b = word_val(abw[C + lane]);
+            const size_t e = ((size_t)t0 + lane) * a.n_vh + h;
+            g = -expf(a.A_log[h]) * softplus_f(load_act<ACT_BF16>(a.alpha, e) + a.dt_bias[h]);
+            b = load_act<ACT_BF16>(a.beta, e);
         }
         float x = g;
 #pragma unroll
@@ -389,21 +361,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
         dec[lane] = expf(__shfl(x, 63) - x);
     }
 
-    // ---- conv: q | k (wave w: tokens 16w .. 16w+15, lane: 4 channels), v (thread: a token, 4
-    // channels of every 16-row block, written straight to the workspace)
-    auto xrow = [&](int t, int lc) -> f4 {  // 4 raw channels of token t0 + t (t >= -3)
-        f4 x;
-        if (t < 0 && c == 0) {
-            x = *reinterpret_cast<const f4 *>(hist + (3 + t) * NCH + lc);
-        } else if constexpr (ACT_BF16) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(raw + (3 + t) * NCH + lc);
-            x = f4{bf16_to_f32((uint16_t)(u.x & 0xffffu)), bf16_to_f32((uint16_t)(u.x >> 16)),
-                   bf16_to_f32((uint16_t)(u.y & 0xffffu)), bf16_to_f32((uint16_t)(u.y >> 16))};
-        } else {
-            x = *reinterpret_cast<const f4 *>(raw + (3 + t) * NCH + lc);
-        }
-        return x;
-    };
+    // ---- conv of q | k into LDS: wave w takes tokens 16w .. 16w+15, a lane 4 channels; every row
+    // it reads is loaded before the first tap sum
     if (lane < QKG) {
         const int lc = 4 * lane;
         const bool isq = lc < D;
@@ -412,15 +371,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
         f4 wqk[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) wqk[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + j) * 4);
-        f4 x0 = xrow(16 * wave - 3, lc), x1 = xrow(16 * wave - 2, lc), x2 = xrow(16 * wave - 1, lc);
+        f4 xs[19];
+#pragma unroll
+        for (int i = 0; i < 19; ++i) xs[i] = ld4(min(16 * wave - 3 + i, Lc - 1), lc);
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
             const int t = 16 * wave + tt;
-            const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
             f4 y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float v = conv4(wqk[j], x0[j], x1[j], x2[j], x3[j]);
+                float v = conv4(wqk[j], xs[tt][j], xs[tt + 1][j], xs[tt + 2][j], xs[tt + 3][j]);
                 if constexpr (QKN) v = v * sigmoid_f(v);
                 y[j] = t < Lc ? v : 0.f;
             }
@@ -433,51 +393,62 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
                 for (int j = 0; j < 4; ++j) y[j] *= sc;
             }
             *reinterpret_cast<f4 *>(M + swz<D>(t, mc)) = y;
-            x0 = x1;
-            x1 = x2;
-            x2 = x3;
         }
     }
+    // ---- conv of v, straight to the workspace: a thread takes 4 channels of TPT consecutive tokens
     {
-        const int t = tid >> 2, e4 = 4 * (tid & 3);
-        float *vdst = a.ws + w.v + (((size_t)c * a.n_vh + h) * NB) * C * kDB + t * kDB + e4;
-#pragma unroll 1
-        for (int j = 0; j < NB; ++j) {
-            const int lc = 2 * D + kDB * j + e4;
-            f4 wv[4];
+        constexpr int VG = D / 4;                 // channel groups of 4
+        constexpr int TPT = C * VG / kPThreads;   // tokens per thread: 8 at d = 128, 4 at d = 64
+        const int vg = tid % VG, tb = (tid / VG) * TPT;
+        const int lc = 2 * D + 4 * vg;
+        f4 wv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + e) * 4);
-            const f4 x0 = xrow(t - 3, lc), x1 = xrow(t - 2, lc), x2 = xrow(t - 1, lc);
-            const f4 x3 = t < Lc ? xrow(t, lc) : f4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + e) * 4);
+        f4 xs[TPT + 3];
+#pragma unroll
+        for (int i = 0; i < TPT + 3; ++i) xs[i] = ld4(min(tb - 3 + i, Lc - 1), lc);
+        float *vdst = a.ws + w.v + (((size_t)c * a.n_vh + h) * NB + vg / 4) * C * kDB + 4 * (vg % 4);
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            const int t = tb + i;
             f4 y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float v = conv4(wv[e], x0[e], x1[e], x2[e], x3[e]);
+                float v = conv4(wv[e], xs[i][e], xs[i + 1][e], xs[i + 2][e], xs[i + 3][e]);
                 if constexpr (QKN) v = v * sigmoid_f(v);
                 y[e] = t < Lc ? v : 0.f;
             }
-            *reinterpret_cast<f4 *>(vdst + (size_t)j * C * kDB) = y;
+            *reinterpret_cast<f4 *>(vdst + t * kDB) = y;
         }
     }
-    lds_barrier();  // q, k and the gates are in LDS; the raw rows are consumed
-    // the upper blocks of A / T and P are zero
-    for (int i = tid; i < C * kCP; i += kPThreads) {
-        Tm[i] = 0.f;
-        Pm[i] = 0.f;
-    }
-    lds_barrier();
+    lds_barrier();  // q, k and the gates are in LDS
 
-    // ---- A = strictly-lower(beta e^{G_t-G_s} K K^T), P = lower(e^{G_t-G_s} Q K^T) (MFMA; waves
-    // 0, 1 build A, waves 2, 3 build P, row tiles {0,3} or {1,2}: 5 tiles per wave)
+    // ---- the q and k images (written by the key head's first value head), then
+    // A = strictly-lower(beta e^{G_t-G_s} K K^T), P = lower(e^{G_t-G_s} Q K^T) into registers (MFMA;
+    // waves 0, 1 build A, waves 2, 3 build P, row tiles {0,3} or {1,2}: 5 tiles per wave)
+    if (h % R == 0) {
+        using MQ = Mat<F32, C, D>;
+        float *qdst = a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D;
+        float *kdst = qdst + C * D;
+        for (int g = tid; g < C * D / 8; g += kPThreads) {
+            const int r = g / (D / 8), c0 = (g % (D / 8)) * 8;
+            float x[8];
+            load8(Q + swz<D>(r, c0), x);
+            MQ::put8(qdst, r, c0, x);
+            load8(K + swz<D>(r, c0), x);
+            MQ::put8(kdst, r, c0, x);
+        }
+    }
+    const int pair = wave & 1;
+    auto tile_rt = [&](int jt) { return pair == 0 ? (jt == 0 ? 0 : 3) : (jt < 2 ? 1 : 2); };
+    auto tile_ct = [&](int jt) { return pair == 0 ? (jt == 0 ? 0 : jt - 1) : (jt < 2 ? jt : jt - 2); };
+    f4 tiles[5];
     {
         const float *Am = wave < 2 ? K : Q;
-        float *Dm = wave < 2 ? Tm : Pm;
-        const int pair = wave & 1;
 #pragma unroll
         for (int jt = 0; jt < 5; ++jt) {
             // pair 0: (0,0) (3,0) (3,1) (3,2) (3,3);  pair 1: (1,0) (1,1) (2,0) (2,1) (2,2)
-            const int rt = pair == 0 ? (jt == 0 ? 0 : 3) : (jt < 2 ? 1 : 2);
-            const int ct = pair == 0 ? (jt == 0 ? 0 : jt - 1) : (jt < 2 ? jt : jt - 2);
+            const int rt = tile_rt(jt), ct = tile_ct(jt);
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D; kk += 32) {
@@ -486,13 +457,31 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
                 load8(K + swz<D>(16 * ct + (lane & 15), kk + (lane >> 4) * 8), bv);
                 acc = mma8<F32>(av, bv, acc);
             }
+            tiles[jt] = acc;
+        }
+    }
+    lds_barrier();  // q and k are consumed: their space holds A / T and P from here on
+    {
+        float *Dm = wave < 2 ? Tm : Pm;
+#pragma unroll
+        for (int jt = 0; jt < 5; ++jt) {
+            const int rt = tile_rt(jt), ct = tile_ct(jt);
             const int s_ = 16 * ct + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * rt + (lane >> 4) * 4 + r;
                 const float ratio = expf(Gam[t] - Gam[s_]);
-                Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * acc[r] : 0.f) : (s_ <= t ? ratio * acc[r] : 0.f);
+                Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * tiles[jt][r] : 0.f)
+                                            : (s_ <= t ? ratio * tiles[jt][r] : 0.f);
             }
+        }
+        // the six 16 x 16 blocks above the diagonal are zero
+        for (int i = tid; i < 6 * 256; i += kPThreads) {
+            const int bk = i >> 8, e = i & 255;
+            const int rt = bk < 3 ? 0 : (bk < 5 ? 1 : 2), ct = bk < 3 ? bk + 1 : (bk < 5 ? bk - 1 : 3);
+            const int at = (16 * rt + (e >> 4)) * kCP + 16 * ct + (e & 15);
+            Tm[at] = 0.f;
+            Pm[at] = 0.f;
         }
     }
     lds_barrier();
@@ -552,9 +541,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
     }
     lds_barrier();
 
-    // ---- the scan's operands, as the Mat images it copies
+    // ---- T, P and the gates for the scan (T and P as Mat images)
     {
-        using MQ = Mat<F32, C, D>;
         using MT = Mat<F32, C, C>;
         const size_t ch = (size_t)c * a.n_vh + h;
         float *tdst = a.ws + w.t + ch * C * C;
@@ -566,18 +554,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
             MT::put8(tdst, r, c0, x);
             load8(Pm + r * kCP + c0, x);
             MT::put8(pdst, r, c0, x);
-        }
-        if (h % R == 0) {  // q and k belong to the key head: its first value head writes them
-            float *qdst = a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D;
-            float *kdst = qdst + C * D;
-            for (int g = tid; g < C * D / 8; g += kPThreads) {
-                const int r = g / (D / 8), c0 = (g % (D / 8)) * 8;
-                float x[8];
-                load8(Q + swz<D>(r, c0), x);
-                MQ::put8(qdst, r, c0, x);
-                load8(K + swz<D>(r, c0), x);
-                MQ::put8(kdst, r, c0, x);
-            }
         }
         if (tid < C) {
             float *g = a.ws + w.g + ch * kGateRec;
@@ -781,39 +757,97 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
         for (int r = 0; r < 4; ++r) st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li] = sreg[q2][r];
 }
 
-// out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) per (token, head); 16 lanes per row.  The
-// conv state after the last token is written by the first rows' threads.
+// N consecutive activations (bf16 or fp32) at element offset off, as fp32; off is a multiple of N.
+template <bool BF16, int N>
+__device__ __forceinline__ void load_n(const void *p, size_t off, float (&x)[N])
+{
+    if constexpr (BF16) {
+        const uint16_t *q = static_cast<const uint16_t *>(p) + off;
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(q + e);
+            x[e] = bf16_to_f32((uint16_t)(u.x & 0xffffu));
+            x[e + 1] = bf16_to_f32((uint16_t)(u.x >> 16));
+            x[e + 2] = bf16_to_f32((uint16_t)(u.y & 0xffffu));
+            x[e + 3] = bf16_to_f32((uint16_t)(u.y >> 16));
+        }
+    } else {
+        const float *q = static_cast<const float *>(p) + off;
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const f4 v = *reinterpret_cast<const f4 *>(q + e);
+            x[e] = v[0];
+            x[e + 1] = v[1];
+            x[e + 2] = v[2];
+            x[e + 3] = v[3];
+        }
+    }
+}
+
+template <bool BF16, int N>
+__device__ __forceinline__ void store_n(void *p, size_t off, const float (&y)[N])
+{
+    if constexpr (BF16) {
+        uint16_t *q = static_cast<uint16_t *>(p) + off;
+#pragma unroll
+        for (int e = 0; e < N; e += 4)
+            *reinterpret_cast<uint2 *>(q + e) = uint2{(uint32_t)f32_to_bf16(y[e]) | ((uint32_t)f32_to_bf16(y[e + 1]) << 16),
+                                                      (uint32_t)f32_to_bf16(y[e + 2]) | ((uint32_t)f32_to_bf16(y[e + 3]) << 16)};
+    } else {
+        float *q = static_cast<float *>(p) + off;
+#pragma unroll
+        for (int e = 0; e < N; e += 4) *reinterpret_cast<f4 *>(q + e) = f4{y[e], y[e + 1], y[e + 2], y[e + 3]};
+    }
+}
+
+// out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) per (token, head): 16 lanes per row, each
+// 16-lane group takes kNormRows rows 16 apart and issues all their loads before any arithmetic.
+// The blocks after the rows write the conv state after the last token.
+constexpr int kNormRows = 4;
+
 template <int D, bool ACT_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillArgs a)
 {
     constexpr int EPL = D / 16;
-    const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int cg = threadIdx.x & 15;
+    const int grp = threadIdx.x >> 4, cg = threadIdx.x & 15;
     const int nrows = a.T * a.n_vh;
-    if (row < nrows) {
-        const float *o = a.ws + (size_t)row * D + cg * EPL;  // the readout sits at the start of the workspace
-        float ov[EPL], ss = 0.f;
+    const int row_blocks = (nrows + 16 * kNormRows - 1) / (16 * kNormRows);
+    if ((int)blockIdx.x < row_blocks) {
+        const int row0 = blockIdx.x * 16 * kNormRows + grp;
+        float ov[kNormRows][EPL], zv[kNormRows][EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            ov[e] = o[e];
-            ss += ov[e] * ov[e];
+        for (int k = 0; k < kNormRows; ++k) {
+            const int row = row0 + 16 * k;
+            if (row < nrows) {  // the same for the 16 lanes of a row
+                const size_t base = (size_t)row * D + cg * EPL;
+                load_n<false, EPL>(a.ws, base, ov[k]);  // the readout sits at the start of the workspace
+                load_n<ACT_BF16, EPL>(a.z, base, zv[k]);
+            }
         }
-        ss = row16_sum(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-        const size_t base = (size_t)row * D + cg * EPL;
+        float nw[EPL];
+        load_n<false, EPL>(a.norm_w, cg * EPL, nw);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const float zz = load_act<ACT_BF16>(a.z, base + e);
-            const float y = ov[e] * inv * a.norm_w[cg * EPL + e] * (zz * sigmoid_f(zz));
-            if constexpr (OUT_BF16)
-                static_cast<uint16_t *>(a.out)[base + e] = f32_to_bf16(y);
-            else
-                static_cast<float *>(a.out)[base + e] = y;
+        for (int k = 0; k < kNormRows; ++k) {
+            const int row = row0 + 16 * k;
+            if (row < nrows) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) ss += ov[k][e] * ov[k][e];
+                ss = row16_sum(ss);
+                const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+                float y[EPL];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const float zz = zv[k][e];
+                    y[e] = ov[k][e] * inv * nw[e] * (zz * sigmoid_f(zz));
+                }
+                store_n<OUT_BF16, EPL>(a.out, (size_t)row * D + cg * EPL, y);
+            }
         }
     } else {
         // conv state after the last token = the last three rows of concat(old conv state, qkv);
-        // one thread per channel, in the row-groups after the token rows
-        const int gc = (row - nrows) * 16 + cg;
+        // one thread per channel
+        const int gc = (blockIdx.x - row_blocks) * 256 + threadIdx.x;
         if (gc < a.C) {
             float r3[3];
 #pragma unroll
@@ -835,8 +869,8 @@ size_t prefill_workspace_bytes(int d, int n_kh, int n_vh, int T)
 
 size_t prefill_lds_bytes(int d, bool act_bf16)
 {
-    const size_t prep = d == 128 ? (act_bf16 ? PrepLds<128, uint16_t>::total : PrepLds<128, float>::total)
-                                 : (act_bf16 ? PrepLds<64, uint16_t>::total : PrepLds<64, float>::total);
+    (void)act_bf16;  // neither kernel stages raw activations in LDS
+    const size_t prep = d == 128 ? PrepLds<128>::total : PrepLds<64>::total;
     const size_t scan = d == 128 ? ScanLds<128>::total : ScanLds<64>::total;  // the same for both dtypes
     return prep > scan ? prep : scan;
 }
@@ -844,18 +878,18 @@ size_t prefill_lds_bytes(int d, bool act_bf16)
 template <int D, bool AB, bool OB, bool QKN>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
-    using act_t = typename std::conditional<AB, uint16_t, float>::type;
     const int nchunks = (a.T + kChunk - 1) / kChunk;
-    const size_t prep_lds = PrepLds<D, act_t>::total;
+    const size_t prep_lds = PrepLds<D>::total;
     hipLaunchKernelGGL((prefill_prep_kernel<D, AB, QKN>), dim3(nchunks * a.n_vh), dim3(kPThreads), prep_lds, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, !AB>), dim3(a.n_vh * (D / kDB)), dim3(kPThreads), ScanLds<D>::total,
                        stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     const long rows = (long)a.T * a.n_vh;
-    const long conv_rows = (a.C + 15) / 16;  // 16 threads per row-group also cover the conv state
-    hipLaunchKernelGGL((prefill_norm_kernel<D, AB, OB>), dim3((unsigned)((rows + conv_rows + 15) / 16)), dim3(256), 0,
-                       stream, a);
+    const long row_blocks = (rows + 16 * kNormRows - 1) / (16 * kNormRows);
+    const long conv_blocks = (a.C + 255) / 256;
+    hipLaunchKernelGGL((prefill_norm_kernel<D, AB, OB>), dim3((unsigned)(row_blocks + conv_blocks)), dim3(256), 0, stream,
+                       a);
     return hipGetLastError();
 }
 template <int D, bool AB, bool OB>

@@ -30,16 +30,16 @@ GDN_API int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, c
     if (!state || !conv_state || !qkv || !z || !alpha || !beta || !A_log || !dt_bias || !conv_w || !norm_w || !out ||
         !workspace)
         return gdn::abi_fail(GDN_ERR_ARG, "gdn_prefill: a required pointer is NULL");
-    if (!aligned16(state) || !aligned16(conv_state) || !aligned16(conv_w) || !aligned16(qkv) || !aligned16(workspace))
-        return gdn::abi_fail(GDN_ERR_ARG, "gdn_prefill: state, conv_state, conv_w, qkv and workspace must be 16-byte aligned");
+    if (!aligned16(state) || !aligned16(conv_state) || !aligned16(conv_w) || !aligned16(qkv) || !aligned16(workspace) ||
+        !aligned16(z) || !aligned16(out) || !aligned16(norm_w))
+        return gdn::abi_fail(GDN_ERR_ARG,
+                             "gdn_prefill: state, conv_state, conv_w, qkv, z, out, norm_w and workspace must be 16-byte aligned");
     if (n_tok < 1) return gdn::abi_fail(GDN_ERR_RANGE, "gdn_prefill: n_tok must be >= 1");
     if (slot < 0 || slot >= d.n_pool) return gdn::abi_fail(GDN_ERR_RANGE, "gdn_prefill: slot outside [0, n_pool)");
     if (ws_bytes < gdn::prefill_workspace_bytes(d.d_v, d.n_kh, d.n_vh, n_tok))
         return gdn::abi_fail(GDN_ERR_ARG, "gdn_prefill: workspace smaller than gdn_prefill_workspace_bytes()");
-    if (d.act_dtype == GDN_BF16 && (d.n_vh & 1))
-        return gdn::abi_fail(GDN_ERR_SHAPE, "gdn_prefill: bf16 activations need an even number of value heads");
     if (gdn::prefill_lds_bytes(d.d_k, d.act_dtype == GDN_BF16) > kMaxLds)
-        return gdn::abi_fail(GDN_ERR_SHAPE, "gdn_prefill: fp32 activations with d = 128 exceed one workgroup's LDS");
+        return gdn::abi_fail(GDN_ERR_SHAPE, "gdn_prefill: the kernels' LDS exceeds one workgroup's 160 KiB");
     gdn::PrefillArgs a{};
     a.n_kh = d.n_kh;
     a.n_vh = d.n_vh;

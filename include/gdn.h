@@ -172,8 +172,11 @@ int gdn_rollback_trim(const gdn_capture *capture, int32_t slot, int32_t trim, in
  * rollback tensors, lucebox-hub internal.h, create_target_cache prefill_only).  Same result as
  * gdn_verify with capture == NULL, computed in chunks of 64 tokens in the WY/UT form with the
  * dense intra-chunk products on MFMA.  workspace: device memory of at least
- * gdn_prefill_workspace_bytes(dims, n_tok) bytes, 256-byte aligned.
+ * gdn_prefill_workspace_bytes(dims, n_tok) bytes (per-chunk operands and the fp32 readout; its
+ * contents need no initialisation and are garbage afterwards).
  *   qkv [n_tok][C], z and out [n_tok][H_v][d_v], alpha and beta [n_tok][H_v].
+ * state, conv_state, conv_w, qkv, z, out, norm_w and workspace must be 16-byte aligned
+ * (GDN_ERR_ARG).
  */
 int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
                 const void *z, const void *alpha, const void *beta, const float *A_log,

@@ -64,6 +64,11 @@ PREFILL_CASES = {
     "fp32_d64_weak_200": (W.shape_with(W.TINY_VERIFY, n_tok=200, n_kh=2, n_vh=4),
                           {"weak_decay": True}, 0),
     "qk_norm_flag_160": (W.shape_with(W.CHUNKED_PREFILL, n_tok=160), {"weak_decay": True}, 1),
+    "fp32_d128_weak_130": (W.shape_with(W.CHUNKED_PREFILL, n_tok=130, act_dtype=W.F32, out_dtype=W.F32),
+                           {"weak_decay": True}, 0),
+    "bf16_odd_heads_96": (W.shape_with(W.CHUNKED_PREFILL, n_tok=96, n_kh=3, n_vh=3), {"weak_decay": True}, 0),
+    "bf16_d64_odd_heads_150": (W.shape_with(W.TINY_VERIFY, n_tok=150, n_kh=1, n_vh=3, act_dtype=W.BF16,
+                                            out_dtype=W.BF16), {"weak_decay": True}, 0),
 }
 
 
