@@ -249,14 +249,6 @@ __host__ __device__ inline PrefillWs prefill_ws(int d, int n_kh, int n_vh, int T
     return w;
 }
 
-// Copy n16 16-byte units from global memory to LDS with global_load_lds (lane i of a wave lands at
-// the wave's base + 16 i).  Thread tid issues units tid, tid + 256, ...: every wave issues
-// floor(n16 / 256) transfers, the first waves one more when n16 is not a multiple of 256.
-__device__ __forceinline__ void dma_image(const float *g, float *l, int n16, int tid)
-{
-    for (int i = tid; i < n16; i += kPThreads) lds_dma16(g + 4 * i, l + 4 * i);
-}
-
 template <int D>
 struct PrepLds {
     static constexpr int C = kChunk;
@@ -570,29 +562,28 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
 //   A: Y^T = beta V^T - (S K^T) diag(beta gamma)        (wave w: tokens 16w .. 16w+15)
 //   B: U^T = Y^T T^T
 //   C: O   = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K
-// The next chunk's operands arrive by global_load_lds while this one computes.  Loads and stores
-// share gfx950's one vector-memory counter and a store may complete before an older load, so a
-// partial wait is only sound when no store was issued after the loads it waits for.  Order within
-// chunk c:
-//   wait: everything but q, P of chunk c  |  A  |  B  |  wait: everything
-//   stores of chunk c-1's readout, then issue T, k, v, gates of chunk c+1  |  C  |  issue q, P of c+1
-// so the one slot for stores follows a full wait, the k / v / gates / T transfers travel during C,
-// and q / P during A and B of the next chunk.  k, v and gates are double-buffered (the next chunk's
-// arrive while C still reads this chunk's).
+// Four compute waves run A, B, C; four producer waves move every operand into LDS with
+// global_load_lds while they compute, so the transfers' issue cost stays off the chain (one
+// producer wave alone issues them too slowly: the transfers are 1 KiB per instruction).  Per
+// chunk c the producer waits for k, v, gates and T of c (its q and P may still travel), then for
+// q and P before C, then issues T, k, v, gates of c+1 during C (k, v, gates double-buffered) and
+// q, P of c+1 once C has read this chunk's.  Only producers issue loads and the compute waves only
+// store, so every wait counts transfers of one kind on a producer's own counter.
+constexpr int kProducers = 4;
+constexpr int kScanThreads = kPThreads + 64 * kProducers;
+
 template <int D>
 struct ScanCounts {
-    static constexpr int per_wave(int n16) { return n16 / kPThreads; }  // the minimum over the waves
-    static constexpr int q = per_wave(kChunk * D / 4);
-    static constexpr int p = per_wave(kChunk * kChunk / 4);
-    static constexpr int top = q + p;  // at the top of a chunk only its q and P may be in flight
-    static_assert(top < 64, "vmcnt holds at most 63");
+    static constexpr int per_wave(int n16) { return n16 / (64 * kProducers); }  // the minimum over producers
+    static constexpr int qp = per_wave(kChunk * D / 4) + per_wave(kChunk * kChunk / 4);
+    static_assert(qp < 64, "vmcnt holds at most 63");
 };
 // s_waitcnt immediate: wait until at most n vector-memory operations are outstanding (gfx9
 // encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
 
 template <int D, bool F32>
-__global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs a)
 {
     using L = ScanLds<D>;
     using N = ScanCounts<D>;
@@ -602,8 +593,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
     using MT = Mat<F32, C, C>;    // T and P images
     using MS = Mat<F32, kDB, D>;  // the S block
     using MU = Mat<F32, kDB, C>;  // Y^T, U^T, U^T diag(dec)
-    constexpr int SCT = D / 16 / 4;  // S column tiles per wave
+    constexpr int SCT = D / 16 / 4;  // S column tiles per compute wave
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool producer = wave >= 4;
+    const int ptid = tid - kPThreads;  // producer thread index
     const int R = a.n_vh / a.n_kh;
     // workgroups are dealt to the 8 XCDs in turn: keep the row blocks of a key head's value heads on
     // one XCD, so the operand images they all read are fetched into that XCD's L2 once
@@ -628,37 +621,42 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
     float *Up = reinterpret_cast<float *>(smem + L::up);
     float *Dp = reinterpret_cast<float *>(smem + L::dp);
 
+    // ---- the producers' transfers (lane i of a global_load_lds lands at the base + 16 i)
+    auto dma = [&](const float *g, float *l, int n16) {
+        for (int i = ptid; i < n16; i += 64 * kProducers) lds_dma16(g + 4 * i, l + 4 * i);
+    };
     auto qk_img = [&](int cc, int which) { return a.ws + w.qk + (((size_t)cc * a.n_kh + hk) * 2 + which) * C * D; };
-    auto issue_kvg = [&](int cc) {
+    auto issue_tkvg = [&](int cc) {  // T, then k, v, gates into buffer cc & 1
         const int b = cc & 1;
         const size_t ch = (size_t)cc * a.n_vh + h;
-        dma_image(qk_img(cc, 1), Kb + b * C * D, C * D / 4, tid);
-        dma_image(a.ws + w.v + (ch * NB + blk) * C * kDB, Vb + b * C * kDB, C * kDB / 4, tid);
-        dma_image(a.ws + w.g + ch * kGateRec, Gb + b * kGateRec, kGateRec / 4, tid);
+        dma(a.ws + w.t + ch * C * C, Tm, C * C / 4);
+        dma(qk_img(cc, 1), Kb + b * C * D, C * D / 4);
+        dma(a.ws + w.v + (ch * NB + blk) * C * kDB, Vb + b * C * kDB, C * kDB / 4);
+        dma(a.ws + w.g + ch * kGateRec, Gb + b * kGateRec, kGateRec / 4);
     };
-    auto issue_t = [&](int cc) { dma_image(a.ws + w.t + ((size_t)cc * a.n_vh + h) * C * C, Tm, C * C / 4, tid); };
     auto issue_qp = [&](int cc) {
-        dma_image(qk_img(cc, 0), Q, C * D / 4, tid);
-        dma_image(a.ws + w.p + ((size_t)cc * a.n_vh + h) * C * C, Pm, C * C / 4, tid);
+        dma(qk_img(cc, 0), Q, C * D / 4);
+        dma(a.ws + w.p + ((size_t)cc * a.n_vh + h) * C * C, Pm, C * C / 4);
     };
 
-    // ---- prologue: the state block.  Each lane keeps the S elements its S' tiles produce, in fp32
-    // registers (rows i = 4 lg + r, columns j = 16 ct + li of its tiles ct); the LDS copy is only
-    // the operand form.
+    // ---- prologue: the state block.  Each compute lane keeps the S elements its S' tiles produce,
+    // in fp32 registers (rows i = 4 lg + r, columns j = 16 ct + li of its tiles ct); the LDS copy is
+    // only the operand form.
     float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
     f4 sreg[SCT];
+    if (producer) {
+        issue_tkvg(0);
+        issue_qp(0);
+    } else {
 #pragma unroll
-    for (int q2 = 0; q2 < SCT; ++q2)
+        for (int q2 = 0; q2 < SCT; ++q2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sreg[q2][r] = st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li];
+            for (int r = 0; r < 4; ++r) sreg[q2][r] = st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li];
 #pragma unroll
-    for (int q2 = 0; q2 < SCT; ++q2)
+        for (int q2 = 0; q2 < SCT; ++q2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): nothing but the prefetches below in flight
-    issue_kvg(0);
-    issue_t(0);
-    issue_qp(0);
+            for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
+    }
 
     f4 o_prev = {0.f, 0.f, 0.f, 0.f};
     auto store_o = [&](int cc) {  // rows t = 16 w + 4 lg + r of chunk cc; whole chunks fit
@@ -676,11 +674,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
         const float *gam = Gb + b * kGateRec;
         const float *bet = gam + C;
         const float *dec = bet + C;
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(N::top));  // k, v, gates, T of chunk c (q, P may travel)
+        if (producer) __builtin_amdgcn_s_waitcnt(vmcnt_imm(N::qp));  // T, k, v, gates of c (q, P may travel)
         lds_barrier();
-
         // ---- A: Y^T[i][t] = beta_t (V[t][i] - gamma_t (K S^T)[t][i])
-        {
+        if (!producer) {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D; kk += 32)
@@ -693,7 +690,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
         }
         lds_barrier();
         // ---- B: U = T Y; U^T and U^T diag(dec) in operand form
-        {
+        if (!producer) {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < C; kk += 32)
@@ -704,16 +701,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
                 MU::put(Up, li, t, acc[r]);
                 MU::put(Dp, li, t, acc[r] * dec[t]);
             }
+        } else {
+            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): q and P of chunk c
         }
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): q and P of chunk c
-        lds_barrier();                      // also: every wave is done with T
-        if (c > 0) store_o(c - 1);
-        if (c + 1 < nchunks) {
-            issue_t(c + 1);
-            issue_kvg(c + 1);  // the buffer chunk c-1 used
-        }
-        // ---- C: O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + (U^T diag(dec)) K
-        {
+        lds_barrier();  // q and P have landed; every compute wave is done with T
+        if (producer) {
+            if (c + 1 < nchunks) issue_tkvg(c + 1);  // k, v, gates into the buffer chunk c-1 used
+        } else {
+            if (c > 0) store_o(c - 1);
+            // ---- C: O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + (U^T diag(dec)) K
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D; kk += 32)
@@ -741,20 +737,26 @@ __global__ __launch_bounds__(kPThreads) void prefill_scan_kernel(PrefillArgs a)
                 sreg[q2] = sa;
             }
         }
-        lds_barrier();  // every wave is done reading S, q, P and this chunk's k
+        lds_barrier();  // every compute wave is done reading S, q, P and this chunk's k
+        if (producer) {
+            if (c + 1 < nchunks) issue_qp(c + 1);
+        } else {
+#pragma unroll
+            for (int q2 = 0; q2 < SCT; ++q2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
+        }
+    }
+    if (producer) {
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no transfer into LDS outlives the workgroup
+    } else {
+        if (nchunks > 0) store_o(nchunks - 1);
+        // ---- the state block after the last token
 #pragma unroll
         for (int q2 = 0; q2 < SCT; ++q2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
-        if (c + 1 < nchunks) issue_qp(c + 1);
+            for (int r = 0; r < 4; ++r) st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li] = sreg[q2][r];
     }
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): every transfer into LDS has landed
-    if (nchunks > 0) store_o(nchunks - 1);
-    // ---- the state block after the last token
-#pragma unroll
-    for (int q2 = 0; q2 < SCT; ++q2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li] = sreg[q2][r];
 }
 
 // N consecutive activations (bf16 or fp32) at element offset off, as fp32; off is a multiple of N.
@@ -882,7 +884,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     const size_t prep_lds = PrepLds<D>::total;
     hipLaunchKernelGGL((prefill_prep_kernel<D, AB, QKN>), dim3(nchunks * a.n_vh), dim3(kPThreads), prep_lds, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<D, !AB>), dim3(a.n_vh * (D / kDB)), dim3(kPThreads), ScanLds<D>::total,
+    hipLaunchKernelGGL((prefill_scan_kernel<D, !AB>), dim3(a.n_vh * (D / kDB)), dim3(kScanThreads), ScanLds<D>::total,
                        stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     const long rows = (long)a.T * a.n_vh;
