@@ -285,9 +285,11 @@ struct ScanLds {
 };
 static_assert(ScanLds<128>::total <= 160 * 1024, "d=128 scan must fit one CU's LDS");
 
-// ============================== kernel 1: per (chunk, value head) ==============================
+// ============================== kernel 1: per (chunk, key head) ==============================
+// The q | k conv and the Gram products K K^T and Q K^T are shared by the key head's value heads;
+// the gates, A / P, T and the v conv are per value head, in a loop.
 template <int D, bool ACT_BF16, bool QKN>
-__global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_prep_kernel(PrefillArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
     using L = PrepLds<D>;
@@ -298,12 +300,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int R = a.n_vh / a.n_kh;
 
-    const int c = blockIdx.x / a.n_vh, h = blockIdx.x % a.n_vh;
-    const int hk = h / R;
+    const int c = blockIdx.x / a.n_kh, hk = blockIdx.x % a.n_kh;
     const int T = a.T;
     const int Cc = a.C;  // conv channels
     const int t0 = c * C, Lc = min(C, T - t0);
-    const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + h * D;
+    const int q0 = hk * D, k0 = a.n_kh * D + hk * D;
+    int v0 = 2 * a.n_kh * D + hk * R * D;  // v channels of the value head in progress
     const PrefillWs w = prefill_ws(D, a.n_kh, a.n_vh, T);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -333,25 +335,55 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
         }
     };
 
-    // ---- gates: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
-    if (wave == 0) {
-        float g = 0.f, b = 0.f;
-        if (lane < Lc) {
-            const size_t e = ((size_t)t0 + lane) * a.n_vh + h;
-            g = -expf(a.A_log[h]) * softplus_f(load_act<ACT_BF16>(a.alpha, e) + a.dt_bias[h]);
-            b = load_act<ACT_BF16>(a.beta, e);
-        }
-        float x = g;
+    // gates of value head h: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
+    auto gates = [&](int h) {
+        if (wave == 0) {
+            float g = 0.f, b = 0.f;
+            if (lane < Lc) {
+                const size_t e = ((size_t)t0 + lane) * a.n_vh + h;
+                g = -expf(a.A_log[h]) * softplus_f(load_act<ACT_BF16>(a.alpha, e) + a.dt_bias[h]);
+                b = load_act<ACT_BF16>(a.beta, e);
+            }
+            float x = g;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (lane >= off) x += y;
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            Gam[lane] = x;
+            gam[lane] = expf(x);
+            bet[lane] = b;
+            dec[lane] = expf(__shfl(x, 63) - x);
         }
-        Gam[lane] = x;
-        gam[lane] = expf(x);
-        bet[lane] = b;
-        dec[lane] = expf(__shfl(x, 63) - x);
-    }
+    };
+
+    // conv of value head h's v, straight to the workspace: a thread takes 4 channels of TPT
+    // consecutive tokens
+    auto conv_v = [&](int h) {
+        constexpr int VG = D / 4;                 // channel groups of 4
+        constexpr int TPT = C * VG / kPThreads;   // tokens per thread: 8 at d = 128, 4 at d = 64
+        const int vg = tid % VG, tb = (tid / VG) * TPT;
+        const int lc = 2 * D + 4 * vg;
+        f4 wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + e) * 4);
+        f4 xs[TPT + 3];
+#pragma unroll
+        for (int i = 0; i < TPT + 3; ++i) xs[i] = ld4(min(tb - 3 + i, Lc - 1), lc);
+        float *vdst = a.ws + w.v + (((size_t)c * a.n_vh + h) * NB + vg / 4) * C * kDB + 4 * (vg % 4);
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            const int t = tb + i;
+            f4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = conv4(wv[e], xs[i][e], xs[i + 1][e], xs[i + 2][e], xs[i + 3][e]);
+                if constexpr (QKN) v = v * sigmoid_f(v);
+                y[e] = t < Lc ? v : 0.f;
+            }
+            *reinterpret_cast<f4 *>(vdst + t * kDB) = y;
+        }
+    };
 
     // ---- conv of q | k into LDS: wave w takes tokens 16w .. 16w+15, a lane 4 channels; every row
     // it reads is loaded before the first tap sum
@@ -387,38 +419,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
             *reinterpret_cast<f4 *>(M + swz<D>(t, mc)) = y;
         }
     }
-    // ---- conv of v, straight to the workspace: a thread takes 4 channels of TPT consecutive tokens
-    {
-        constexpr int VG = D / 4;                 // channel groups of 4
-        constexpr int TPT = C * VG / kPThreads;   // tokens per thread: 8 at d = 128, 4 at d = 64
-        const int vg = tid % VG, tb = (tid / VG) * TPT;
-        const int lc = 2 * D + 4 * vg;
-        f4 wv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + e) * 4);
-        f4 xs[TPT + 3];
-#pragma unroll
-        for (int i = 0; i < TPT + 3; ++i) xs[i] = ld4(min(tb - 3 + i, Lc - 1), lc);
-        float *vdst = a.ws + w.v + (((size_t)c * a.n_vh + h) * NB + vg / 4) * C * kDB + 4 * (vg % 4);
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int t = tb + i;
-            f4 y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = conv4(wv[e], xs[i][e], xs[i + 1][e], xs[i + 2][e], xs[i + 3][e]);
-                if constexpr (QKN) v = v * sigmoid_f(v);
-                y[e] = t < Lc ? v : 0.f;
-            }
-            *reinterpret_cast<f4 *>(vdst + t * kDB) = y;
-        }
-    }
-    lds_barrier();  // q, k and the gates are in LDS
+    lds_barrier();  // q and k are in LDS
 
-    // ---- the q and k images (written by the key head's first value head), then
-    // A = strictly-lower(beta e^{G_t-G_s} K K^T), P = lower(e^{G_t-G_s} Q K^T) into registers (MFMA;
-    // waves 0, 1 build A, waves 2, 3 build P, row tiles {0,3} or {1,2}: 5 tiles per wave)
-    if (h % R == 0) {
+    // ---- the q and k images, then the lower 16 x 16 tiles of K K^T (waves 0, 1) and Q K^T (waves
+    // 2, 3) into registers (MFMA; row tiles {0,3} or {1,2}: 5 tiles per wave).  Each value head's
+    // A = strictly-lower(beta e^{G_t-G_s} K K^T) and P = lower(e^{G_t-G_s} Q K^T) scale them.
+    {
         using MQ = Mat<F32, C, D>;
         float *qdst = a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D;
         float *kdst = qdst + C * D;
@@ -453,106 +459,115 @@ __global__ __launch_bounds__(kPThreads) void prefill_prep_kernel(PrefillArgs a)
         }
     }
     lds_barrier();  // q and k are consumed: their space holds A / T and P from here on
-    {
-        float *Dm = wave < 2 ? Tm : Pm;
+#pragma unroll 1
+    for (int hh = 0; hh < R; ++hh) {
+        const int h = hk * R + hh;
+        v0 = 2 * a.n_kh * D + h * D;
+        if (hh > 0) lds_barrier();  // the previous head's T, P and gates are written out
+        gates(h);
+        conv_v(h);
+        lds_barrier();
+        {
+            float *Dm = wave < 2 ? Tm : Pm;
 #pragma unroll
-        for (int jt = 0; jt < 5; ++jt) {
-            const int rt = tile_rt(jt), ct = tile_ct(jt);
-            const int s_ = 16 * ct + (lane & 15);
+            for (int jt = 0; jt < 5; ++jt) {
+                const int rt = tile_rt(jt), ct = tile_ct(jt);
+                const int s_ = 16 * ct + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * rt + (lane >> 4) * 4 + r;
-                const float ratio = expf(Gam[t] - Gam[s_]);
-                Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * tiles[jt][r] : 0.f)
-                                            : (s_ <= t ? ratio * tiles[jt][r] : 0.f);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * rt + (lane >> 4) * 4 + r;
+                    const float ratio = expf(Gam[t] - Gam[s_]);
+                    Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * tiles[jt][r] : 0.f)
+                                                : (s_ <= t ? ratio * tiles[jt][r] : 0.f);
+                }
+            }
+            // the six 16 x 16 blocks above the diagonal are zero
+            for (int i = tid; i < 6 * 256; i += kPThreads) {
+                const int bk = i >> 8, e = i & 255;
+                const int rt = bk < 3 ? 0 : (bk < 5 ? 1 : 2), ct = bk < 3 ? bk + 1 : (bk < 5 ? bk - 1 : 3);
+                const int at = (16 * rt + (e >> 4)) * kCP + 16 * ct + (e & 15);
+                Tm[at] = 0.f;
+                Pm[at] = 0.f;
             }
         }
-        // the six 16 x 16 blocks above the diagonal are zero
-        for (int i = tid; i < 6 * 256; i += kPThreads) {
-            const int bk = i >> 8, e = i & 255;
-            const int rt = bk < 3 ? 0 : (bk < 5 ? 1 : 2), ct = bk < 3 ? bk + 1 : (bk < 5 ? bk - 1 : 3);
-            const int at = (16 * rt + (e >> 4)) * kCP + 16 * ct + (e & 15);
-            Tm[at] = 0.f;
-            Pm[at] = 0.f;
+        lds_barrier();
+        // ---- T = (I + A)^-1: 16x16 diagonal blocks by forward substitution (wave w, lane c < 16
+        // solves column c of block w), then the blocks below them
+        if (lane < 16) {
+            const int wv = wave, cc = lane;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                for (int s_ = 0; s_ < r; ++s_) acc -= Tm[(16 * wv + r) * kCP + 16 * wv + s_] * x[s_];
+                x[r] = (r < cc) ? 0.f : acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tm[(16 * wv + r) * kCP + 16 * wv + cc] = x[r];
         }
-    }
-    lds_barrier();
-    // ---- T = (I + A)^-1: 16x16 diagonal blocks by forward substitution (wave w, lane c < 16
-    // solves column c of block w), then the blocks below them
-    if (lane < 16) {
-        const int wv = wave, cc = lane;
-        float x[16];
+        lds_barrier();
+        // T_10 = -T_11 A_10 T_00 (wave 0) and T_32 = -T_33 A_32 T_22 (wave 1), the product A T
+        // parked in the scratch; T_ij = -T_ii (sum_k A_ik T_kj) for the 32 x 32 block below
+        float *scr_all = reinterpret_cast<float *>(smem + L::scr);
+        float *scr = scr_all + wave * 256;  // [16][16] per wave
+        auto park = [&](f4 v) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == cc) ? 1.f : 0.f;
+            for (int r = 0; r < 4; ++r) scr[((lane >> 4) * 4 + r) * 16 + (lane & 15)] = v[r];
+        };
+        auto blk16s = [&](const float *X, int xr0, int xc0, const float *Y, f4 acc) {  // acc += X(block) Y
 #pragma unroll
-            for (int s_ = 0; s_ < r; ++s_) acc -= Tm[(16 * wv + r) * kCP + 16 * wv + s_] * x[s_];
-            x[r] = (r < cc) ? 0.f : acc;
+            for (int st2 = 0; st2 < 4; ++st2) {
+                const int kk = 4 * st2 + (lane >> 4);
+                acc = mfma4f32(X[(xr0 + (lane & 15)) * kCP + xc0 + kk], Y[kk * 16 + (lane & 15)], acc);
+            }
+            return acc;
+        };
+        auto put_neg = [&](int r0, int c0, f4 v) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Tm[(r0 + (lane >> 4) * 4 + r) * kCP + c0 + (lane & 15)] = -v[r];
+        };
+        if (wave < 2) {
+            const int i = wave == 0 ? 1 : 3, j = i - 1;
+            park(blk16(Tm, 16 * i, 16 * j, Tm, 16 * j, 16 * j, f4{0.f, 0.f, 0.f, 0.f}, lane));
+            put_neg(16 * i, 16 * j, blk16s(Tm, 16 * i, 16 * i, scr, f4{0.f, 0.f, 0.f, 0.f}));
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(16 * wv + r) * kCP + 16 * wv + cc] = x[r];
-    }
-    lds_barrier();
-    // T_10 = -T_11 A_10 T_00 (wave 0) and T_32 = -T_33 A_32 T_22 (wave 1), the product A T
-    // parked in the scratch; T_ij = -T_ii (sum_k A_ik T_kj) for the 32 x 32 block below
-    float *scr_all = reinterpret_cast<float *>(smem + L::scr);
-    float *scr = scr_all + wave * 256;  // [16][16] per wave
-    auto park = [&](f4 v) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) scr[((lane >> 4) * 4 + r) * 16 + (lane & 15)] = v[r];
-    };
-    auto blk16s = [&](const float *X, int xr0, int xc0, const float *Y, f4 acc) {  // acc += X(block) Y
-#pragma unroll
-        for (int st2 = 0; st2 < 4; ++st2) {
-            const int kk = 4 * st2 + (lane >> 4);
-            acc = mfma4f32(X[(xr0 + (lane & 15)) * kCP + xc0 + kk], Y[kk * 16 + (lane & 15)], acc);
+        lds_barrier();
+        const int r3 = 2 + (wave >> 1), c3 = wave & 1;  // block (r3, c3) of the lower-left 32 x 32
+        {  // X_rc = A_r0 T_0c + A_r1 T_1c
+            f4 x = blk16(Tm, 16 * r3, 16, Tm, 16, 16 * c3, f4{0.f, 0.f, 0.f, 0.f}, lane);
+            if (c3 == 0) x = blk16(Tm, 16 * r3, 0, Tm, 0, 0, x, lane);
+            park(x);
         }
-        return acc;
-    };
-    auto put_neg = [&](int r0, int c0, f4 v) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Tm[(r0 + (lane >> 4) * 4 + r) * kCP + c0 + (lane & 15)] = -v[r];
-    };
-    if (wave < 2) {
-        const int i = wave == 0 ? 1 : 3, j = i - 1;
-        park(blk16(Tm, 16 * i, 16 * j, Tm, 16 * j, 16 * j, f4{0.f, 0.f, 0.f, 0.f}, lane));
-        put_neg(16 * i, 16 * j, blk16s(Tm, 16 * i, 16 * i, scr, f4{0.f, 0.f, 0.f, 0.f}));
-    }
-    lds_barrier();
-    const int r3 = 2 + (wave >> 1), c3 = wave & 1;  // block (r3, c3) of the lower-left 32 x 32
-    {  // X_rc = A_r0 T_0c + A_r1 T_1c
-        f4 x = blk16(Tm, 16 * r3, 16, Tm, 16, 16 * c3, f4{0.f, 0.f, 0.f, 0.f}, lane);
-        if (c3 == 0) x = blk16(Tm, 16 * r3, 0, Tm, 0, 0, x, lane);
-        park(x);
-    }
-    lds_barrier();
-    {  // T_2c = -T_22 X_2c ;  T_3c = -(T_32 X_2c + T_33 X_3c)  (X_2c parked by wave c, X_3c by wave 2 + c)
-        f4 acc = blk16s(Tm, 16 * r3, 32, scr_all + c3 * 256, f4{0.f, 0.f, 0.f, 0.f});
-        if (r3 == 3) acc = blk16s(Tm, 48, 48, scr, acc);
-        put_neg(16 * r3, 16 * c3, acc);
-    }
-    lds_barrier();
+        lds_barrier();
+        {  // T_2c = -T_22 X_2c ;  T_3c = -(T_32 X_2c + T_33 X_3c)  (X_2c parked by wave c, X_3c by wave 2 + c)
+            f4 acc = blk16s(Tm, 16 * r3, 32, scr_all + c3 * 256, f4{0.f, 0.f, 0.f, 0.f});
+            if (r3 == 3) acc = blk16s(Tm, 48, 48, scr, acc);
+            put_neg(16 * r3, 16 * c3, acc);
+        }
+        lds_barrier();
 
-    // ---- T, P and the gates for the scan (T and P as Mat images)
-    {
-        using MT = Mat<F32, C, C>;
-        const size_t ch = (size_t)c * a.n_vh + h;
-        float *tdst = a.ws + w.t + ch * C * C;
-        float *pdst = a.ws + w.p + ch * C * C;
-        for (int g = tid; g < C * C / 8; g += kPThreads) {
-            const int r = g / (C / 8), c0 = (g % (C / 8)) * 8;
-            float x[8];
-            load8(Tm + r * kCP + c0, x);
-            MT::put8(tdst, r, c0, x);
-            load8(Pm + r * kCP + c0, x);
-            MT::put8(pdst, r, c0, x);
-        }
-        if (tid < C) {
-            float *g = a.ws + w.g + ch * kGateRec;
-            g[tid] = gam[tid];
-            g[C + tid] = bet[tid];
-            g[2 * C + tid] = dec[tid];
-            g[3 * C + tid] = 0.f;
+        // ---- T, P and the gates for the scan (T and P as Mat images)
+        {
+            using MT = Mat<F32, C, C>;
+            const size_t ch = (size_t)c * a.n_vh + h;
+            float *tdst = a.ws + w.t + ch * C * C;
+            float *pdst = a.ws + w.p + ch * C * C;
+            for (int g = tid; g < C * C / 8; g += kPThreads) {
+                const int r = g / (C / 8), c0 = (g % (C / 8)) * 8;
+                float x[8];
+                load8(Tm + r * kCP + c0, x);
+                MT::put8(tdst, r, c0, x);
+                load8(Pm + r * kCP + c0, x);
+                MT::put8(pdst, r, c0, x);
+            }
+            if (tid < C) {
+                float *g = a.ws + w.g + ch * kGateRec;
+                g[tid] = gam[tid];
+                g[C + tid] = bet[tid];
+                g[2 * C + tid] = dec[tid];
+                g[3 * C + tid] = 0.f;
+            }
         }
     }
 }
@@ -882,7 +897,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
     const int nchunks = (a.T + kChunk - 1) / kChunk;
     const size_t prep_lds = PrepLds<D>::total;
-    hipLaunchKernelGGL((prefill_prep_kernel<D, AB, QKN>), dim3(nchunks * a.n_vh), dim3(kPThreads), prep_lds, stream, a);
+    hipLaunchKernelGGL((prefill_prep_kernel<D, AB, QKN>), dim3(nchunks * a.n_kh), dim3(kPThreads), prep_lds, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, !AB>), dim3(a.n_vh * (D / kDB)), dim3(kScanThreads), ScanLds<D>::total,
                        stream, a);
