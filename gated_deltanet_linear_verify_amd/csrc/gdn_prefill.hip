@@ -320,20 +320,24 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     const act_t *qkv = static_cast<const act_t *>(a.qkv);
     auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
-    // raw channels lc .. lc+3 of token t0 + t, -3 <= t < Lc (callers clamp t past the chunk); before
-    // the first chunk the three rows come from the conv state
-    auto ld4 = [&](int t, int lc) -> f4 {
-        if (c == 0 && t < 0)
-            return *reinterpret_cast<const f4 *>(a.conv_state + ((size_t)a.slot * 3 + 3 + t) * Cc + gchan(lc));
-        const size_t off = ((size_t)t0 + t) * Cc + gchan(lc);
-        if constexpr (ACT_BF16) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(qkv + off);
+    // Rows are loaded raw (every load of a conv issued before any is used) and converted after:
+    // channels lc .. lc+3 of token t0 + t; before the first chunk the three rows at t < 0 come
+    // from the conv state (fp32) instead.
+    using raw4 = typename std::conditional<ACT_BF16, uint2, f4>::type;
+    auto ld_raw = [&](int t, int lc) -> raw4 {
+        return *reinterpret_cast<const raw4 *>(qkv + ((size_t)t0 + t) * Cc + gchan(lc));
+    };
+    auto cvt = [](raw4 u) -> f4 {
+        if constexpr (ACT_BF16)
             return f4{bf16_to_f32((uint16_t)(u.x & 0xffffu)), bf16_to_f32((uint16_t)(u.x >> 16)),
                       bf16_to_f32((uint16_t)(u.y & 0xffffu)), bf16_to_f32((uint16_t)(u.y >> 16))};
-        } else {
-            return *reinterpret_cast<const f4 *>(qkv + off);
-        }
+        else
+            return u;
     };
+    auto hist4 = [&](int t, int lc) -> f4 {  // -3 <= t < 0, first chunk only
+        return *reinterpret_cast<const f4 *>(a.conv_state + ((size_t)a.slot * 3 + 3 + t) * Cc + gchan(lc));
+    };
+    const int tmin = c == 0 ? 0 : -3;  // lowest row of qkv a conv may read
 
     // gates of value head h: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
     auto gates = [&](int h) {
@@ -367,9 +371,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         f4 wv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + e) * 4);
+        raw4 rw[TPT + 3];
+#pragma unroll
+        for (int i = 0; i < TPT + 3; ++i) rw[i] = ld_raw(min(max(tb - 3 + i, tmin), Lc - 1), lc);
+        const bool head_rows = c == 0 && tb == 0;  // this thread's first three rows precede the call
+        f4 hs[3] = {};
+        if (head_rows)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) hs[i] = hist4(i - 3, lc);
         f4 xs[TPT + 3];
 #pragma unroll
-        for (int i = 0; i < TPT + 3; ++i) xs[i] = ld4(min(tb - 3 + i, Lc - 1), lc);
+        for (int i = 0; i < TPT + 3; ++i) xs[i] = (i < 3 && head_rows) ? hs[i < 3 ? i : 0] : cvt(rw[i]);
         float *vdst = a.ws + w.v + (((size_t)c * a.n_vh + h) * NB + vg / 4) * C * kDB + 4 * (vg % 4);
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
@@ -395,9 +407,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         f4 wqk[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) wqk[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + j) * 4);
+        raw4 rw[19];
+#pragma unroll
+        for (int i = 0; i < 19; ++i) rw[i] = ld_raw(min(max(16 * wave - 3 + i, tmin), Lc - 1), lc);
+        const bool head_rows = c == 0 && wave == 0;  // the wave's first three rows precede the call
+        f4 hs[3] = {};
+        if (head_rows)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) hs[i] = hist4(i - 3, lc);
         f4 xs[19];
 #pragma unroll
-        for (int i = 0; i < 19; ++i) xs[i] = ld4(min(16 * wave - 3 + i, Lc - 1), lc);
+        for (int i = 0; i < 19; ++i) xs[i] = (i < 3 && head_rows) ? hs[i < 3 ? i : 0] : cvt(rw[i]);
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
             const int t = 16 * wave + tt;
