@@ -106,9 +106,10 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         else
             return x;
     };
-    // a malformed parent (outside [-1, i)) is treated as -1: the node starts from the committed state
+    // a malformed parent (outside [-1, i)) is treated as -1: the node starts from the committed state.
+    // Parents are read from LDS (slot 3 of each node's ancestor record), filled once at staging.
     auto parent_of = [&](int i) -> int {
-        const int p = par[i];
+        const int p = anc[i * 4 + 3];
         return (p >= -1 && p < i) ? p : -1;
     };
 
@@ -131,12 +132,17 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
             for (int r = 0; r < 3; ++r) csv[j][r] = cs_s[(uint32_t)(r * C + gc)];
         }
     }
-    float al = 0.f, be = 0.f;
-    if (tid < T) {
-        const size_t tok = ((size_t)b * T + tid) * a.n_vh + h;
-        al = load_act<ACT_BF16>(a.alpha, tok);
-        be = load_act<ACT_BF16>(a.beta, tok);
-    }
+    // alpha, beta and the parent of node tid.  The loads sit outside any branch (threads past T load
+    // node T-1's) and nothing is computed from them before the wait below: a bf16 conversion, or a
+    // branch join over a loaded register, would make the compiler wait for every load issued so
+    // far before the state loads start.
+    using word_t = typename std::conditional<ACT_BF16, uint16_t, uint32_t>::type;  // bf16 or fp32 bits
+    const int node = min(tid, T - 1);
+    const size_t tok = ((size_t)b * T + node) * a.n_vh + h;
+    uint32_t al_raw = static_cast<const word_t *>(a.alpha)[tok];
+    uint32_t be_raw = static_cast<const word_t *>(a.beta)[tok];
+    int par_raw = par[node];
+    float alog = a.A_log[h], dtb = a.dt_bias[h];
     // the committed state: kept in registers for the whole launch (restart point)
     float R0[G::RPL][G::CPL];
     const int wih = wave;
@@ -150,6 +156,21 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
 #pragma unroll
             for (int e = 0; e < 4; ++e) R0[i][4 * c4 + e] = v[e];
         }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): raw rows landed, registers loaded
+    asm volatile("" : "+v"(al_raw), "+v"(be_raw), "+v"(par_raw), "+v"(alog), "+v"(dtb));  // nothing above
+    auto word_f32 = [](uint32_t w) -> float {
+        if constexpr (ACT_BF16)
+            return bf16_to_f32((uint16_t)w);
+        else
+            return __builtin_bit_cast(float, w);
+    };
+    if (tid < T) {
+        const float g = -expf(alog) * softplus_f(word_f32(al_raw) + dtb);
+        rbk[tid * 4 + 0] = expf(g);
+        rbk[tid * 4 + 1] = word_f32(be_raw);
+        anc[tid * 4 + 3] = par_raw;
+    }
+    __syncthreads();
     // ancestors 1..3 of every node (its conv window); where the root path ends, the slot's conv
     // state rows fill in: with L path nodes inside the window, ancestor j > L-1 is conv row 2-(j-L)
     if (tid < T) {
@@ -167,11 +188,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         anc[tid * 4 + 0] = code[0];
         anc[tid * 4 + 1] = code[1];
         anc[tid * 4 + 2] = code[2];
-        const float g = -expf(a.A_log[h]) * softplus_f(al + a.dt_bias[h]);
-        rbk[tid * 4 + 0] = expf(g);
-        rbk[tid * 4 + 1] = be;
     }
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): raw rows landed, registers loaded
     __syncthreads();
 
     // ================= conv of every node (one thread per channel) + conv-state capture =========

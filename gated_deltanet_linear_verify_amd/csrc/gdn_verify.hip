@@ -126,14 +126,18 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
         const int e0 = it * VEC, t = e0 / (R * D), within = e0 % (R * D);
         lds_dma16(z_b + (uint32_t)(t * a.n_vh * D + within), zs + e0);
     }
-    // alpha and beta: at most one (token, head) per thread
-    float al = 0.f, be = 0.f;
-    if (tid < nt * R) {
-        const int t = tid / R, hh = tid % R;
-        const size_t tok = ((size_t)b * T + t0 + t) * a.n_vh + hk * R + hh;
-        al = load_act<ACT_BF16>(a.alpha, tok);
-        be = load_act<ACT_BF16>(a.beta, tok);
-    }
+    // alpha and beta: at most one (token, head) per thread, with the head's A_log and dt_bias.  The
+    // loads sit outside any branch (threads past nt * R load a valid entry they never use) and
+    // nothing is computed from them before the wait below: a bf16 conversion, or a branch join
+    // over a loaded register, would make the compiler wait for every load issued so far, the qkv
+    // and z transfers included, before the state loads even start.
+    const int ab_i = min(tid, nt * R - 1);
+    const int ab_h = hk * R + ab_i % R;
+    const size_t ab_tok = ((size_t)b * T + t0 + ab_i / R) * a.n_vh + ab_h;
+    using word_t = typename std::conditional<ACT_BF16, uint16_t, uint32_t>::type;  // bf16 or fp32 bits
+    uint32_t al_raw = static_cast<const word_t *>(a.alpha)[ab_tok];
+    uint32_t be_raw = static_cast<const word_t *>(a.beta)[ab_tok];
+    float alog = a.A_log[ab_h], dtb = a.dt_bias[ab_h];
     // conv taps and the slot's conv state (xext rows 0..2 of the launch) of this thread's channels
     f4 wv[2];
     float csv[2][3];
@@ -159,15 +163,21 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[i][4 * c4 + e] = v[e];
         }
-    float nw = 0.f;
-    if (tid < D) nw = a.norm_w[tid];
+    float nw = a.norm_w[min(tid, D - 1)];
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): registers loaded, LDS rows landed
+    asm volatile("" : "+v"(al_raw), "+v"(be_raw), "+v"(alog), "+v"(dtb), "+v"(nw));  // nothing above
+    auto word_f32 = [](uint32_t w) -> float {
+        if constexpr (ACT_BF16)
+            return bf16_to_f32((uint16_t)w);
+        else
+            return __builtin_bit_cast(float, w);
+    };
     if (tid < D) nws[tid] = nw;
     if (tid < nt * R) {
-        const int t = tid / R, hh = tid % R, h2 = hk * R + hh;
-        const float g = -expf(a.A_log[h2]) * softplus_f(al + a.dt_bias[h2]);
+        const int t = tid / R, hh = tid % R;
+        const float g = -expf(alog) * softplus_f(word_f32(al_raw) + dtb);
         rb[(hh * TT + t) * 2 + 0] = expf(g);
-        rb[(hh * TT + t) * 2 + 1] = be;
+        rb[(hh * TT + t) * 2 + 1] = word_f32(be_raw);
     }
     __syncthreads();
 
