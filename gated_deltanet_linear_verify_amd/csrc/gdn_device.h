@@ -60,6 +60,22 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// A 16-byte store for write-once streams that no later kernel re-reads soon: global_store_dwordx4
+// with the nontemporal and system-scope (sc1) cache-policy bits.  Measured on MI355X, plain stores
+// of the 2 GiB verify capture, or of the state a rollback copies, leave dirty lines in L2 and the
+// Infinity Cache that the next kernel pays to write back; nt alone keeps that cost off the next
+// kernel, and sc1 with it streams faster still.  The compiler does not see this store in its
+// memory-counter bookkeeping, so use it only where no later wait in the kernel depends on it.
+__device__ __forceinline__ void store_stream(void *p, f4 v)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt" : : "v"(p), "v"(v) : "memory");
+#else
+    (void)p;
+    (void)v;
+#endif
+}
+
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4).  The LDS address must be
 // the same for the whole wave up to lane * 16: lane i lands at lds + 16 i of the first active lane.
 // Tracked by the vector-memory counter like any load.  The builtin exists only for the device

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
 #pragma unroll
                 for (int c4 = 0; c4 < G::NC4; ++c4) {
                     const f4 v = {S[i][4 * c4], S[i][4 * c4 + 1], S[i][4 * c4 + 2], S[i][4 * c4 + 3]};
-                    __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(cp + (size_t)(4 * i) * D + 64 * c4));
+                    store_stream(cp + (size_t)(4 * i) * D + 64 * c4, v);
                 }
         }
     }

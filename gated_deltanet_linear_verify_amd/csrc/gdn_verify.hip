@@ -33,10 +33,9 @@
 
 namespace gdn {
 
-// Capture stores are nontemporal: plain stores leave ~2 GB of dirty lines in L2 / Infinity Cache
-// that the next kernel (the rollback) pays to write back; measured on MI355X, the verify +
-// rollback step is faster with nt stores.
-__device__ __forceinline__ void store_cap(float *p, f4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(p)); }
+// Capture stores stream past the caches (store_stream): the 2 GiB capture is written once and only
+// the rollback's few positions are read back.
+__device__ __forceinline__ void store_cap(float *p, f4 v) { store_stream(p, v); }
 
 // Occupancy cap: about 8 waves per CU.  The capture stream writes faster with fewer concurrent
 // write streams per CU (measured: ~5.9 vs ~5.6 TB/s for the bare store pattern), and 2 waves per
