@@ -220,3 +220,29 @@ def digest(inputs: dict, extra: Optional[dict] = None) -> str:
     if extra:
         h.update(repr(sorted(extra.items())).encode())
     return h.hexdigest()
+
+
+# Width of the pages' model (TargetWeights n_embd), the input of the GDN block's projections.
+HIDDEN = 5120
+
+
+def make_block_inputs(shape: Shape, hidden: int, seed: int = 0) -> dict:
+    """Inputs of one GDN block call: make_inputs' layer inputs (state, conv state, gate and norm
+    parameters, conv taps, slots; its qkv / z / alpha / beta are replaced by the block's own
+    projections) plus x [B][T][hidden] ~ N(0, 1) and random projection weights, one output
+    feature per row with the input index fastest: w_qkv [C][hidden], w_z [H_v d_v][hidden],
+    w_beta and w_alpha [H_v][hidden], each ~ N(0, 1/hidden), and w_out [hidden][H_v d_v] ~
+    N(0, 1/(H_v d_v)).  All bf16-rounded (fp32 arrays holding bf16 values)."""
+    inp = make_inputs(shape, seed)
+    for k in ("qkv", "z", "alpha", "beta"):
+        del inp[k]
+    rng = np.random.default_rng(seed + 7919)
+    B, T, Hv, dv, C = shape.n_batch, shape.n_tok, shape.n_vh, shape.d_v, shape.conv_channels
+    s_in, s_out = 1.0 / np.sqrt(hidden), 1.0 / np.sqrt(Hv * dv)
+    inp["x"] = round_to(rng.standard_normal((B, T, hidden)), BF16)
+    inp["w_qkv"] = round_to(rng.normal(0.0, s_in, (C, hidden)), BF16)
+    inp["w_z"] = round_to(rng.normal(0.0, s_in, (Hv * dv, hidden)), BF16)
+    inp["w_beta"] = round_to(rng.normal(0.0, s_in, (Hv, hidden)), BF16)
+    inp["w_alpha"] = round_to(rng.normal(0.0, s_in, (Hv, hidden)), BF16)
+    inp["w_out"] = round_to(rng.normal(0.0, s_out, (hidden, Hv * dv)), BF16)
+    return inp

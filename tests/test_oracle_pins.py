@@ -420,3 +420,66 @@ def test_tree_rejects_malformed_parents():
     inp["parent"] = np.array([[-1, 0, 2, 1]] * shape.n_batch, dtype=np.int32)
     with pytest.raises(ValueError):
         ref.tree_units(shape, inp)
+
+
+# ---------------------------------------------------------------- the block's projections
+
+def test_linear_equals_integer_brute_force():
+    """x W^T on small integer matrices (exact in fp64) against a pure-Python triple loop; the
+    shapes are all different, so a transposed operand cannot pass."""
+    from oracle import block
+    rng = np.random.default_rng(3)
+    x = rng.integers(-9, 10, (3, 5))
+    w = rng.integers(-9, 10, (4, 5))
+    want = [[sum(int(x[m, k]) * int(w[n, k]) for k in range(5)) for n in range(4)] for m in range(3)]
+    assert np.array_equal(block.linear(x, w), np.array(want, dtype=np.float64))
+
+
+def test_linear_identity_and_sigmoid():
+    from scipy.special import expit
+    from oracle import block
+    w = np.arange(12.0).reshape(3, 4)
+    assert np.array_equal(block.linear(np.eye(4), w), w.T)  # unit rows pick out the weights' columns
+    xs = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(block.sigmoid(xs), expit(xs), rtol=1e-15, atol=0)
+    assert block.sigmoid(np.array([0.0]))[0] == 0.5
+
+
+def test_bf16_rounding_against_torch():
+    """The oracle's own round-to-nearest-even bf16 against torch's conversion, ties included."""
+    import torch
+    from oracle import block
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(4096) * 10.0 ** rng.integers(-6, 6, 4096),
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0])])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(block.bf16(x), want.astype(np.float64))
+    assert block.bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0           # tie, to even
+    assert block.bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6  # tie, to even
+
+
+def test_block_composes_its_parts():
+    """With unit rows as x the projections return chosen columns of the weights, so the block
+    must equal the chain verify of those exact activations followed by the output projection."""
+    from oracle import block
+    shape = W.shape_with(TINY, act_dtype=W.BF16, out_dtype=W.BF16, n_tok=2, n_batch=1, n_pool=1)
+    B, T, Hv, dv, C = shape.n_batch, shape.n_tok, shape.n_vh, shape.d_v, shape.conv_channels
+    hidden = B * T
+    inp = W.make_block_inputs(shape, hidden, seed=5)
+    inp["x"] = np.eye(hidden).reshape(B, T, hidden)
+    plain = W.make_inputs(shape, 5)
+    # choose the weights so that the projections reproduce plain's activations
+    inp["w_qkv"] = plain["qkv"].reshape(hidden, C).T.astype(np.float64)
+    inp["w_z"] = plain["z"].reshape(hidden, Hv * dv).T.astype(np.float64)
+    inp["w_alpha"] = plain["alpha"].reshape(hidden, Hv).T.astype(np.float64)
+    logit = np.log(plain["beta"] / (1.0 - plain["beta"]))  # sigmoid(logit) = beta
+    inp["w_beta"] = logit.reshape(hidden, Hv).T
+    r = block.block_verify(shape, inp, flags=0)
+    want = ref.verify_pool(shape, plain, flags=0)
+    np.testing.assert_allclose(r["proj"]["beta"].reshape(plain["beta"].shape), plain["beta"], rtol=4e-3)
+    lay = dict(plain)
+    lay["beta"] = r["proj"]["beta"].reshape(plain["beta"].shape)
+    want = ref.verify_pool(shape, lay, flags=0)
+    assert np.array_equal(r["state"], want["state"])
+    y = block.linear(block.bf16(want["out"]).reshape(B, T, Hv * dv), inp["w_out"])
+    assert np.array_equal(r["y"], y)
