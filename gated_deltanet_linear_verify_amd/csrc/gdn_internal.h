@@ -81,6 +81,22 @@ struct SlotCopyArgs {
 };
 hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream);
 
+// Projections y = x W^T (bf16 in, fp32 accumulate): product columns [n0, n1) of segment s go to
+// seg[s].ptr[m * ld + n - n0], as bf16 or fp32, optionally through a sigmoid.
+constexpr int kMaxLinearSegs = 4;
+struct LinearSeg {
+    int32_t n0, ld, bf16, sigmoid;
+    void *ptr;
+};
+struct LinearArgs {
+    const uint16_t *x;  // [M][K] bf16
+    const uint16_t *w;  // [N][K] bf16
+    int32_t M, N, K;    // K a multiple of 64
+    int32_t n_segs;     // 1 .. kMaxLinearSegs, ascending n0, seg[0].n0 == 0
+    LinearSeg seg[kMaxLinearSegs];
+};
+hipError_t launch_linear(const LinearArgs &a, hipStream_t stream);
+
 // The C ABI's thread-local last error (gdn_last_error): set it and return code, or clear it and
 // return GDN_OK.
 int abi_fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -1,0 +1,140 @@
+// gdn_linear.hip - the GDN block's projections, y = x W^T, on MFMA (gfx950).
+//
+// lucebox-hub internal.h, struct TargetLayer: the block reads its activations through the fused
+// q / k / v projection (wqkv), the z projection (wqkv_gate) and the per-token beta and alpha
+// projections (ssm_beta, ssm_alpha), and writes its result through ssm_out.  Each is a product of
+// the token rows x [M][K] (bf16) with a weight W [N][K] (bf16, one output feature per row, input
+// index fastest), accumulated in fp32.  One launch may feed several destinations: the product's
+// columns are split into segments, each with its own pointer, row stride, storage type and an
+// optional sigmoid (beta is sigmoid(x W_beta^T)), so the four input projections are one GEMM over
+// the concatenated weight.
+//
+// Tiling: a workgroup computes a 128 x 128 block of y with 4 waves of 64 x 64 (4 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16).  K advances 64 at a time; the next x and W tiles travel into the other
+// half of a double-buffered LDS by global_load_lds while the current ones are multiplied.  Within
+// an LDS tile row (64 bf16 = 8 chunks of 16 bytes) chunk c of row r sits at position c ^ (r & 7),
+// so the 16 rows an operand load touches spread over the banks; the DMA writes LDS linearly, so
+// the swizzle is applied by choosing the global chunk each lane fetches.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kLBM = 128, kLBN = 128, kLBK = 64;  // workgroup tile
+constexpr int kLThreads = 256;
+constexpr int kLChunks = kLBK / 8;  // 16-byte chunks per tile row
+
+__device__ __forceinline__ f4 mfma_bf16(bf16x8_t a, bf16x8_t b, f4 c)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+#else
+    (void)a;
+    (void)b;
+    return c;
+#endif
+}
+
+// LDS byte offset of chunk c of tile row r (one tile: kLBM rows x kLChunks chunks)
+__device__ __forceinline__ int lchunk(int r, int c) { return (r * kLChunks + (c ^ (r & 7))) * 16; }
+
+__global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][kLBM * kLBK * 2];  // [buffer][x, W]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;  // the wave's 64 x 64 quadrant
+    const int m0 = blockIdx.y * kLBM, n0 = blockIdx.x * kLBN;
+    const int K = a.K;
+    const uint16_t *x = a.x, *w = a.w;
+
+    // this thread's 4 + 4 transfers of a k tile: LDS position p = tid + 256 i (row p / 8, slot
+    // p % 8) holds chunk slot ^ (row & 7) of that row; rows past M or N re-read the last row
+    // (their results are never stored), so every thread issues the same 8 transfers
+    const uint16_t *xsrc[4], *wsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = tid + kLThreads * i, r = p / kLChunks, c = (p % kLChunks) ^ (r & 7);
+        xsrc[i] = x + (size_t)min(m0 + r, a.M - 1) * K + 8 * c;
+        wsrc[i] = w + (size_t)min(n0 + r, a.N - 1) * K + 8 * c;
+    }
+    auto issue = [&](int kt, int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(xsrc[i] + kt * kLBK, lds[buf][0] + (tid + kLThreads * i) * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(wsrc[i] + kt * kLBK, lds[buf][1] + (tid + kLThreads * i) * 16);
+    };
+
+    f4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / kLBK;
+    issue(0, 0);
+#pragma unroll 1
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) {
+            issue(kt + 1, buf ^ 1);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | 8);  // vmcnt(8): all but the next tile's 8 transfers
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        lds_barrier();
+        const unsigned char *xs = lds[buf][0], *ws = lds[buf][1];
+#pragma unroll
+        for (int ks = 0; ks < kLBK / 32; ++ks) {
+            const int c = 4 * ks + lg;  // this lane's chunk of the 32-deep step
+            bf16x8_t af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(xs + lchunk(64 * wm + 16 * i + li, c));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const bf16x8_t *>(ws + lchunk(64 * wn + 16 * j + li, c));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
+        }
+        lds_barrier();  // every wave is done with this buffer before the transfer two tiles on
+    }
+
+    // ---- epilogue: element (row 4 lg + r, column li) of each 16 x 16 tile to its segment
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + 64 * wn + 16 * j + li;
+        if (n >= a.N) continue;
+        int sgi = 0;
+#pragma unroll
+        for (int q = 1; q < kMaxLinearSegs; ++q)
+            if (q < a.n_segs && n >= a.seg[q].n0) sgi = q;
+        const LinearSeg &sg = a.seg[sgi];
+        const int nc = n - sg.n0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
+                if (m >= a.M) continue;
+                float v = acc[i][j][r];
+                if (sg.sigmoid) v = 1.0f / (1.0f + expf(-v));
+                const size_t at = (size_t)m * sg.ld + nc;
+                if (sg.bf16)
+                    static_cast<uint16_t *>(sg.ptr)[at] = f32_to_bf16(v);
+                else
+                    static_cast<float *>(sg.ptr)[at] = v;
+            }
+    }
+}
+
+hipError_t launch_linear(const LinearArgs &a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((a.N + kLBN - 1) / kLBN), (unsigned)((a.M + kLBM - 1) / kLBM));
+    hipLaunchKernelGGL(linear_kernel, grid, dim3(kLThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -128,3 +128,36 @@ def layers_graph(layers: list, slot_ids, accepted_idx,
     """The same step recorded once (gdn_graph_create) over the uploaded layers' buffers."""
     B, T = layers[0]["qkv"].shape[0], layers[0]["qkv"].shape[1]
     return gdn.Graph(layers[0]["dims"], layers, layers[0]["capture"].t_cap, T, slot_ids, B, accepted_idx, phases)
+
+
+def upload_block(shape: Shape, inp: dict, *, flags: int = gdn.GDN_F_QK_NORM_SILU) -> dict:
+    """Device tensors of one GDN block call (workloads.make_block_inputs): the layer's buffers as
+    upload() makes them (qkv, z, alpha, beta become outputs of the input projection), plus
+    x [B*T][hidden], the concatenated input weight [C + H_v d_v + 2 H_v][hidden], w_out and
+    y [B][T][hidden] (bf16)."""
+    B, T, Hv, dv, C = shape.n_batch, shape.n_tok, shape.n_vh, shape.d_v, shape.conv_channels
+    hidden = inp["x"].shape[-1]
+    lay = dict(inp)
+    lay.update(qkv=np.zeros((B, T, C), np.float32), z=np.zeros((B, T, Hv, dv), np.float32),
+               alpha=np.zeros((B, T, Hv), np.float32), beta=np.zeros((B, T, Hv), np.float32))
+    d = upload(shape, lay, flags=flags)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16).contiguous()
+    d["x"] = bf(inp["x"].reshape(B * T, hidden))
+    d["w_in"] = bf(np.concatenate([inp["w_qkv"], inp["w_z"], inp["w_beta"], inp["w_alpha"]], axis=0))
+    d["w_out"] = bf(inp["w_out"])
+    d["y"] = torch.empty((B, T, hidden), dtype=torch.bfloat16, device="cuda")
+    d["hidden"] = hidden
+    return d
+
+
+def block_step(d: dict, stream=None) -> None:
+    """One GDN block call: the four input projections as one gdn_linear (beta through a sigmoid),
+    gdn_verify with capture over every token, the output projection of the gated output."""
+    B, T, C = d["qkv"].shape
+    Hv, dv = d["z"].shape[2], d["z"].shape[3]
+    Z, hidden, M = Hv * dv, d["hidden"], B * T
+    segs = [(0, C, d["qkv"], C, 0), (C, C + Z, d["z"], Z, 0),
+            (C + Z, C + Z + Hv, d["beta"], Hv, 1), (C + Z + Hv, C + Z + 2 * Hv, d["alpha"], Hv, 0)]
+    gdn.gdn_linear(d["x"], d["w_in"], M, C + Z + 2 * Hv, hidden, segs, stream)
+    verify(d, stream=stream)
+    gdn.gdn_linear(d["out"], d["w_out"], M, hidden, Z, [(0, hidden, d["y"], hidden, 0)], stream)

@@ -23,7 +23,7 @@ GDN_F_CHECK_INDICES = 0x2
 EXPORTS = ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch", "gdn_rollback_trim",
            "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_capture_bytes", "gdn_reset",
            "gdn_snapshot", "gdn_restore", "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch",
-           "gdn_graph_destroy", "gdn_last_error", "gdn_version")
+           "gdn_graph_destroy", "gdn_linear", "gdn_last_error", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -48,6 +48,11 @@ class gdn_capture(ctypes.Structure):
 class gdn_layer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("state", "conv_state", "qkv", "z", "alpha", "beta", "A_log",
                                                 "dt_bias", "conv_w", "norm_w", "cap_ssm", "cap_conv", "out")]
+
+
+class gdn_out_seg(ctypes.Structure):
+    _fields_ = [("n0", ctypes.c_int32), ("n1", ctypes.c_int32), ("ld", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("sigmoid", ctypes.c_int32), ("ptr", ctypes.c_void_p)]
 
 
 GDN_GRAPH_VERIFY = 0x1
@@ -84,10 +89,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_graph_create.argtypes = [D, ctypes.POINTER(gdn_layer), I, I, I, P, I, P, ctypes.c_uint32,
                                        ctypes.POINTER(ctypes.c_void_p)]
         L.gdn_graph_launch.argtypes = [P, P]
+        L.gdn_linear.argtypes = [P, P, I, I, I, ctypes.POINTER(gdn_out_seg), I, P]
         L.gdn_graph_destroy.argtypes = [P]
         for f in ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch",
                   "gdn_rollback_trim", "gdn_prefill", "gdn_reset", "gdn_snapshot", "gdn_restore",
-                  "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch", "gdn_graph_destroy"):
+                  "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch", "gdn_graph_destroy",
+                  "gdn_linear"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_version.restype = ctypes.c_char_p
@@ -176,6 +183,16 @@ def gdn_rollback_layers(layers, slots, accepted_idx, n: int, stream=None) -> Non
     """One launch (per 64 layers) restoring every layer's capture for the listed slots."""
     arr = (gdn_capture * len(layers))(*[c.c for c in layers])
     _check(lib().gdn_rollback_layers(arr, len(layers), _p(slots), _p(accepted_idx), n, _stream(stream)))
+
+
+def gdn_linear(x, w, M: int, N: int, K: int, segs, stream=None) -> None:
+    """y = x W^T into column segments: segs is a list of (n0, n1, tensor, ld, sigmoid) with the
+    tensor's dtype (bf16 or fp32) as the storage type."""
+    import torch
+    arr = (gdn_out_seg * len(segs))(*[
+        gdn_out_seg(n0, n1, ld, GDN_BF16 if t.dtype == torch.bfloat16 else GDN_F32, int(bool(sg)), _p(t))
+        for (n0, n1, t, ld, sg) in segs])
+    _check(lib().gdn_linear(_p(x), _p(w), M, N, K, arr, len(segs), _stream(stream)))
 
 
 class Graph:

@@ -282,6 +282,31 @@ int gdn_graph_launch(const gdn_graph *graph, void *stream);
 /* Free the graph (NULL is a no-op).  Pending replays finish first. */
 int gdn_graph_destroy(gdn_graph *graph);
 
+/*
+ * The GDN block's projections on MFMA: y = x W^T with x [M][K] and W [N][K] bf16 (row-major; W
+ * holds one output feature per row, input index fastest), fp32 accumulation.  lucebox-hub
+ * internal.h, struct TargetLayer: wqkv (fused q / k / v), wqkv_gate (z), ssm_beta, ssm_alpha
+ * (per-token projections) and ssm_out (output projection); the four input projections are one
+ * call over their concatenated weights, split by gdn_out_seg.
+ *
+ * segs[0 .. n_segs) cut the product's columns into consecutive ranges [n0, n1) (segs[0].n0 = 0,
+ * each n0 the previous n1, the last n1 = N); column n of segment s, row m, is stored at
+ * ptr[m * ld + (n - n0)] as dtype (GDN_BF16, round to nearest even, or GDN_F32), through
+ * 1 / (1 + e^-v) when sigmoid is nonzero.  Errors: NULL or misaligned x / W (16 bytes) or a NULL
+ * ptr -> GDN_ERR_ARG; M, N < 1 or K not a positive multiple of 64 -> GDN_ERR_SHAPE; n_segs
+ * outside [1, 4], ranges that do not tile [0, N), ld < n1 - n0 -> GDN_ERR_ARG; bad dtype ->
+ * GDN_ERR_DTYPE.
+ */
+typedef struct gdn_out_seg {
+    int32_t n0, n1; /* product columns [n0, n1) */
+    int32_t ld;     /* destination row stride in elements (>= n1 - n0) */
+    int32_t dtype;  /* GDN_BF16 or GDN_F32 */
+    int32_t sigmoid;
+    void *ptr;
+} gdn_out_seg;
+int gdn_linear(const void *x, const void *w, int32_t M, int32_t N, int32_t K, const gdn_out_seg *segs,
+               int32_t n_segs, void *stream);
+
 /* Thread-local description of the last error of this thread ("" after success). */
 const char *gdn_last_error(void);
 

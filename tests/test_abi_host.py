@@ -223,3 +223,31 @@ def test_graph_validation():
     assert h.value is None
     assert L.gdn_graph_launch(None, None) == gdn.GDN_ERR_ARG
     assert L.gdn_graph_destroy(None) == gdn.GDN_OK
+
+
+def test_linear_validation():
+    """gdn_linear checks pointers, shapes and the column segments before any launch."""
+    L = _lib_or_skip()
+
+    def segs(*spec):
+        return (gdn.gdn_out_seg * len(spec))(*[gdn.gdn_out_seg(n0, n1, ld, dt, sg, 0x2000)
+                                                for (n0, n1, ld, dt, sg) in spec])
+
+    good = segs((0, 100, 100, gdn.GDN_BF16, 0), (100, 164, 64, gdn.GDN_F32, 1))
+
+    def call(x=FAKE, w=FAKE, M=8, N=164, K=128, s=good, n=2):
+        return L.gdn_linear(x, w, M, N, K, s, n, None)
+
+    assert call(x=None) == gdn.GDN_ERR_ARG
+    assert call(w=ctypes.c_void_p(0x1008)) == gdn.GDN_ERR_ARG
+    assert call(M=0) == gdn.GDN_ERR_SHAPE
+    assert call(K=96) == gdn.GDN_ERR_SHAPE
+    assert call(K=0) == gdn.GDN_ERR_SHAPE
+    assert call(n=0) == gdn.GDN_ERR_ARG
+    assert call(n=5) == gdn.GDN_ERR_ARG
+    assert call(N=200) == gdn.GDN_ERR_ARG                      # segments end short of N
+    assert call(s=segs((0, 100, 100, 1, 0), (90, 164, 74, 0, 0))) == gdn.GDN_ERR_ARG   # overlap
+    assert call(s=segs((0, 100, 99, 1, 0), (100, 164, 64, 0, 0))) == gdn.GDN_ERR_ARG   # ld too small
+    assert call(s=segs((0, 100, 100, 7, 0), (100, 164, 64, 0, 0))) == gdn.GDN_ERR_DTYPE
+    bad_ptr = (gdn.gdn_out_seg * 1)(gdn.gdn_out_seg(0, 164, 164, 1, 0, None))
+    assert call(s=bad_ptr, n=1) == gdn.GDN_ERR_ARG
