@@ -182,6 +182,30 @@ def components(args) -> dict:
                                  "one_slot_us_launch_per_layer": us_per_layer_1}
     del caps
     torch.cuda.empty_cache()
+    # the whole GDN block: input projections (one gdn_linear), verify with capture, output
+    # projection, at the model's width of 5120; 64 slots and 1 slot of 16 drafted tokens
+    for name, nb in (("gdn_block_64_slots", 64), ("gdn_block_1_slot", 1)):
+        s = W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=nb, n_batch=nb)
+        d = device.upload_block(s, W.make_block_inputs(s, W.HIDDEN, seed=3))
+        M, C, Z, Hv = nb * s.n_tok, s.conv_channels, s.n_vh * s.d_v, s.n_vh
+        n_in = C + Z + 2 * Hv
+        segs = [(0, C, d["qkv"], C, 0), (C, C + Z, d["z"], Z, 0),
+                (C + Z, C + Z + Hv, d["beta"], Hv, 1), (C + Z + Hv, n_in, d["alpha"], Hv, 0)]
+        us_in = time_launches(lambda: gdn.gdn_linear(d["x"], d["w_in"], M, n_in, W.HIDDEN, segs), 20)
+        us_ver = time_launches(lambda: device.verify(d), 20)
+        us_out = time_launches(lambda: gdn.gdn_linear(d["out"], d["w_out"], M, W.HIDDEN, Z,
+                                                      [(0, W.HIDDEN, d["y"], W.HIDDEN, 0)]), 20)
+        us_all = time_launches(lambda: device.block_step(d), 20)
+        f_in, f_out = 2.0 * M * n_in * W.HIDDEN, 2.0 * M * W.HIDDEN * Z
+        out[name] = {
+            "workload": f"{nb} slot(s) x 16 tokens, width 5120 -> qkv|z|beta|alpha ({n_in}) -> verify -> 5120",
+            "us_block": us_all, "us_in_proj": us_in, "us_verify": us_ver, "us_out_proj": us_out,
+            "tokens_per_s": M / (us_all * 1e-6),
+            "in_proj_tflops": f_in / (us_in * 1e-6) / 1e12, "out_proj_tflops": f_out / (us_out * 1e-6) / 1e12,
+            "in_proj_mfma_util_vs_bf16_peak": f_in / (us_in * 1e-6) / PEAK_BF16_FLOPS,
+            "out_proj_mfma_util_vs_bf16_peak": f_out / (us_out * 1e-6) / PEAK_BF16_FLOPS}
+        del d
+    torch.cuda.empty_cache()
     # chunked prefill: one 8192-token sequence
     s = W.CHUNKED_PREFILL
     d = device.upload(s, W.make_inputs(s, 0), capture=False)

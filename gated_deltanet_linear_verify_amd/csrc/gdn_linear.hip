@@ -9,9 +9,10 @@
 // optional sigmoid (beta is sigmoid(x W_beta^T)), so the four input projections are one GEMM over
 // the concatenated weight.
 //
-// Tiling: a workgroup computes a 128 x 128 block of y with 4 waves of 64 x 64 (4 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16).  K advances 64 at a time; the next x and W tiles travel into the other
-// half of a double-buffered LDS by global_load_lds while the current ones are multiplied.  Within
+// Tiling: a workgroup computes a block of y with 4 waves in 2 x 2, each a grid of 16 x 16 tiles of
+// v_mfma_f32_16x16x32_bf16 (128 x 128 blocks for many rows, 32 x 64 for few).  K advances 64 at a
+// time; the next x and W tiles travel into the other half of a double-buffered LDS by
+// global_load_lds while the current ones are multiplied.  Within
 // an LDS tile row (64 bf16 = 8 chunks of 16 bytes) chunk c of row r sits at position c ^ (r & 7),
 // so the 16 rows an operand load touches spread over the banks; the DMA writes LDS linearly, so
 // the swizzle is applied by choosing the global chunk each lane fetches.
@@ -22,7 +23,7 @@ namespace gdn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kLBM = 128, kLBN = 128, kLBK = 64;  // workgroup tile
+constexpr int kLBK = 64;  // k depth of a tile
 constexpr int kLThreads = 256;
 constexpr int kLChunks = kLBK / 8;  // 16-byte chunks per tile row
 
@@ -37,41 +38,59 @@ __device__ __forceinline__ f4 mfma_bf16(bf16x8_t a, bf16x8_t b, f4 c)
 #endif
 }
 
-// LDS byte offset of chunk c of tile row r (one tile: kLBM rows x kLChunks chunks)
+// LDS byte offset of chunk c of tile row r
 __device__ __forceinline__ int lchunk(int r, int c) { return (r * kLChunks + (c ^ (r & 7))) * 16; }
 
+// Workgroup tile (32 WM) x (32 WN): 4 waves in 2 x 2, each (16 WM) x (16 WN) = WM x WN MFMA tiles.
+template <int WM, int WN>
+struct LinTile {
+    static constexpr int BM = 32 * WM, BN = 32 * WN;
+    static constexpr int XT = BM * kLChunks / kLThreads;  // x transfers per thread and k tile
+    static constexpr int WT = BN * kLChunks / kLThreads;  // W transfers per thread and k tile
+    static constexpr size_t lds = 2 * (size_t)(BM + BN) * kLBK * 2;  // two buffers of x and W tiles
+    static_assert(XT >= 1 && WT >= 1 && XT + WT < 64, "tile transfer counts");
+};
+
+template <int WM, int WN>
 __global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][kLBM * kLBK * 2];  // [buffer][x, W]
+    using TL = LinTile<WM, WN>;
+    constexpr int BM = TL::BM, BN = TL::BN;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [buffer][x tile | W tile]
+    constexpr int XB = BM * kLBK * 2, BUF = (BM + BN) * kLBK * 2;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;  // the wave's 64 x 64 quadrant
-    const int m0 = blockIdx.y * kLBM, n0 = blockIdx.x * kLBN;
+    const int wm = wave >> 1, wn = wave & 1;  // the wave's quadrant
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int K = a.K;
-    const uint16_t *x = a.x, *w = a.w;
 
-    // this thread's 4 + 4 transfers of a k tile: LDS position p = tid + 256 i (row p / 8, slot
-    // p % 8) holds chunk slot ^ (row & 7) of that row; rows past M or N re-read the last row
-    // (their results are never stored), so every thread issues the same 8 transfers
-    const uint16_t *xsrc[4], *wsrc[4];
+    // this thread's transfers of a k tile: LDS position p = tid + 256 i (row p / 8, slot p % 8)
+    // holds chunk slot ^ (row & 7) of that row; rows past M or N re-read the last row (their
+    // results are never stored), so every thread issues the same number of transfers
+    const uint16_t *xsrc[TL::XT], *wsrc[TL::WT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TL::XT; ++i) {
         const int p = tid + kLThreads * i, r = p / kLChunks, c = (p % kLChunks) ^ (r & 7);
-        xsrc[i] = x + (size_t)min(m0 + r, a.M - 1) * K + 8 * c;
-        wsrc[i] = w + (size_t)min(n0 + r, a.N - 1) * K + 8 * c;
+        xsrc[i] = a.x + (size_t)min(m0 + r, a.M - 1) * K + 8 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < TL::WT; ++i) {
+        const int p = tid + kLThreads * i, r = p / kLChunks, c = (p % kLChunks) ^ (r & 7);
+        wsrc[i] = a.w + (size_t)min(n0 + r, a.N - 1) * K + 8 * c;
     }
     auto issue = [&](int kt, int buf) {
+        unsigned char *base = lds + buf * BUF;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(xsrc[i] + kt * kLBK, lds[buf][0] + (tid + kLThreads * i) * 16);
+        for (int i = 0; i < TL::XT; ++i) lds_dma16(xsrc[i] + kt * kLBK, base + (tid + kLThreads * i) * 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(wsrc[i] + kt * kLBK, lds[buf][1] + (tid + kLThreads * i) * 16);
+        for (int i = 0; i < TL::WT; ++i) lds_dma16(wsrc[i] + kt * kLBK, base + XB + (tid + kLThreads * i) * 16);
     };
 
-    f4 acc[4][4];
+    f4 acc[WM][WN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < WN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / kLBK;
     issue(0, 0);
@@ -80,32 +99,35 @@ __global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
         const int buf = kt & 1;
         if (kt + 1 < nk) {
             issue(kt + 1, buf ^ 1);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | 8);  // vmcnt(8): all but the next tile's 8 transfers
+            // all but the next tile's transfers (only loads are in flight: the wait is exact)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | ((TL::XT + TL::WT) & 0xF) | (((TL::XT + TL::WT) >> 4) << 14));
         } else {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         lds_barrier();
-        const unsigned char *xs = lds[buf][0], *ws = lds[buf][1];
+        const unsigned char *xs = lds + buf * BUF, *ws = xs + XB;
 #pragma unroll
         for (int ks = 0; ks < kLBK / 32; ++ks) {
             const int c = 4 * ks + lg;  // this lane's chunk of the 32-deep step
-            bf16x8_t af[4], bf[4];
+            bf16x8_t af[WM], bf[WN];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(xs + lchunk(64 * wm + 16 * i + li, c));
+            for (int i = 0; i < WM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t *>(xs + lchunk(16 * WM * wm + 16 * i + li, c));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const bf16x8_t *>(ws + lchunk(64 * wn + 16 * j + li, c));
+            for (int j = 0; j < WN; ++j)
+                bf[j] = *reinterpret_cast<const bf16x8_t *>(ws + lchunk(16 * WN * wn + 16 * j + li, c));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < WM; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < WN; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
         }
         lds_barrier();  // every wave is done with this buffer before the transfer two tiles on
     }
 
     // ---- epilogue: element (row 4 lg + r, column li) of each 16 x 16 tile to its segment
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 64 * wn + 16 * j + li;
+    for (int j = 0; j < WN; ++j) {
+        const int n = n0 + 16 * WN * wn + 16 * j + li;
         if (n >= a.N) continue;
         int sgi = 0;
 #pragma unroll
@@ -114,10 +136,10 @@ __global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
         const LinearSeg &sg = a.seg[sgi];
         const int nc = n - sg.n0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WM; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
+                const int m = m0 + 16 * WM * wm + 16 * i + 4 * lg + r;
                 if (m >= a.M) continue;
                 float v = acc[i][j][r];
                 if (sg.sigmoid) v = 1.0f / (1.0f + expf(-v));
@@ -130,11 +152,22 @@ __global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
     }
 }
 
+template <int WM, int WN>
+static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
+{
+    using TL = LinTile<WM, WN>;
+    const dim3 grid((unsigned)((a.N + TL::BN - 1) / TL::BN), (unsigned)((a.M + TL::BM - 1) / TL::BM));
+    hipLaunchKernelGGL((linear_kernel<WM, WN>), grid, dim3(kLThreads), TL::lds, stream, a);
+    return hipGetLastError();
+}
+
+// Tile by rows: many rows take 128 x 128 tiles (two workgroups per CU; 128 x 256 tiles measured
+// slower, at one wave per SIMD); a few rows (one slot's drafted tokens) take 32 x 64 tiles, so
+// the weight stream is spread over enough workgroups.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((a.N + kLBN - 1) / kLBN), (unsigned)((a.M + kLBM - 1) / kLBM));
-    hipLaunchKernelGGL(linear_kernel, grid, dim3(kLThreads), 0, stream, a);
-    return hipGetLastError();
+    if (a.M <= 64) return launch_tile<1, 2>(a, stream);
+    return launch_tile<4, 4>(a, stream);
 }
 
 }  // namespace gdn
