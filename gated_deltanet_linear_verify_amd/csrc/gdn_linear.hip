@@ -61,7 +61,13 @@ __global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;  // the wave's quadrant
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    // Tiles are numbered n-major, m fastest (t = n_tile * mt + m_tile), and workgroups are dealt
+    // to the 8 XCDs in turn; XCD x takes the contiguous tile range [x T/8, (x+1) T/8), so the
+    // workgroups sharing a weight tile run on one XCD, one after another, and read it from that
+    // XCD's L2 instead of once per XCD.
+    const int mt = (a.M + BM - 1) / BM, ntiles = gridDim.x;
+    const int t = ntiles % 8 == 0 ? (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int m0 = (t % mt) * BM, n0 = (t / mt) * BN;
     const int K = a.K;
 
     // this thread's transfers of a k tile: LDS position p = tid + 256 i (row p / 8, slot p % 8)
@@ -156,7 +162,8 @@ template <int WM, int WN>
 static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
 {
     using TL = LinTile<WM, WN>;
-    const dim3 grid((unsigned)((a.N + TL::BN - 1) / TL::BN), (unsigned)((a.M + TL::BM - 1) / TL::BM));
+    const unsigned tiles = (unsigned)((a.N + TL::BN - 1) / TL::BN) * (unsigned)((a.M + TL::BM - 1) / TL::BM);
+    const dim3 grid(tiles);
     hipLaunchKernelGGL((linear_kernel<WM, WN>), grid, dim3(kLThreads), TL::lds, stream, a);
     return hipGetLastError();
 }
