@@ -9,7 +9,7 @@
 // optional sigmoid (beta is sigmoid(x W_beta^T)), so the four input projections are one GEMM over
 // the concatenated weight.
 //
-// Tiling: a workgroup computes a block of y with 4 waves in 2 x 2, each a grid of 16 x 16 tiles of
+// Tiling: a workgroup computes a block of y with a grid of waves, each a grid of 16 x 16 tiles of
 // v_mfma_f32_16x16x32_bf16 (128 x 128 blocks for many rows, 32 x 64 for few).  K advances 64 at a
 // time; the next x and W tiles travel into the other half of a double-buffered LDS by
 // global_load_lds while the current ones are multiplied.  Within
@@ -24,7 +24,6 @@ namespace gdn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kLBK = 64;  // k depth of a tile
-constexpr int kLThreads = 256;
 constexpr int kLChunks = kLBK / 8;  // 16-byte chunks per tile row
 
 __device__ __forceinline__ f4 mfma_bf16(bf16x8_t a, bf16x8_t b, f4 c)
@@ -41,26 +40,29 @@ __device__ __forceinline__ f4 mfma_bf16(bf16x8_t a, bf16x8_t b, f4 c)
 // LDS byte offset of chunk c of tile row r
 __device__ __forceinline__ int lchunk(int r, int c) { return (r * kLChunks + (c ^ (r & 7))) * 16; }
 
-// Workgroup tile (32 WM) x (32 WN): 4 waves in 2 x 2, each (16 WM) x (16 WN) = WM x WN MFMA tiles.
-template <int WM, int WN>
+// Workgroup tile (16 WM GM) x (16 WN GN): GM x GN waves, each (16 WM) x (16 WN) = WM x WN MFMA
+// tiles.
+template <int GM, int GN, int WM, int WN>
 struct LinTile {
-    static constexpr int BM = 32 * WM, BN = 32 * WN;
-    static constexpr int XT = BM * kLChunks / kLThreads;  // x transfers per thread and k tile
-    static constexpr int WT = BN * kLChunks / kLThreads;  // W transfers per thread and k tile
+    static constexpr int THREADS = 64 * GM * GN;
+    static constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
+    static constexpr int XT = BM * kLChunks / THREADS;  // x transfers per thread and k tile
+    static constexpr int WT = BN * kLChunks / THREADS;  // W transfers per thread and k tile
     static constexpr size_t lds = 2 * (size_t)(BM + BN) * kLBK * 2;  // two buffers of x and W tiles
     static_assert(XT >= 1 && WT >= 1 && XT + WT < 64, "tile transfer counts");
+    static_assert(BM * kLChunks % THREADS == 0 && BN * kLChunks % THREADS == 0, "even transfers");
 };
 
-template <int WM, int WN>
-__global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
+template <int GM, int GN, int WM, int WN>
+__global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
 {
-    using TL = LinTile<WM, WN>;
-    constexpr int BM = TL::BM, BN = TL::BN;
+    using TL = LinTile<GM, GN, WM, WN>;
+    constexpr int BM = TL::BM, BN = TL::BN, kLThreads = TL::THREADS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [buffer][x tile | W tile]
     constexpr int XB = BM * kLBK * 2, BUF = (BM + BN) * kLBK * 2;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;  // the wave's quadrant
+    const int wm = wave / GN, wn = wave % GN;  // the wave's place in the GM x GN grid
     // Tiles are numbered n-major, m fastest (t = n_tile * mt + m_tile), and workgroups are dealt
     // to the 8 XCDs in turn; XCD x takes the contiguous tile range [x T/8, (x+1) T/8), so the
     // workgroups sharing a weight tile run on one XCD, one after another, and read it from that
@@ -158,23 +160,25 @@ __global__ __launch_bounds__(kLThreads) void linear_kernel(LinearArgs a)
     }
 }
 
-template <int WM, int WN>
+template <int GM, int GN, int WM, int WN>
 static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
 {
-    using TL = LinTile<WM, WN>;
+    using TL = LinTile<GM, GN, WM, WN>;
     const unsigned tiles = (unsigned)((a.N + TL::BN - 1) / TL::BN) * (unsigned)((a.M + TL::BM - 1) / TL::BM);
     const dim3 grid(tiles);
-    hipLaunchKernelGGL((linear_kernel<WM, WN>), grid, dim3(kLThreads), TL::lds, stream, a);
+    hipLaunchKernelGGL((linear_kernel<GM, GN, WM, WN>), grid, dim3(TL::THREADS), TL::lds, stream, a);
     return hipGetLastError();
 }
 
-// Tile by rows: many rows take 128 x 128 tiles (two workgroups per CU; 128 x 256 tiles measured
-// slower, at one wave per SIMD); a few rows (one slot's drafted tokens) take 32 x 64 tiles, so
-// the weight stream is spread over enough workgroups.
+// Tile by rows: many rows take 128 x 128 tiles worked by 16 waves of 32 x 32 (two workgroups per
+// CU: the most resident waves to cover each wave's LDS operand latency; measured against 4 and 8
+// waves per tile and 256-wide tiles, which bring more flops per transferred byte but leave fewer
+// waves); a few rows (one slot's drafted tokens) take 32 x 64 tiles, so the weight stream is spread
+// over enough workgroups.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t stream)
 {
-    if (a.M <= 64) return launch_tile<1, 2>(a, stream);
-    return launch_tile<4, 4>(a, stream);
+    if (a.M <= 64) return launch_tile<2, 2, 1, 2>(a, stream);
+    return launch_tile<4, 4, 2, 2>(a, stream);
 }
 
 }  // namespace gdn
