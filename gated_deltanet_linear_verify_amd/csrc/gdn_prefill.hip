@@ -259,8 +259,9 @@ struct PrepLds {
     static constexpr size_t tm = 0;                              // once q, k are consumed: [C][kCP] A, then T
     static constexpr size_t pm = tm + sizeof(float) * C * kCP;   //                         [C][kCP] P
     static constexpr size_t scr = pm + sizeof(float) * C * kCP;  //                         [4][16][16] scratch
-    static constexpr size_t gate = qk_bytes > tp_bytes ? qk_bytes : tp_bytes;  // Gamma, gamma, beta, decay [4][C]
-    static constexpr size_t total = gate + sizeof(float) * 4 * C;
+    static constexpr int heads = 4;  // value heads whose gates are resident at once
+    static constexpr size_t gate = qk_bytes > tp_bytes ? qk_bytes : tp_bytes;  // per head: Gamma, gamma, beta, decay [4][C]
+    static constexpr size_t total = gate + sizeof(float) * heads * 4 * C;
 };
 static_assert(2 * PrepLds<128>::total <= 160 * 1024, "two d=128 prep workgroups must fit one CU's LDS");
 
@@ -313,10 +314,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     float *K = reinterpret_cast<float *>(smem + L::k);
     float *Tm = reinterpret_cast<float *>(smem + L::tm);
     float *Pm = reinterpret_cast<float *>(smem + L::pm);
-    float *Gam = reinterpret_cast<float *>(smem + L::gate);  // Gamma_t
-    float *gam = Gam + C;                                    // gamma_t = exp(Gamma_t)
-    float *bet = gam + C;                                    // beta_t (0 past the end)
-    float *dec = bet + C;                                    // exp(Gamma_C - Gamma_t)
+    // gates of value head hk R + hh, kept in slot hh % L::heads: Gamma_t, gamma_t = exp(Gamma_t),
+    // beta_t (0 past the end), exp(Gamma_C - Gamma_t)
+    auto gate_slot = [&](int hh) { return reinterpret_cast<float *>(smem + L::gate) + (hh % L::heads) * 4 * C; };
 
     const act_t *qkv = static_cast<const act_t *>(a.qkv);
     auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
@@ -339,46 +339,64 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     };
     const int tmin = c == 0 ? 0 : -3;  // lowest row of qkv a conv may read
 
-    // gates of value head h: Gamma = prefix sum of g (wave 0); padded tokens get g = 0, beta = 0
-    auto gates = [&](int h) {
-        if (wave == 0) {
-            float g = 0.f, b = 0.f;
-            if (lane < Lc) {
-                const size_t e = ((size_t)t0 + lane) * a.n_vh + h;
-                g = -expf(a.A_log[h]) * softplus_f(load_act<ACT_BF16>(a.alpha, e) + a.dt_bias[h]);
-                b = load_act<ACT_BF16>(a.beta, e);
-            }
-            float x = g;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            Gam[lane] = x;
-            gam[lane] = expf(x);
-            bet[lane] = b;
-            dec[lane] = expf(__shfl(x, 63) - x);
+    // Gate inputs of value head hk R + hh at this lane's token.  The loads are unconditional (a lane
+    // past the chunk or a head past R reads a valid entry it discards) and raw, so that nothing
+    // computed from them makes the compiler wait for them where they are issued.
+    using word_t = typename std::conditional<ACT_BF16, uint16_t, uint32_t>::type;  // bf16 or fp32 bits
+    struct GateIn {
+        uint32_t al, be;
+        float alog, dtb;
+    };
+    auto gate_load = [&](int hh) -> GateIn {
+        const int h = hk * R + min(hh, R - 1);
+        const size_t e = ((size_t)t0 + min(lane, Lc - 1)) * a.n_vh + h;
+        return GateIn{static_cast<const word_t *>(a.alpha)[e], static_cast<const word_t *>(a.beta)[e], a.A_log[h],
+                      a.dt_bias[h]};
+    };
+    auto word_f32 = [](uint32_t u) -> float {
+        if constexpr (ACT_BF16)
+            return bf16_to_f32((uint16_t)u);
+        else
+            return __builtin_bit_cast(float, u);
+    };
+    // one wave: Gamma = prefix sum of g; padded tokens get g = 0, beta = 0
+    auto gate_put = [&](int hh, const GateIn &in) {
+        float g = 0.f, b = 0.f;
+        if (lane < Lc) {
+            g = -expf(in.alog) * softplus_f(word_f32(in.al) + in.dtb);
+            b = word_f32(in.be);
         }
+        float x = g;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        float *G = gate_slot(hh);
+        G[lane] = x;
+        G[C + lane] = expf(x);
+        G[2 * C + lane] = b;
+        G[3 * C + lane] = expf(__shfl(x, 63) - x);
     };
 
     // conv of value head h's v, straight to the workspace: a thread takes 4 channels of TPT
-    // consecutive tokens
-    auto conv_v = [&](int h) {
-        constexpr int VG = D / 4;                 // channel groups of 4
-        constexpr int TPT = C * VG / kPThreads;   // tokens per thread: 8 at d = 128, 4 at d = 64
-        const int vg = tid % VG, tb = (tid / VG) * TPT;
-        const int lc = 2 * D + 4 * vg;
-        f4 wv[4];
+    // consecutive tokens.  conv_issue loads its taps and rows (the three rows before the call from
+    // the conv state too, whether or not this thread starts the call); conv_finish, issued after
+    // other work, converts them, sums the taps and stores.
+    constexpr int VG = D / 4;                // channel groups of 4
+    constexpr int TPT = C * VG / kPThreads;  // tokens per thread: 8 at d = 128, 4 at d = 64
+    const int vg = tid % VG, tb = (tid / VG) * TPT;
+    const int vlc = 2 * D + 4 * vg;
+    auto conv_issue = [&](f4 (&wv)[4], raw4 (&rw)[TPT + 3], f4 (&hs)[3]) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + e) * 4);
-        raw4 rw[TPT + 3];
+        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(vlc + e) * 4);
 #pragma unroll
-        for (int i = 0; i < TPT + 3; ++i) rw[i] = ld_raw(min(max(tb - 3 + i, tmin), Lc - 1), lc);
+        for (int i = 0; i < TPT + 3; ++i) rw[i] = ld_raw(min(max(tb - 3 + i, tmin), Lc - 1), vlc);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) hs[i] = hist4(i - 3, vlc);
+    };
+    auto conv_finish = [&](int h, const f4 (&wv)[4], const raw4 (&rw)[TPT + 3], const f4 (&hs)[3]) {
         const bool head_rows = c == 0 && tb == 0;  // this thread's first three rows precede the call
-        f4 hs[3] = {};
-        if (head_rows)
-#pragma unroll
-            for (int i = 0; i < 3; ++i) hs[i] = hist4(i - 3, lc);
         f4 xs[TPT + 3];
 #pragma unroll
         for (int i = 0; i < TPT + 3; ++i) xs[i] = (i < 3 && head_rows) ? hs[i < 3 ? i : 0] : cvt(rw[i]);
@@ -396,6 +414,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             *reinterpret_cast<f4 *>(vdst + t * kDB) = y;
         }
     };
+
+    // the first value heads' gate inputs travel with the q | k rows below
+    GateIn gin = gate_load(wave);
 
     // ---- conv of q | k into LDS: wave w takes tokens 16w .. 16w+15, a lane 4 channels; every row
     // it reads is loaded before the first tap sum
@@ -439,7 +460,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             *reinterpret_cast<f4 *>(M + swz<D>(t, mc)) = y;
         }
     }
-    lds_barrier();  // q and k are in LDS
+    asm volatile("" : "+v"(gin.al), "+v"(gin.be), "+v"(gin.alog), "+v"(gin.dtb));  // loaded by now
+    if (wave < min(R, L::heads)) gate_put(wave, gin);
+    lds_barrier();  // q, k and the first heads' gates are in LDS
 
     // ---- the q and k images, then the lower 16 x 16 tiles of K K^T (waves 0, 1) and Q K^T (waves
     // 2, 3) into registers (MFMA; row tiles {0,3} or {1,2}: 5 tiles per wave).  Each value head's
@@ -484,9 +507,15 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int h = hk * R + hh;
         v0 = 2 * a.n_kh * D + h * D;
         if (hh > 0) lds_barrier();  // the previous head's T, P and gates are written out
-        gates(h);
-        conv_v(h);
-        lds_barrier();
+        if (hh > 0 && hh % L::heads == 0) {  // the next group of heads' gates
+            if (wave < min(R - hh, L::heads)) gate_put(hh + wave, gate_load(hh + wave));
+            lds_barrier();
+        }
+        const float *Gam = gate_slot(hh), *gam = Gam + C, *bet = gam + C, *dec = bet + C;
+        // this head's v rows are loaded now and convolved once A / P and T are built
+        f4 cwv[4], chs[3];
+        raw4 crw[TPT + 3];
+        conv_issue(cwv, crw, chs);
         {
             float *Dm = wave < 2 ? Tm : Pm;
 #pragma unroll
@@ -565,6 +594,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             if (r3 == 3) acc = blk16s(Tm, 48, 48, scr, acc);
             put_neg(16 * r3, 16 * c3, acc);
         }
+        conv_finish(h, cwv, crw, chs);
         lds_barrier();
 
         // ---- T, P and the gates for the scan (T and P as Mat images)
