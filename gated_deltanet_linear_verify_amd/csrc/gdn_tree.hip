@@ -11,10 +11,13 @@
 // in LDS (global_load_lds), computes every node's conv output, gate and beta into LDS, and
 // builds a depth-first processing schedule.  The node loop then runs in DFS order: a node whose
 // parent is the node just processed continues from the state in registers (each step is
-// Geo::step, the same arithmetic as the chain kernel); any other node
-// restarts from a register copy of the committed state and re-runs its parent's root path
-// (compute only, nothing stored) before its own step.  No state is ever re-read from memory, so
-// the loop never waits on the memory counter that the capture stores occupy.
+// Geo::step, the same arithmetic as the chain kernel).  A node with two or more children leaves a
+// register copy of its state in one of kTreeSaved save slots, which its later children restore;
+// children are visited lightest subtree first, so a slot is released (its node's last child
+// started) before the deepest descent, and few slots cover a whole tree.  When a parent's copy was
+// evicted, its root path is re-run from the nearest saved ancestor or the committed state
+// (compute only, nothing stored).  No state is ever re-read from memory, so the loop never waits
+// on the memory counter that the capture stores occupy.
 #include "gdn_device.h"
 #include "gdn_geo.h"
 #include "gdn_internal.h"
@@ -24,9 +27,14 @@
 namespace gdn {
 
 constexpr int kTreeMaxNodes = 64;
-// Schedule entry: node index | restart-from-committed-state flag | capture-and-output flag.
+constexpr int kTreeSaved = 3;  // register save slots for states that later siblings restore
+// Schedule entry: node index (bits 0-7) | restart-from-committed-state flag | capture-and-output
+// flag | 1 + the save slot restored before the step (bits 10-11, 0: none) | 1 + the save slot
+// written after it (bits 12-13, 0: none).
 constexpr int kSchedRestart = 0x100;
 constexpr int kSchedEmit = 0x200;
+constexpr int kSchedRestoreShift = 10;
+constexpr int kSchedSaveShift = 12;
 constexpr int kSchedMax = kTreeMaxNodes * (kTreeMaxNodes + 1) / 2 + kTreeMaxNodes;
 
 // Waves per head: twice the chain kernel's.  A tree's node steps form one dependent chain per
@@ -54,10 +62,130 @@ struct TreeLds {
                + region(T)                                // raw rows, then os
                + sizeof(float) * 4 * (size_t)T            // rho, beta, k.q
                + sizeof(int) * 4 * (size_t)T              // ancestors 1..3 (+ pad)
-               + sizeof(int) * 4 * kTreeMaxNodes          // DFS scratch
                + sizeof(uint16_t) * kSchedMax + 16;       // schedule + its length
     }
 };
+
+// Depth-first schedule of a tree of T <= 64 nodes, built by one wave with lane n standing for node
+// n and every step a whole-wave one (cross-lane reads, no LDS round trips, no sequential walk over
+// the nodes).  Siblings (roots too) are visited in order of subtree size, then index, so that the
+// largest subtree comes last.  Save slots: a node with two or more children leaves a copy of its
+// state for its later children in slot d mod kTreeSaved, where d counts its ancestors still
+// awaiting a later child when it is visited (the nodes whose copies are live at that moment, each
+// in its own slot d' mod kTreeSaved); a later child restores the parent's copy unless a node
+// visited in between was saved at depth d' >= d + kTreeSaved, which overwrote it, and then re-runs
+// the parent's root path from the committed state instead (compute only, nothing stored).
+// anc[4 n + 3] holds node n's parent.
+__device__ __forceinline__ void build_schedule(int T, int lane, const int *anc, uint16_t *sched, int *nsched)
+{
+    auto rl = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };  // v of lane l (uniform l)
+    auto from = [](int v, int l) { return __shfl(v, l); };                   // v of lane l (per lane)
+    const bool node = lane < T;
+    int par = -1;
+    if (node) {
+        const int p = anc[lane * 4 + 3];
+        par = (p >= -1 && p < lane) ? p : -1;  // a malformed parent makes a root
+    }
+    // ancestor-or-self mask (two words) and depth: walk up, one level per round
+    uint32_t am_lo = node && lane < 32 ? 1u << lane : 0u, am_hi = node && lane >= 32 ? 1u << (lane - 32) : 0u;
+    // The loops below are branch-free (selects, not conditions) and the ones over all lanes run a
+    // fixed 64 times, lanes past T standing for no node (parent -1, size 0, no ancestors): they add
+    // nothing, and the loops unroll.
+    int depth = 0;
+    for (int a = par; __any(a >= 0);) {
+        const bool in = a >= 0;
+        const int up = from(par, in ? a : 0);
+        am_lo |= in && a < 32 ? 1u << (a & 31) : 0u;
+        am_hi |= in && a >= 32 ? 1u << (a & 31) : 0u;
+        depth += in ? 1 : 0;
+        a = in ? up : -1;
+    }
+    // children and subtree sizes
+    int kids = 0, size = 0;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+        const int pm = rl(par, m);
+        const uint32_t lo = (uint32_t)rl((int)am_lo, m), hi = (uint32_t)rl((int)am_hi, m);
+        kids += pm == lane ? 1 : 0;
+        size += (int)(((lane < 32 ? lo : hi) >> (lane & 31)) & 1u);
+    }
+    // sizes of the siblings visited before this node
+    int off = 0;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+        const int pm = rl(par, m), sm = rl(size, m);
+        const bool before = (pm == par) & ((sm < size) | ((sm == size) & (m < lane)));
+        off += before ? sm : 0;
+    }
+    // preorder position and d: walk up again, summing each level's offset and whether it keeps its
+    // parent awaiting a later child
+    // (every cross-lane read below runs on the whole wave, outside any condition: a lane reads
+    // only lanes that execute the read with it)
+    const int pp = par < 0 ? 0 : par;
+    const int pkids = from(kids, pp), psize = from(size, pp);
+    const int opens = (par >= 0 && pkids >= 2 && off + size != psize - 1) ? 1 : 0;
+    const int step = off + (par >= 0 ? 1 : 0);
+    int pre = 0, d = 0;
+    for (int c = node ? lane : -1; __any(c >= 0);) {
+        const bool in = c >= 0;
+        const int cc = in ? c : 0;
+        const int sp = from(step, cc), op = from(opens, cc), pc = from(par, cc);
+        pre += in ? sp : 0;
+        d += in ? op : 0;
+        c = in ? pc : -1;
+    }
+    if (!node) pre = lane;  // the lanes past T keep their places: pre is a permutation of the lanes
+    const int ord = __builtin_amdgcn_ds_permute(pre * 4, lane);  // ord[i]: the node at position i
+    const int prev = from(ord, pre > 0 ? pre - 1 : 0);
+    const bool restore = node && par >= 0 && pre > 0 && par != prev;
+    const int dq = from(d, pp), preq = from(pre, pp), depq = from(depth, pp);
+    const uint32_t amq_lo = (uint32_t)from((int)am_lo, pp), amq_hi = (uint32_t)from((int)am_hi, pp);
+    // the deepest save between the parent's visit and this one
+    const int dsave = node && kids >= 2 ? d : -1;
+    const int dsave_at = from(dsave, ord);  // by position
+    int dmax = -1;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {  // positions past T hold no node: dsave -1
+        const int v = rl(dsave_at, i);
+        dmax = ((i > preq) & (i < pre) & (v > dmax)) ? v : dmax;
+    }
+    const bool live = dmax < dq + kTreeSaved;
+    const bool rerun = restore && !live;
+    // entries: the re-run root path (root .. parent), then the node; offsets by position
+    const int cnt = node ? 1 + (rerun ? depq + 1 : 0) : 0;
+    const int cnt_ord = from(cnt, ord);
+    const int cnt_at = lane < T ? cnt_ord : 0;
+    int incl = cnt_at;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const int base = from(incl - cnt_at, pre);
+    if (node) {
+        int e = lane | kSchedEmit;
+        if (par < 0)
+            e |= kSchedRestart;
+        else if (restore && live)
+            e |= (dq % kTreeSaved + 1) << kSchedRestoreShift;
+        if (kids >= 2) e |= (d % kTreeSaved + 1) << kSchedSaveShift;
+        int at = base;
+        if (rerun) {  // the parent's root path in index order: ancestors have smaller indices
+            uint32_t lo = amq_lo, hi = amq_hi;
+            for (int k = 0; lo | hi; ++k) {
+                const int x = lo ? __builtin_ctz(lo) : 32 + __builtin_ctz(hi);
+                if (lo)
+                    lo &= lo - 1;
+                else
+                    hi &= hi - 1;
+                sched[at++] = (uint16_t)(x | (k == 0 ? kSchedRestart : 0));
+            }
+        }
+        sched[at] = (uint16_t)e;
+    }
+    const int total = rl(incl, 63);
+    if (lane == 0) *nsched = total;
+}
 
 template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN>
 __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(VerifyArgs a)
@@ -90,8 +218,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     float *os = reinterpret_cast<float *>(raw);          // [T][D]   readout, rows in perm order (loop)
     float *rbk = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(raw) + L::region(T));  // [T][4]
     int *anc = reinterpret_cast<int *>(rbk + 4 * T);  // [T][4]: ancestors 1..3 (>= 0 node, -1-r conv row r)
-    int *dfs = anc + 4 * T;                                        // [4][kTreeMaxNodes] DFS scratch
-    uint16_t *sched = reinterpret_cast<uint16_t *>(dfs + 4 * kTreeMaxNodes);
+    uint16_t *sched = reinterpret_cast<uint16_t *>(anc + 4 * T);
     int *nsched = reinterpret_cast<int *>(sched + kSchedMax);
 
     const int C = a.C;
@@ -119,18 +246,18 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         const int r = it / nvr, lc = (it % nvr) * VEC;
         lds_dma16(qkv_b + (uint32_t)(r * C + gchan(lc)), raw + it * VEC);
     }
-    constexpr int CPT = (NCH + 63) / 64 / NW + 1;  // channels per thread (upper bound)
-    f4 wv[CPT];
-    float csv[CPT][3];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int lc = tid + j * nthr;
-        if (lc < NCH) {
-            const int gc = gchan(lc);
-            wv[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
-#pragma unroll
-            for (int r = 0; r < 3; ++r) csv[j][r] = cs_s[(uint32_t)(r * C + gc)];
-        }
+    // conv channels: thread 64 + lc takes channel lc (wave 0 builds the schedule meanwhile)
+    static_assert(NCH <= 64 * (NW - 1) && NCH % 64 == 0, "one conv channel per thread of whole waves 1 ..");
+    const int lc = tid - 64;
+    const bool conv_thread = lc >= 0 && lc < NCH;
+    f4 wv = {0.f, 0.f, 0.f, 0.f};
+    float cs0 = 0.f, cs1 = 0.f, cs2 = 0.f;  // the slot's conv state rows
+    if (conv_thread) {
+        const int gc = gchan(lc);
+        wv = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
+        cs0 = cs_s[(uint32_t)gc];
+        cs1 = cs_s[(uint32_t)(C + gc)];
+        cs2 = cs_s[(uint32_t)(2 * C + gc)];
     }
     // alpha, beta and the parent of node tid.  The loads sit outside any branch (threads past T load
     // node T-1's) and nothing is computed from them before the wait below: a bf16 conversion, or a
@@ -191,68 +318,56 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     }
     __syncthreads();
 
-    // ================= conv of every node (one thread per channel) + conv-state capture =========
-    float *cct = a.cap_conv + (size_t)s * a.t_cap * 3 * C;  // [t_cap][3][C] of this slot
+    if (wave == 0) {
+        build_schedule(T, lane, anc, sched, nsched);
+    } else if (conv_thread) {
+        // ================= conv of every node (one thread per channel) + conv-state capture =====
+        float *cct = a.cap_conv + (size_t)s * a.t_cap * 3 * C;  // [t_cap][3][C] of this slot
+        const int gc = gchan(lc);
+        const bool own = lc >= 2 * D || lead;
+        float *dst = lc < D ? qs + lc : (lc < 2 * D ? ks + (lc - D) : vs + G::perm(lc - 2 * D));
+        // the row an ancestor code names; the conv-state rows come in as values, not captures: a
+        // select between captured variables becomes a load through a select of their addresses,
+        // which keeps them in scratch memory
+        // (the row is read unconditionally, node 0's for a conv-state code, so that no read sits
+        // under a branch and a batch's reads are all in flight together)
+        auto X = [raw, lc, to_f32](int code, float c0, float c1, float c2) -> float {
+            const float h = code == -1 ? c0 : (code == -2 ? c1 : c2);
+            const float r = to_f32(raw[max(code, 0) * NCH + lc]);
+            return code >= 0 ? r : h;
+        };
+        // Nodes in batches of CB = 16: one LDS read brings the batch's ancestor codes, lane 4 j + i
+        // holding code i of node n0 + j, and they are taken from there lane by lane (readlane: the
+        // conv waves are whole); then every row read of the batch is issued before its first store
+        // (the compiler cannot move a read above a store to LDS it may alias).
+        constexpr int CB = 16;
+#pragma unroll 1
+        for (int n0 = 0; n0 < T; n0 += CB) {
+            const int codes = anc[min(n0 + (lane >> 2), T - 1) * 4 + (lane & 3)];
+            float x[CB][4];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int lc = tid + j * nthr;
-        if (lc < NCH) {
-            const int gc = gchan(lc);
-            const f4 w = wv[j];
-            const bool own = lc >= 2 * D || lead;
-            float *dst = lc < D ? qs + lc : (lc < 2 * D ? ks + (lc - D) : vs + G::perm(lc - 2 * D));
-            auto X = [&](int code) -> float {
-                return code >= 0 ? to_f32(raw[code * NCH + lc]) : csv[j][-1 - code];
-            };
-            for (int n = 0; n < T; ++n) {
-                const int a1 = anc[n * 4 + 0], a2 = anc[n * 4 + 1], a3 = anc[n * 4 + 2];
-                const float x1 = X(a1), x2 = X(a2), xn = to_f32(raw[n * NCH + lc]);
-                float y = conv4(w, X(a3), x2, x1, xn);
+            for (int j = 0; j < CB; ++j) {
+                const int n = min(n0 + j, T - 1);
+                x[j][0] = X(__builtin_amdgcn_readlane(codes, 4 * j + 2), cs0, cs1, cs2);
+                x[j][1] = X(__builtin_amdgcn_readlane(codes, 4 * j + 1), cs0, cs1, cs2);
+                x[j][2] = X(__builtin_amdgcn_readlane(codes, 4 * j), cs0, cs1, cs2);
+                x[j][3] = to_f32(raw[n * NCH + lc]);
+            }
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const int n = n0 + j;
+                if (n >= T) break;
+                float y = conv4(wv, x[j][0], x[j][1], x[j][2], x[j][3]);
                 if constexpr (QKN) y = y * sigmoid_f(y);
                 dst[n * D] = y;
                 if (own) {  // 3-row conv state after node n: [ancestor 2, ancestor 1, n]
                     float *cp = cct + (size_t)n * 3 * C + gc;
-                    cp[0] = x2;
-                    cp[(size_t)C] = x1;
-                    cp[(size_t)2 * C] = xn;
+                    cp[0] = x[j][1];
+                    cp[(size_t)C] = x[j][2];
+                    cp[(size_t)2 * C] = x[j][3];
                 }
             }
         }
-    }
-    // depth-first schedule (thread 0): children in increasing index, roots in increasing index
-    if (tid == 0) {
-        int *first = dfs, *sib = dfs + kTreeMaxNodes, *stack = dfs + 2 * kTreeMaxNodes;
-        int *path = dfs + 3 * kTreeMaxNodes;
-        for (int n = 0; n < T; ++n) first[n] = -1;
-        int first_root = -1;
-        for (int n = T - 1; n >= 0; --n) {  // prepend in reverse: lists come out in increasing order
-            const int p = parent_of(n);
-            int *head = p >= 0 ? &first[p] : &first_root;
-            sib[n] = *head;
-            *head = n;
-        }
-        int cnt = 0, in_regs = -1, sp = 0;  // in_regs: node whose state the registers hold (-1: none)
-        // the stack holds sibling-list cursors: pop a node, push its next sibling, then its first child
-        if (first_root >= 0) stack[sp++] = first_root;
-        while (sp > 0) {
-            const int n = stack[--sp];
-            if (sib[n] >= 0) stack[sp++] = sib[n];
-            if (first[n] >= 0) stack[sp++] = first[n];
-            const int p = parent_of(n);
-            if (p >= 0 && p == in_regs) {
-                sched[cnt++] = (uint16_t)(n | kSchedEmit);
-            } else if (p < 0) {
-                sched[cnt++] = (uint16_t)(n | kSchedRestart | kSchedEmit);
-            } else {  // re-run the parent's root path from the committed state, then the node
-                int L = 0;
-                for (int m = p; m >= 0; m = parent_of(m)) path[L++] = m;
-                for (int k = L - 1; k >= 0; --k)
-                    sched[cnt++] = (uint16_t)(path[k] | (k == L - 1 ? kSchedRestart : 0));
-                sched[cnt++] = (uint16_t)(n | kSchedEmit);
-            }
-            in_regs = n;
-        }
-        *nsched = cnt;
     }
     __syncthreads();
     // ================= the node loop in schedule order =================
@@ -264,17 +379,23 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     const size_t hd = (size_t)D * D;
     float *cap_base = a.cap_ssm + ((size_t)s * a.t_cap * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
     const size_t cap_nstride = (size_t)a.n_vh * hd;
+    float SV[kTreeSaved][G::RPL][G::CPL];  // save slots (indexed by constants only: registers)
+    auto copy_state = [](float (&dst)[G::RPL][G::CPL], const float (&src)[G::RPL][G::CPL]) {
+#pragma unroll
+        for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+            for (int c = 0; c < G::CPL; ++c) dst[i][c] = src[i][c];
+    };
     const int ns = *nsched;
 #pragma unroll 1
     for (int k = 0; k < ns; ++k) {
-        const int e = sched[k];
+        const int e = __builtin_amdgcn_readfirstlane(sched[k]);  // uniform: scalar branches below
         const int n = e & 0xff;
-        if (e & kSchedRestart) {
+        const int rs = (e >> kSchedRestoreShift) & 3, sv = (e >> kSchedSaveShift) & 3;
+        if (e & kSchedRestart) copy_state(S, R0);
 #pragma unroll
-            for (int i = 0; i < G::RPL; ++i)
-#pragma unroll
-                for (int c = 0; c < G::CPL; ++c) S[i][c] = R0[i][c];
-        }
+        for (int j = 0; j < kTreeSaved; ++j)
+            if (rs == j + 1) copy_state(S, SV[j]);
         const f4 sc = *reinterpret_cast<const f4 *>(rbk + n * 4);
         float o[G::RPL];
         G::template step<QKN>(S, ks + n * D, qs + n * D, vs + n * D + wih * G::RPW + rg * G::RPL, sc[0], sc[1], cg, o);
@@ -293,6 +414,9 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
                     store_stream(cp + (size_t)(4 * i) * D + 64 * c4, v);
                 }
         }
+#pragma unroll
+        for (int j = 0; j < kTreeSaved; ++j)
+            if (sv == j + 1) copy_state(SV[j], S);
     }
     __syncthreads();
 
