@@ -172,3 +172,25 @@ def test_tree_too_many_nodes_rejected():
     with pytest.raises(gdn.GdnError) as ei:
         device.verify_tree(d)
     assert ei.value.code == gdn.GDN_ERR_SHAPE
+
+
+def _kary_parents(n, k):
+    return np.array([-1] + [(i - 1) // k for i in range(1, n)], dtype=np.int32)
+
+
+def test_tree_bushy_shapes_beyond_the_save_slots():
+    """Trees whose depth-first walk keeps more branch points open than the kernel has save slots
+    (complete binary and ternary trees, a forest of them): a child whose parent's copy was
+    evicted re-runs the parent's root path, and every node still matches the oracle."""
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=3, n_batch=3, n_tok=63)
+    device, _ = _mods()
+    inp = W.make_tree_inputs(shape, 4)
+    binary = _kary_parents(63, 2)
+    ternary = _kary_parents(63, 3)
+    forest = np.concatenate([_kary_parents(31, 2), _kary_parents(32, 2) + np.where(
+        _kary_parents(32, 2) >= 0, 31, 0)]).astype(np.int32)
+    inp["parent"] = np.stack([binary, ternary, forest])
+    d = _tree_upload(shape, inp)
+    device.verify_tree(d)
+    torch.cuda.synchronize()
+    _check_tree(shape, inp, d)
