@@ -233,7 +233,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU code (got --gpus "
-              f"{args.gpus}); sharding is described in DESIGN.md", file=sys.stderr)
+              f"{args.gpus})", file=sys.stderr)
         return 2
 
     import numpy as np
