@@ -69,6 +69,10 @@ PREFILL_CASES = {
     "bf16_odd_heads_96": (W.shape_with(W.CHUNKED_PREFILL, n_tok=96, n_kh=3, n_vh=3), {"weak_decay": True}, 0),
     "bf16_d64_odd_heads_150": (W.shape_with(W.TINY_VERIFY, n_tok=150, n_kh=1, n_vh=3, act_dtype=W.BF16,
                                             out_dtype=W.BF16), {"weak_decay": True}, 0),
+    # six value heads per key head: more than the prep keeps gates for at once (a second group)
+    "bf16_d64_six_per_key_head_130": (W.shape_with(W.TINY_VERIFY, n_tok=130, n_kh=1, n_vh=6, act_dtype=W.BF16,
+                                                   out_dtype=W.BF16), {"weak_decay": True}, 0),
+    "bf16_d128_gqa4_70": (W.shape_with(W.CHUNKED_PREFILL, n_tok=70, n_kh=4, n_vh=16), {"weak_decay": True}, 0),
 }
 
 
