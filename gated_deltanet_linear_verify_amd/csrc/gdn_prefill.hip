@@ -65,6 +65,24 @@ __device__ __forceinline__ f4 mfma4f32(float a, float b, f4 c)
 #endif
 }
 
+// Transposing 64-bit LDS load (ds_read_b64_tr_b16).  In every group of 16 lanes, lane i receives
+// element i % 4 of the 4-element chunks that lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 of
+// the group address, in that order.  So when lane 4 j + q of a group points at row r0 + j, columns
+// c0 + 4 q .. c0 + 4 q + 3 of a row-major bf16 matrix, lane i of the group gets column c0 + i,
+// rows r0 .. r0 + 3: four consecutive k values of a column, as an MFMA operand wants them.
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_tr;
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned long long lds_load_tr4(const __bf16 *p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto lp = (__attribute__((address_space(3))) bf16x4_tr *)(const_cast<__bf16 *>(p));
+    return __builtin_bit_cast(unsigned long long, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+#else
+    (void)p;
+    return 0;
+#endif
+}
+
 // 8 fp32 values -> bf16 hi and lo parts (hi = RNE(x), lo = RNE(x - hi)).
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo)
 {
@@ -184,6 +202,20 @@ struct Mat {
             f.hi = *reinterpret_cast<const bf16x8 *>(hp + idx(r, c0));
             f.lo = *reinterpret_cast<const bf16x8 *>(hp + ROWS * COLS + idx(r, c0));
         }
+        return f;
+    }
+    // operand fragment down a column (bf16 planes only): lane li of its 16-lane group gets column
+    // c0 + li, rows r0 .. r0 + 7 (r0 the same for the group, c0 a multiple of 8), by two transposing
+    // loads per plane
+    __device__ static Frag<F32> load_col(const float *m, int r0, int c0, int li)
+    {
+        static_assert(!F32, "transposing loads move 16-bit elements");
+        const __bf16 *hp = reinterpret_cast<const __bf16 *>(m);
+        const int r = r0 + (li >> 2), c = c0 + 4 * (li & 3);
+        const int a0 = idx(r, c), a1 = idx(r + 4, c);
+        Frag<F32> f;
+        f.hi = __builtin_bit_cast(bf16x8, u64x2{lds_load_tr4(hp + a0), lds_load_tr4(hp + a1)});
+        f.lo = __builtin_bit_cast(bf16x8, u64x2{lds_load_tr4(hp + ROWS * COLS + a0), lds_load_tr4(hp + ROWS * COLS + a1)});
         return f;
     }
     // element (r, c) into fragment slot e (gathers down a column)
@@ -795,8 +827,12 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
 #pragma unroll
                 for (int kk = 0; kk < C; kk += 32) {
                     Frag<F32> kf;  // K[s][j] down the column, s = kk + 8 lg + e
+                    if constexpr (F32) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) MK::get(K, kk + 8 * lg + e, j, kf, e);
+                        for (int e = 0; e < 8; ++e) MK::get(K, kk + 8 * lg + e, j, kf, e);
+                    } else {
+                        kf = MK::load_col(K, kk + 8 * lg, j - li, li);
+                    }
                     sa = mma<F32>(MU::load(Dp, li, kk + 8 * lg), kf, sa);
                 }
                 sreg[q2] = sa;
