@@ -209,7 +209,7 @@ def components(args) -> dict:
     # chunked prefill: one 8192-token sequence
     s = W.CHUNKED_PREFILL
     d = device.upload(s, W.make_inputs(s, 0), capture=False)
-    us = time_launches(lambda: device.prefill(d), 10)
+    us = time_launches(lambda: device.prefill(d), 20)
     fl = bytemodel.prefill_flops(s)
     out["chunked_prefill"] = {"workload": "1 slot x 8192 tokens, 16/32 heads, d=128, bf16, chunk 64",
                               "us": us, "tokens_per_s": s.n_tok / (us * 1e-6),

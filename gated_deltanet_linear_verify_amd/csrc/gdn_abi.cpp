@@ -148,28 +148,41 @@ namespace gdn {
 int abi_check_dims(const gdn_dims *d) { return check_dims(d); }
 }  // namespace gdn
 
-GDN_API int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, const void *qkv, const void *z,
-                       const void *alpha, const void *beta, const float *A_log, const float *dt_bias,
-                       const float *conv_w, const float *norm_w, const gdn_capture *capture, void *out,
-                       int32_t n_tok, const int32_t *slot_ids, int32_t n_batch, void *stream)
+namespace {
+// Chain verify, from the slots' states (resume == NULL) or from the capture positions in resume.
+int verify_chain(const char *fn, const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
+                 const void *z, const void *alpha, const void *beta, const float *A_log, const float *dt_bias,
+                 const float *conv_w, const float *norm_w, const gdn_capture *capture, void *out, int32_t n_tok,
+                 const int32_t *slot_ids, const int32_t *resume, int32_t n_batch, void *stream)
 {
     if (int r = check_dims(dims)) return r;
     const gdn_dims &d = *dims;
     if (!state || !conv_state || !qkv || !z || !alpha || !beta || !A_log || !dt_bias || !conv_w || !norm_w || !out ||
         !slot_ids)
-        return fail(GDN_ERR_ARG, "gdn_verify: a required pointer is NULL");
+        return fail(GDN_ERR_ARG, "%s: a required pointer is NULL", fn);
     if (!aligned16(state) || !aligned16(conv_state) || !aligned16(conv_w) || !aligned16(z) || !aligned16(qkv))
-        return fail(GDN_ERR_ARG, "gdn_verify: state, conv_state, conv_w, qkv and z must be 16-byte aligned");
-    if (n_tok < 1) return fail(GDN_ERR_RANGE, "gdn_verify: n_tok must be >= 1 (got %d)", n_tok);
+        return fail(GDN_ERR_ARG, "%s: state, conv_state, conv_w, qkv and z must be 16-byte aligned", fn);
+    if (n_tok < 1) return fail(GDN_ERR_RANGE, "%s: n_tok must be >= 1 (got %d)", fn, n_tok);
     if (n_batch < 1 || n_batch > d.n_pool)
-        return fail(GDN_ERR_RANGE, "gdn_verify: n_batch %d outside [1, n_pool = %d]", n_batch, d.n_pool);
+        return fail(GDN_ERR_RANGE, "%s: n_batch %d outside [1, n_pool = %d]", fn, n_batch, d.n_pool);
     if (capture)
         if (int r = check_capture(capture, GDN_CHAIN, n_tok, dims)) return r;
+    if (resume && !capture)
+        return fail(GDN_ERR_ARG, "%s: resuming from capture positions needs the capture", fn);
     if (gdn::verify_chain_lds_bytes(d.d_k, d.n_vh / d.n_kh, d.act_dtype == GDN_BF16) > kMaxLds)
-        return fail(GDN_ERR_SHAPE, "gdn_verify: LDS tile exceeds 160 KiB");
+        return fail(GDN_ERR_SHAPE, "%s: LDS tile exceeds 160 KiB", fn);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (d.flags & GDN_F_CHECK_INDICES)
+    if (d.flags & GDN_F_CHECK_INDICES) {
         if (int r = check_slots(slot_ids, n_batch, d.n_pool, st)) return r;
+        if (resume) {
+            std::vector<int32_t> h;
+            if (int r = fetch_i32(resume, n_batch, st, h)) return r;
+            for (int i = 0; i < n_batch; ++i)
+                if (h[i] >= capture->t_cap)
+                    return fail(GDN_ERR_RANGE, "%s: resume_idx[%d] = %d outside [-1, t_cap = %d)", fn, i, h[i],
+                                capture->t_cap);
+        }
+    }
 
     gdn::VerifyArgs a = make_args(d, n_tok, n_batch);
     a.t_cap = capture ? capture->t_cap : 0;
@@ -187,9 +200,33 @@ GDN_API int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, co
     a.cap_conv = capture ? capture->conv : nullptr;
     a.out = out;
     a.slot_ids = slot_ids;
+    a.resume = resume;
     gdn::LaunchCfg c{d.act_dtype == GDN_BF16, d.out_dtype == GDN_BF16, (d.flags & GDN_F_QK_NORM_SILU) != 0};
-    if (hipError_t e = gdn::launch_verify_chain(a, c, st)) return hip_fail(e, "gdn_verify launch");
+    if (hipError_t e = gdn::launch_verify_chain(a, c, st))
+        return fail(GDN_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
     return ok();
+}
+}  // namespace
+
+GDN_API int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, const void *qkv, const void *z,
+                       const void *alpha, const void *beta, const float *A_log, const float *dt_bias,
+                       const float *conv_w, const float *norm_w, const gdn_capture *capture, void *out,
+                       int32_t n_tok, const int32_t *slot_ids, int32_t n_batch, void *stream)
+{
+    return verify_chain("gdn_verify", dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, conv_w, norm_w,
+                        capture, out, n_tok, slot_ids, nullptr, n_batch, stream);
+}
+
+GDN_API int gdn_verify_resume(const gdn_dims *dims, float *state, float *conv_state, const void *qkv, const void *z,
+                              const void *alpha, const void *beta, const float *A_log, const float *dt_bias,
+                              const float *conv_w, const float *norm_w, const gdn_capture *capture, void *out,
+                              int32_t n_tok, const int32_t *slot_ids, const int32_t *resume_idx, int32_t n_batch,
+                              void *stream)
+{
+    if (!resume_idx) return fail(GDN_ERR_ARG, "gdn_verify_resume: resume_idx is NULL");
+    if (!capture) return fail(GDN_ERR_ARG, "gdn_verify_resume: capture is NULL");
+    return verify_chain("gdn_verify_resume", dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, conv_w,
+                        norm_w, capture, out, n_tok, slot_ids, resume_idx, n_batch, stream);
 }
 
 GDN_API int gdn_verify_tree(const gdn_dims *dims, const float *state, const float *conv_state, const void *qkv,

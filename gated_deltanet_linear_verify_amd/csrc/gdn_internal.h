@@ -23,6 +23,9 @@ struct VerifyArgs {
     float *cap_conv;
     void *out;
     const int32_t *slot_ids;
+    const int32_t *resume;  // chain verify with capture: per batch entry, the capture position whose
+                            // state and conv window the first token starts from (< 0: the slot's
+                            // state); NULL: every entry starts from the slot's state
     const int32_t *parent;  // tree only
     int32_t n_batch;
 };

@@ -82,6 +82,18 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     const int h = hk * R + hl;
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the workgroup
+    // A rollback left pending by the previous round: the first launch of the call starts from the
+    // state after capture position ra of this same capture, written by that round's verify, instead
+    // of from the slot's state.  This workgroup reads only its own heads' and channels' slices of
+    // position ra, and every read lands before its first capture store.
+    int ra = -1;
+    if constexpr (CAP) {
+        if (a.resume) {
+            const int r = a.resume[b];
+            if (r >= a.t_cap) return;  // outside the capture: every launch skips the entry (uniform)
+            if (a.t0 == 0) ra = r;
+        }
+    }
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     float *ks = reinterpret_cast<float *>(smem_raw);  // [TT][D]
@@ -100,6 +112,8 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     const int nch = (2 + R) * D;
     const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + hk * R * D;
     float *cs_s = a.conv_state + (size_t)s * 3 * C;
+    // conv state the launch starts from: the slot's, or capture window rows ra+1 .. ra+3
+    const float *cs_src = ra >= 0 ? a.cap_conv + ((size_t)s * (3 + a.t_cap) + ra + 1) * C : cs_s;
     const size_t hd = (size_t)D * D;
     const act_t *qkv_b = static_cast<const act_t *>(a.qkv) + ((size_t)b * T + t0) * C;
     const act_t *z_b = static_cast<const act_t *>(a.z) + ((size_t)b * T + t0) * a.n_vh * D + (size_t)hk * R * D;
@@ -147,13 +161,15 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
             const int gc = gchan(lc);
             wv[it] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
 #pragma unroll
-            for (int r = 0; r < 3; ++r) csv[it][r] = cs_s[(uint32_t)(r * C + gc)];
+            for (int r = 0; r < 3; ++r) csv[it][r] = cs_src[(uint32_t)(r * C + gc)];
         }
     }
     // the recurrent state, into registers
     float S[G::RPL][G::CPL];  // S[i][4 c4 + e] = state row (row0 + 4 i), column (64 c4 + 4 cg + e)
     const int row0 = wih * G::RPW + rg;
-    float *st_ptr = a.state + ((size_t)s * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
+    const float *st_src = ra >= 0 ? a.cap_ssm + (((size_t)s * a.t_cap + ra) * a.n_vh + h) * hd
+                                  : a.state + ((size_t)s * a.n_vh + h) * hd;
+    const float *st_ptr = st_src + (size_t)row0 * D + cg * 4;
 #pragma unroll
     for (int i = 0; i < G::RPL; ++i)
 #pragma unroll

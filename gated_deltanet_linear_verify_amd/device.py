@@ -40,6 +40,8 @@ def upload(shape: Shape, inp: dict, *, device: str = "cuda", t_cap: Optional[int
         "state": f32(inp["state"]),
         "conv_state": f32(inp["conv_state"]),
         "slot_ids": torch.from_numpy(np.ascontiguousarray(inp["slot_ids"], dtype=np.int32)).to(device),
+        # the prefill's slot, kept on the host so that a call does not read it back from the device
+        "slot": int(np.asarray(inp["slot_ids"]).reshape(-1)[0]),
         "out": torch.empty((B, T, Hv, dv), dtype=outd, device=device),
     }
     if "parent" in inp:
@@ -67,6 +69,16 @@ def verify(d: dict, n_batch: Optional[int] = None, stream=None, with_capture: bo
                    stream)
 
 
+def verify_resume(d: dict, resume_idx, n_batch: Optional[int] = None, stream=None) -> None:
+    """gdn_verify_resume over every token of the uploaded inputs: entry b starts from capture
+    position resume_idx[b] (device int32) of the uploaded capture, or from its slot's state if < 0."""
+    T = d["qkv"].shape[1]
+    B = d["qkv"].shape[0] if n_batch is None else n_batch
+    gdn.gdn_verify_resume(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"],
+                          d["beta"], d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"],
+                          d["capture"], d["out"], T, d["slot_ids"], resume_idx, B, stream)
+
+
 def verify_tree(d: dict, stream=None) -> None:
     B, T = d["parent"].shape
     gdn.gdn_verify_tree(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"],
@@ -82,7 +94,7 @@ def prefill(d: dict, stream=None) -> None:
     if ws is None or ws.numel() * 4 < need:
         ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=d["qkv"].device)
         d["workspace"] = ws
-    slot = int(d["slot_ids"][0].item()) if "slot" not in d else d["slot"]
+    slot = d["slot"]
     gdn.gdn_prefill(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"], d["beta"],
                     d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"], d["out"], T, slot, ws,
                     ws.numel() * 4, stream)

@@ -20,7 +20,7 @@ GDN_CHAIN, GDN_TREE = 0, 1
 GDN_F_QK_NORM_SILU = 0x1
 GDN_F_CHECK_INDICES = 0x2
 
-EXPORTS = ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch", "gdn_rollback_trim",
+EXPORTS = ("gdn_verify", "gdn_verify_resume", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch", "gdn_rollback_trim",
            "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_capture_bytes", "gdn_reset",
            "gdn_snapshot", "gdn_restore", "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch",
            "gdn_graph_destroy", "gdn_linear", "gdn_last_error", "gdn_version")
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         Cp = ctypes.POINTER(gdn_capture)
         L.gdn_verify.argtypes = [D, P, P, P, P, P, P, P, P, P, P, Cp, P, I, P, I, P]
         L.gdn_verify_tree.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, Cp, P, I, P, I, P]
+        L.gdn_verify_resume.argtypes = [D, P, P, P, P, P, P, P, P, P, P, Cp, P, I, P, P, I, P]
         L.gdn_rollback.argtypes = [Cp, I, I, P]
         L.gdn_rollback_batch.argtypes = [Cp, P, P, I, P]
         L.gdn_rollback_trim.argtypes = [Cp, I, I, I, P]
@@ -160,6 +161,16 @@ def gdn_verify(dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, con
                             _p(alpha), _p(beta), _p(A_log), _p(dt_bias), _p(conv_w), _p(norm_w),
                             capture.ref if capture is not None else None, _p(out), n_tok,
                             _p(slot_ids), n_batch, _stream(stream)))
+
+
+def gdn_verify_resume(dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, conv_w, norm_w,
+                      capture: Capture, out, n_tok: int, slot_ids, resume_idx, n_batch: int,
+                      stream=None) -> None:
+    _check(lib().gdn_verify_resume(ctypes.byref(dims), _p(state), _p(conv_state), _p(qkv), _p(z),
+                                   _p(alpha), _p(beta), _p(A_log), _p(dt_bias), _p(conv_w),
+                                   _p(norm_w), capture.ref if capture is not None else None,
+                                   _p(out), n_tok, _p(slot_ids), _p(resume_idx), n_batch,
+                                   _stream(stream)))
 
 
 def gdn_verify_tree(dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, conv_w, norm_w,

@@ -120,6 +120,30 @@ int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, const void
                int32_t n_batch, void *stream);
 
 /*
+ * gdn_verify with the previous round's rollback folded into the state load.  For batch entry b
+ * with r = resume_idx[b] >= 0, the first token starts from the state after capture position r of
+ * `capture` and the conv state of window rows r+1 .. r+3: what gdn_rollback(capture, slot, r)
+ * would have restored into the slot (hf2q qwen35_target.rs, rollback_kv: the state after the
+ * accepted position; lucebox-hub internal.h, struct DeltaNetCapture: the state at offset
+ * commit_n-1 and the conv slice from commit_n).  Entries with r < 0 start from state[slot] and
+ * conv_state[slot], as gdn_verify does.  The same capture is then overwritten by this call's own
+ * positions, in the same launch: a round's pending rollback costs no copy and no launch.  The
+ * results, including state[slot] and conv_state[slot] after the last token, are bit-identical to
+ * gdn_rollback (or gdn_rollback_batch) followed by gdn_verify.
+ *   capture: required, mode GDN_CHAIN, t_cap >= n_tok; position r must hold what the previous
+ *            verify of that slot wrote (r < that call's n_tok; the library cannot check this).
+ *   resume_idx: device int32 [n_batch].  An entry with r >= t_cap is skipped: nothing of it is
+ *            written.  With GDN_F_CHECK_INDICES it is GDN_ERR_RANGE before any launch.
+ *   Every other argument as gdn_verify.  resume_idx or capture NULL -> GDN_ERR_ARG.
+ */
+int gdn_verify_resume(const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
+                      const void *z, const void *alpha, const void *beta, const float *A_log,
+                      const float *dt_bias, const float *conv_w, const float *norm_w,
+                      const gdn_capture *capture, void *out, int32_t n_tok,
+                      const int32_t *slot_ids, const int32_t *resume_idx, int32_t n_batch,
+                      void *stream);
+
+/*
  * Tree verify: n_tok draft-tree nodes per batch entry, node i hanging off parent[b][i]
  * (device int32 [n_batch][n_tok]; -1 = starts from the committed state, else 0 <= parent < i;
  * node 0 is the root and must have parent -1).  lucebox-hub internal.h, QwenGraphInputs::

@@ -45,6 +45,14 @@ int main(void)
     CHECK(gdn_verify(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, 1, NULL), GDN_ERR_RANGE); /* t_cap < n_tok */
     cap.t_cap = 16; cap.mode = GDN_TREE;
     CHECK(gdn_verify(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, 1, NULL), GDN_ERR_ARG); /* wrong mode */
+    /* verify resuming from capture positions */
+    cap.t_cap = 16; cap.mode = GDN_CHAIN;
+    CHECK(gdn_verify_resume(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, NULL, 1, NULL), GDN_ERR_ARG);
+    CHECK(gdn_verify_resume(&d, F, F, F, F, F, F, F, F, F, F, NULL, F, 4, F, F, 1, NULL), GDN_ERR_ARG);
+    CHECK(gdn_verify_resume(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 0, F, F, 1, NULL), GDN_ERR_RANGE);
+    CHECK(gdn_verify_resume(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, F, 5, NULL), GDN_ERR_RANGE);
+    cap.mode = GDN_TREE;
+    CHECK(gdn_verify_resume(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, F, 1, NULL), GDN_ERR_ARG);
     /* tree */
     CHECK(gdn_verify_tree(&d, F, F, F, F, F, F, F, F, F, F, NULL, &cap, F, 4, F, 1, NULL), GDN_ERR_ARG);
     CHECK(gdn_verify_tree(&d, F, F, F, F, F, F, F, F, F, F, F, &cap, F, 0, F, 1, NULL), GDN_ERR_RANGE);

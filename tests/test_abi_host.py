@@ -78,6 +78,29 @@ def test_verify_rejects_null_and_range_before_launch():
     assert L.gdn_verify(ctypes.byref(d), *args, ctypes.byref(cap), FAKE, 4, FAKE, 1, None) == gdn.GDN_ERR_ARG
 
 
+def test_verify_resume_validation():
+    L = _lib_or_skip()
+    d = _dims()
+    args = [FAKE] * 10
+    cap = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 16, gdn.GDN_CHAIN)
+    # resume_idx and capture are required
+    assert L.gdn_verify_resume(ctypes.byref(d), *args, ctypes.byref(cap), FAKE, 4, FAKE, None, 1,
+                               None) == gdn.GDN_ERR_ARG
+    assert L.gdn_verify_resume(ctypes.byref(d), *args, None, FAKE, 4, FAKE, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    # the rest is gdn_verify's validation
+    assert L.gdn_verify_resume(ctypes.byref(d), *args, ctypes.byref(cap), FAKE, 0, FAKE, FAKE, 1,
+                               None) == gdn.GDN_ERR_RANGE
+    assert L.gdn_verify_resume(ctypes.byref(d), *args, ctypes.byref(cap), FAKE, 4, FAKE, FAKE, 2,
+                               None) == gdn.GDN_ERR_RANGE
+    small = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 3, gdn.GDN_CHAIN)
+    assert L.gdn_verify_resume(ctypes.byref(d), *args, ctypes.byref(small), FAKE, 4, FAKE, FAKE, 1,
+                               None) == gdn.GDN_ERR_RANGE
+    tree = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 16, gdn.GDN_TREE)
+    assert L.gdn_verify_resume(ctypes.byref(d), *args, ctypes.byref(tree), FAKE, 4, FAKE, FAKE, 1,
+                               None) == gdn.GDN_ERR_ARG
+    assert "resume" in gdn.last_error() or "mode" in gdn.last_error()
+
+
 def test_rollback_validation():
     L = _lib_or_skip()
     d = _dims(n_pool=4)

@@ -1,0 +1,185 @@
+"""GPU parity of gdn_verify_resume: a verify that starts each entry from a capture position of the
+previous round (its rollback folded into the state load), against gdn_rollback_batch + gdn_verify
+bit for bit and against the oracle run from the restored state (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+from gated_deltanet_linear_verify_amd import workloads as W
+from oracle import ref
+from tests.gpu_util import out_err, rel_err, say, to_np, tol_for
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_linear_verify_amd import gdn
+    gdn.lib()  # fail loudly if the HIP library is missing
+
+
+def _dev():
+    from gated_deltanet_linear_verify_amd import device
+    return device
+
+
+def _gdn():
+    from gated_deltanet_linear_verify_amd import gdn
+    return gdn
+
+
+ACTS = ("qkv", "z", "alpha", "beta")
+
+
+def _next_round(d, inp2):
+    """Load the second round's activations into the uploaded buffers (state and capture stay)."""
+    for k in ACTS:
+        src = torch.from_numpy(np.ascontiguousarray(inp2[k], dtype=np.float32)).to(d[k].device)
+        d[k].copy_(src.to(d[k].dtype))
+
+
+def _snapshot(d, T):
+    return {"state": to_np(d["state"]), "conv_state": to_np(d["conv_state"]),
+            "out": to_np(d["out"].float()), "cap_ssm": to_np(d["cap_ssm"][:, :T]),
+            "cap_conv": to_np(d["cap_conv"][:, :3 + T])}
+
+
+def _accepted(shape, inp, rng, with_fresh=True):
+    """Per-entry accepted position of round 1 (K - trim); with_fresh marks a few entries -1 (start
+    from the slot's state, as after a fully accepted round that was already committed)."""
+    K = shape.n_tok - 1
+    acc = np.array([K - int(t) for t in inp["trims"]], dtype=np.int32)
+    if with_fresh and shape.n_batch > 1:
+        acc[rng.choice(shape.n_batch, size=max(1, shape.n_batch // 4), replace=False)] = -1
+    return acc
+
+
+RESUME_CASES = {
+    # name: (shape, seed of round 1, seed of round 2)
+    "tiny_fp32": (W.shape_with(W.TINY_VERIFY, n_pool=4, n_batch=3), 0, 1),
+    "bf16_d128_ten_slots": (W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=12, n_batch=10), 7, 8),
+    "bf16_three_launches_37": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=37, n_pool=3, n_batch=2), 3, 4),
+    "bf16_gqa4_one_token": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_kh=4, n_vh=16, n_tok=1, n_pool=3, n_batch=3),
+                            5, 6),
+}
+
+
+@pytest.mark.parametrize("name", list(RESUME_CASES))
+def test_resume_equals_rollback_then_verify_bitwise(name):
+    shape, s1, s2 = RESUME_CASES[name]
+    say(f"[resume == rollback + verify] {name}")
+    dev, gdn = _dev(), _gdn()
+    inp1, inp2 = W.make_inputs(shape, s1), W.make_inputs(shape, s2)
+    acc = _accepted(shape, inp1, np.random.default_rng(s2))
+    T = shape.n_tok
+    # reference path: verify, batched rollback of the entries with a pending rollback, verify
+    a = dev.upload(shape, inp1)
+    dev.verify(a)
+    sel = np.nonzero(acc >= 0)[0]
+    if len(sel):
+        slots = torch.from_numpy(np.asarray(inp1["slot_ids"], dtype=np.int32)[sel]).cuda()
+        gdn.gdn_rollback_batch(a["capture"], slots, torch.from_numpy(acc[sel]).cuda(), len(sel))
+    _next_round(a, inp2)
+    dev.verify(a)
+    # fused path: verify, then verify_resume from the accepted positions
+    b = dev.upload(shape, inp1)
+    dev.verify(b)
+    _next_round(b, inp2)
+    dev.verify_resume(b, torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+    ra, rb = _snapshot(a, T), _snapshot(b, T)
+    for k in ra:
+        np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
+    say(f"  {W.describe(shape)}: state, conv state, out and capture bit-identical; accepted {acc.tolist()}")
+
+
+def test_resume_against_oracle_from_the_restored_state():
+    """The resumed round equals the oracle's verify of round 2 started from the oracle's capture at
+    each accepted position of round 1 (conv window rows bit exact, the rest within tolerance)."""
+    shape = W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=6, n_batch=5)
+    say("[resume vs oracle] 5 slots, 16 tokens, bf16 d=128")
+    dev = _dev()
+    inp1, inp2 = W.make_inputs(shape, 11), W.make_inputs(shape, 12)
+    acc = _accepted(shape, inp1, np.random.default_rng(3))
+    o1 = ref.verify_pool(shape, inp1)
+    # round 2's starting point per slot: the oracle's capture at the accepted position, or its
+    # state after the whole round for entries that start from the slot's state
+    inp_r2 = dict(inp1)  # the layer's parameters and slots stay; the activations are round 2's
+    for k in ACTS:
+        inp_r2[k] = inp2[k]
+    st = np.array(inp1["state"], dtype=np.float32, copy=True)
+    cs = np.array(inp1["conv_state"], dtype=np.float32, copy=True)
+    for b in range(shape.n_batch):
+        s = int(inp1["slot_ids"][b])
+        if acc[b] >= 0:
+            st[s] = o1["cap_ssm"][s, acc[b]]
+            cs[s] = o1["cap_conv"][s][acc[b] + 1:acc[b] + 4]
+        else:
+            st[s] = o1["state"][s]
+            cs[s] = o1["conv_state"][s]
+    inp_r2["state"], inp_r2["conv_state"] = st, cs
+    o2 = ref.verify_pool(shape, inp_r2)
+    d = dev.upload(shape, inp1)
+    dev.verify(d)
+    _next_round(d, inp2)
+    dev.verify_resume(d, torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+    g_st, g_out, g_cap = to_np(d["state"]), to_np(d["out"]), to_np(d["cap_ssm"])
+    g_cc, g_cs = to_np(d["cap_conv"]), to_np(d["conv_state"])
+    worst = {"state": 0.0, "cap": 0.0, "out": 0.0}
+    for b in range(shape.n_batch):
+        s = int(inp1["slot_ids"][b])
+        np.testing.assert_array_equal(g_cc[s, :3 + shape.n_tok], o2["cap_conv"][s])
+        np.testing.assert_array_equal(g_cs[s], o2["conv_state"][s])
+        for h in range(shape.n_vh):
+            worst["state"] = max(worst["state"], rel_err(g_st[s, h], o2["state"][s, h]))
+            worst["out"] = max(worst["out"], out_err(shape, g_out[b, :, h], o2["out"][b, :, h]))
+            for t in range(shape.n_tok):
+                worst["cap"] = max(worst["cap"], rel_err(g_cap[s, t, h], o2["cap_ssm"][s, t, h]))
+    tol = tol_for(shape)
+    say(f"  worst rel err {worst} (tol {tol}); accepted {acc.tolist()}")
+    for k, v in worst.items():
+        assert v <= tol, (k, v, tol)
+
+
+def test_resume_out_of_range_entry_is_skipped():
+    """An entry whose resume position lies outside the capture writes nothing (every launch of a
+    multi-launch call skips it); the other entries run normally."""
+    shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=20, n_pool=4, n_batch=3)
+    say("[resume out of range] 3 entries, 20 tokens (two launches)")
+    dev, gdn = _dev(), _gdn()
+    inp1, inp2 = W.make_inputs(shape, 21), W.make_inputs(shape, 22)
+    d = dev.upload(shape, inp1)
+    dev.verify(d)
+    _next_round(d, inp2)
+    torch.cuda.synchronize()
+    before = _snapshot(d, shape.n_tok)
+    d["out"].fill_(7.0)
+    bad_b = 1
+    acc = np.array([3, shape.n_tok, -1], dtype=np.int32)  # entry 1: position t_cap, outside
+    dev.verify_resume(d, torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+    after = _snapshot(d, shape.n_tok)
+    s_bad = int(inp1["slot_ids"][bad_b])
+    for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
+        np.testing.assert_array_equal(after[k][s_bad], before[k][s_bad], err_msg=k)
+    assert np.all(after["out"][bad_b] == 7.0)
+    for b in (0, 2):
+        assert not np.all(after["out"][b] == 7.0)
+        s = int(inp1["slot_ids"][b])
+        assert not np.array_equal(after["state"][s], before["state"][s])
+    # with GDN_F_CHECK_INDICES the host rejects it before any launch, and nothing changes
+    e = dev.upload(shape, inp1, flags=gdn.GDN_F_CHECK_INDICES)
+    dev.verify(e)
+    torch.cuda.synchronize()
+    ref_e = _snapshot(e, shape.n_tok)
+    with pytest.raises(gdn.GdnError) as ei:
+        dev.verify_resume(e, torch.from_numpy(acc).cuda())
+    assert ei.value.code == gdn.GDN_ERR_RANGE
+    torch.cuda.synchronize()
+    now = _snapshot(e, shape.n_tok)
+    for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
+        np.testing.assert_array_equal(now[k], ref_e[k], err_msg=k)
