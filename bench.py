@@ -5,8 +5,11 @@
 A step is one spec-decode round of one GDN layer on the 64-slot workload (64 slots, 16 key /
 32 value heads, d = 128, K+1 = 16 bf16 tokens per slot, fp32 state and capture): gdn_verify
 (conv, gate, delta rule, readout, norm/gate, per-position capture) followed by gdn_rollback_batch
-with a random per-slot trim.  Inputs are seeded synthetic data already resident in HBM; input
-sets rotate so the 128 MiB state never sits in the 256 MB Infinity Cache between its uses.
+with a random per-slot trim.  The same rounds as single gdn_verify_resume launches (each slot
+starts from its accepted capture position instead of having it copied back; bit-identical
+results) are timed beside it as step_resume.  Inputs are seeded synthetic data already resident in
+HBM; input sets rotate, each with its own state and capture, so the 128 MiB state never sits in
+the 256 MB Infinity Cache between its uses.
 
 Prints one JSON line: tokens/s (value), the verify kernel's achieved HBM bandwidth against the
 8 TB/s peak (roofline, timed with HIP events on the launch stream over the timed region), and
@@ -250,26 +253,22 @@ def main() -> int:
     shape = W.MULTI_SLOT_VERIFY
     B, T = shape.n_batch, shape.n_tok
 
-    log(f"[bench] allocating {args.sets} input sets + capture for {W.describe(shape)}")
+    log(f"[bench] allocating {args.sets} input sets, each with its own capture, for {W.describe(shape)}")
     sets = []
     base = None
     for i in range(args.sets):
         inp = W.make_inputs(shape, seed=i)
         if base is None:
             base = inp
-            d = device.upload(shape, inp, fill_capture=0.0)
-        else:
-            d = device.upload(shape, inp, capture=False)
-            # one capture buffer, re-described for this set's state (rollback restores into it)
-            d["cap_ssm"], d["cap_conv"] = sets[0]["cap_ssm"], sets[0]["cap_conv"]
-            d["capture"] = gdn.Capture(d["dims"], d["cap_ssm"], d["cap_conv"], d["state"],
-                                       d["conv_state"], T, gdn.GDN_CHAIN)
+        d = device.upload(shape, inp, fill_capture=0.0)
         acc = (T - 1 - inp["trims"]).astype(np.int32)
         d["accepted"] = torch.from_numpy(acc).cuda()
+        device.verify(d)  # the round before the first timed one: every capture position is written
         sets.append(d)
     stream = torch.cuda.current_stream()
 
     def step(i: int, ev=None):
+        """One round: verify with capture, then the batched rollback copy."""
         d = sets[i % len(sets)]
         if ev is not None:
             ev[0].record(stream)
@@ -280,35 +279,48 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def step_resume(i: int, ev=None):
+        """The same round as one launch: the previous round's rollback folded into the verify."""
+        d = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        device.verify_resume(d, d["accepted"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+            ev[2].record(stream)
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    verify_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    rollback_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    def timed(fn, steps: int, warmup: int):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for i in range(steps):
+            fn(i, evs[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        verify_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        second_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        return t_start.elapsed_time(t_end) / steps, wall / steps, verify_ms, second_ms
+
+    ms_step, wall_step, verify_ms, rollback_ms = timed(step, args.steps, args.warmup)
+    rs_steps = max(20, args.steps // 2)
+    rs_ms_step, _, rs_verify_ms, _ = timed(step_resume, rs_steps, min(args.warmup, 10))
     r_avg = sum(rollback_ms) / len(rollback_ms)
-    ms_step = total_ms / args.steps
     v_avg = sum(verify_ms) / len(verify_ms)
     vb = bytemodel.verify_bytes(shape)
     rb = bytemodel.rollback_bytes(shape, B)
     achieved = vb / (v_avg * 1e-3) / 1e9
     traffic = measured_traffic()
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us), "
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall_step * 1e6:.1f} us), "
         f"verify {v_avg * 1e3:.1f} us avg (p10 {np.percentile(verify_ms, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(verify_ms, 90) * 1e3:.1f}) -> {achieved:.0f} GB/s; "
-        f"step {(vb + rb) / (ms_step * 1e-3) / 1e9:.0f} GB/s")
+        f"p90 {np.percentile(verify_ms, 90) * 1e3:.1f}) -> {achieved:.0f} GB/s, rollback {r_avg * 1e3:.1f} us; "
+        f"step {(vb + rb) / (ms_step * 1e-3) / 1e9:.0f} GB/s; resume step {rs_ms_step * 1e3:.1f} us")
 
     result = {
         "metric": METRIC,
@@ -328,12 +340,19 @@ def main() -> int:
                    "activations": "bf16", "state_and_capture": "f32",
                    "step": "gdn_verify + gdn_rollback_batch", "rotating_sets": args.sets},
         "hbm_gbps_step": (vb + rb) / (ms_step * 1e-3) / 1e9,
+        "step_resume": {"step": "gdn_verify_resume (the previous round's rollback folded into the state load)",
+                        "steps": rs_steps, "ms_per_step": rs_ms_step,
+                        "tokens_per_s": B * T / (rs_ms_step * 1e-3),
+                        "verify_us": sum(rs_verify_ms) / len(rs_verify_ms) * 1e3,
+                        "hbm_gbps_step": vb / (rs_ms_step * 1e-3) / 1e9},
         "rollback": {"us": r_avg * 1e3, "hbm_gbps": rb / (r_avg * 1e-3) / 1e9, "algorithmic_bytes": rb},
         "roofline": {"kernel": "verify_chain_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": vb,
                      "avg_launch_us": v_avg * 1e3},
     }
+    sets.clear()  # 4 x 2.2 GB of state and capture, not needed by the components
+    torch.cuda.empty_cache()
     if not args.no_components:
         result["components"] = components(args)
     if not args.no_cpu_baseline:

@@ -66,10 +66,15 @@ __device__ __forceinline__ float wave_sum(float x)
 // Infinity Cache that the next kernel pays to write back; nt alone keeps that cost off the next
 // kernel, and sc1 with it streams faster still.  The compiler does not see this store in its
 // memory-counter bookkeeping, so use it only where no later wait in the kernel depends on it.
+// Nor does it see the ISA's wait-state rule for stores of more than 64 bits of data: a VALU
+// instruction may not write the store's data registers in the cycle after it issues.  The compiler
+// does reuse those registers at once when they die with the store (seen on a final-state store
+// whose data came back corrupted), so the s_nop that it would insert for a store it knows about
+// is part of the asm.
 __device__ __forceinline__ void store_stream(void *p, f4 v)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt" : : "v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 #else
     (void)p;
     (void)v;
