@@ -24,12 +24,16 @@ def params_bytes(s: Shape) -> int:
     return 4 * (2 * s.n_vh + 4 * s.conv_channels + s.d_v)
 
 
-def verify_bytes(s: Shape, capture: bool = True) -> int:
+def verify_bytes(s: Shape, capture: bool = True, commit: bool = True) -> int:
+    """Chain verify; commit=False is the deferred commit (GDN_F_DEFER_COMMIT), which reads the state
+    and conv state but does not write them back."""
     a, o = _ab(s.act_dtype), _ab(s.out_dtype)
     C, Hv, dv, dk, T = s.conv_channels, s.n_vh, s.d_v, s.d_k, s.n_tok
     per = (T * (C * a + 2 * Hv * a + Hv * dv * (a + o)) + 8 * Hv * dv * dk + 24 * C + 4)
     if capture:
         per += 4 * T * Hv * dv * dk + 4 * (3 + T) * C
+    if not commit:
+        per -= 4 * Hv * dv * dk + 12 * C
     return s.n_batch * per + params_bytes(s)
 
 

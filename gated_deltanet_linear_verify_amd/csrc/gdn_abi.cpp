@@ -51,7 +51,7 @@ int hip_fail(hipError_t e, const char *what)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr uint32_t kKnownFlags = GDN_F_QK_NORM_SILU | GDN_F_CHECK_INDICES;
+constexpr uint32_t kKnownFlags = GDN_F_QK_NORM_SILU | GDN_F_CHECK_INDICES | GDN_F_DEFER_COMMIT;
 constexpr size_t kMaxLds = 160 * 1024;
 
 size_t channels(const gdn_dims &d) { return 2 * (size_t)d.n_kh * d.d_k + (size_t)d.n_vh * d.d_v; }
@@ -169,6 +169,8 @@ int verify_chain(const char *fn, const gdn_dims *dims, float *state, float *conv
         if (int r = check_capture(capture, GDN_CHAIN, n_tok, dims)) return r;
     if (resume && !capture)
         return fail(GDN_ERR_ARG, "%s: resuming from capture positions needs the capture", fn);
+    if ((d.flags & GDN_F_DEFER_COMMIT) && !capture)
+        return fail(GDN_ERR_ARG, "%s: GDN_F_DEFER_COMMIT needs the capture, which then holds the state", fn);
     if (gdn::verify_chain_lds_bytes(d.d_k, d.n_vh / d.n_kh, d.act_dtype == GDN_BF16) > kMaxLds)
         return fail(GDN_ERR_SHAPE, "%s: LDS tile exceeds 160 KiB", fn);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -201,6 +203,7 @@ int verify_chain(const char *fn, const gdn_dims *dims, float *state, float *conv
     a.out = out;
     a.slot_ids = slot_ids;
     a.resume = resume;
+    a.defer = (d.flags & GDN_F_DEFER_COMMIT) ? 1 : 0;
     gdn::LaunchCfg c{d.act_dtype == GDN_BF16, d.out_dtype == GDN_BF16, (d.flags & GDN_F_QK_NORM_SILU) != 0};
     if (hipError_t e = gdn::launch_verify_chain(a, c, st))
         return fail(GDN_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));

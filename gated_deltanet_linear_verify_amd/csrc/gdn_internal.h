@@ -28,6 +28,8 @@ struct VerifyArgs {
                             // state); NULL: every entry starts from the slot's state
     const int32_t *parent;  // tree only
     int32_t n_batch;
+    int32_t defer;  // chain verify with capture: leave state and conv_state untouched (the state
+                    // after the last token stays at its capture position)
 };
 
 struct LaunchCfg {

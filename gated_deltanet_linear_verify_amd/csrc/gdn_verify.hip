@@ -86,6 +86,8 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     // state after capture position ra of this same capture, written by that round's verify, instead
     // of from the slot's state.  This workgroup reads only its own heads' and channels' slices of
     // position ra, and every read lands before its first capture store.
+    // With the commit deferred, a launch after the first continues from the previous launch's last
+    // capture position in the same way, since the state buffer is not written.
     int ra = -1;
     if constexpr (CAP) {
         if (a.resume) {
@@ -93,7 +95,9 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
             if (r >= a.t_cap) return;  // outside the capture: every launch skips the entry (uniform)
             if (a.t0 == 0) ra = r;
         }
+        if (a.defer && a.t0 > 0) ra = a.t0 - 1;
     }
+    const bool commit = !(CAP && a.defer);  // write the state and conv state after the last token
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     float *ks = reinterpret_cast<float *>(smem_raw);  // [TT][D]
@@ -229,9 +233,11 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
             }
             // conv state after the launch's last token (xext rows nt .. nt+2); this thread was the
             // only reader of these elements
-            cs_s[gc] = x0;
-            cs_s[(size_t)C + gc] = x1;
-            cs_s[(size_t)2 * C + gc] = x2;
+            if (commit) {
+                cs_s[gc] = x0;
+                cs_s[(size_t)C + gc] = x1;
+                cs_s[(size_t)2 * C + gc] = x2;
+            }
         }
     }
     __syncthreads();
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
         }
     }
     // ---- final state (address rebuilt from a wave-uniform base so none is kept across the loop)
-    {
+    if (commit) {
         uint32_t off = (uint32_t)(row0 * D + cg * 4);
         asm volatile("" : "+v"(off));
         float *sp = a.state + ((size_t)s * a.n_vh + h) * hd;

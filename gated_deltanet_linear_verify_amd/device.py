@@ -69,12 +69,13 @@ def verify(d: dict, n_batch: Optional[int] = None, stream=None, with_capture: bo
                    stream)
 
 
-def verify_resume(d: dict, resume_idx, n_batch: Optional[int] = None, stream=None) -> None:
+def verify_resume(d: dict, resume_idx, n_batch: Optional[int] = None, stream=None, dims=None) -> None:
     """gdn_verify_resume over every token of the uploaded inputs: entry b starts from capture
-    position resume_idx[b] (device int32) of the uploaded capture, or from its slot's state if < 0."""
+    position resume_idx[b] (device int32) of the uploaded capture, or from its slot's state if < 0.
+    ``dims`` replaces the uploaded dims (e.g. the same shape with other flags)."""
     T = d["qkv"].shape[1]
     B = d["qkv"].shape[0] if n_batch is None else n_batch
-    gdn.gdn_verify_resume(d["dims"], d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"],
+    gdn.gdn_verify_resume(d["dims"] if dims is None else dims, d["state"], d["conv_state"], d["qkv"], d["z"], d["alpha"],
                           d["beta"], d["A_log"], d["dt_bias"], d["conv_w"], d["norm_w"],
                           d["capture"], d["out"], T, d["slot_ids"], resume_idx, B, stream)
 

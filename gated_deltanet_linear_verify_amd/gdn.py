@@ -19,6 +19,7 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_CHAIN, GDN_TREE = 0, 1
 GDN_F_QK_NORM_SILU = 0x1
 GDN_F_CHECK_INDICES = 0x2
+GDN_F_DEFER_COMMIT = 0x4
 
 EXPORTS = ("gdn_verify", "gdn_verify_resume", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch", "gdn_rollback_trim",
            "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_capture_bytes", "gdn_reset",

@@ -73,6 +73,15 @@ enum gdn_capture_mode { GDN_CHAIN = 0, GDN_TREE = 1 };
 /* Copy device index arrays (slot_ids, parent, rollback slots / indices) to the host and
  * validate them before launching.  Synchronises with `stream`. */
 #define GDN_F_CHECK_INDICES 0x2u
+/* Chain verify with capture (gdn_verify, gdn_verify_resume) leaves state[slot] and
+ * conv_state[slot] untouched, as tree verify does: the state after the last token is capture
+ * position n_tok-1 and its conv state window rows n_tok .. n_tok+2.  The caller commits a
+ * position with gdn_rollback / gdn_rollback_batch, or passes it to the next round's
+ * gdn_verify_resume, which reads it from the capture; so a round that accepts every token also
+ * ends in a commit, unlike the pages' trim-0 early return (hf2q qwen35_target.rs, rollback_kv).
+ * A call of more than one launch (n_tok > 16) carries the state between its launches through its
+ * own capture positions.  Without a capture it is GDN_ERR_ARG; other calls ignore it. */
+#define GDN_F_DEFER_COMMIT 0x4u
 
 typedef struct gdn_dims {
     int32_t n_kh;      /* key heads H_k */

@@ -45,6 +45,9 @@ int main(void)
     CHECK(gdn_verify(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, 1, NULL), GDN_ERR_RANGE); /* t_cap < n_tok */
     cap.t_cap = 16; cap.mode = GDN_TREE;
     CHECK(gdn_verify(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, 1, NULL), GDN_ERR_ARG); /* wrong mode */
+    /* a deferred commit needs the capture */
+    gdn_dims defer = d; defer.flags = GDN_F_DEFER_COMMIT;
+    CHECK(gdn_verify(&defer, F, F, F, F, F, F, F, F, F, F, NULL, F, 4, F, 1, NULL), GDN_ERR_ARG);
     /* verify resuming from capture positions */
     cap.t_cap = 16; cap.mode = GDN_CHAIN;
     CHECK(gdn_verify_resume(&d, F, F, F, F, F, F, F, F, F, F, &cap, F, 4, F, NULL, 1, NULL), GDN_ERR_ARG);

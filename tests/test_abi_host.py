@@ -99,6 +99,10 @@ def test_verify_resume_validation():
     assert L.gdn_verify_resume(ctypes.byref(d), *args, ctypes.byref(tree), FAKE, 4, FAKE, FAKE, 1,
                                None) == gdn.GDN_ERR_ARG
     assert "resume" in gdn.last_error() or "mode" in gdn.last_error()
+    # a deferred commit keeps the state in the capture, so it needs one
+    dd = _dims(flags=gdn.GDN_F_DEFER_COMMIT)
+    assert L.gdn_verify(ctypes.byref(dd), *args, None, FAKE, 4, FAKE, 1, None) == gdn.GDN_ERR_ARG
+    assert "DEFER" in gdn.last_error()
 
 
 def test_rollback_validation():

@@ -25,6 +25,9 @@ def test_verify_bytes_match_hand_totals():
     cap = 4 * 64 * 16 * 32 * 128 * 128
     assert cap == 2 * 1024 ** 3
     assert abs(cap / B.verify_bytes(W.MULTI_SLOT_VERIFY) - 0.858) < 1e-3
+    # a deferred commit writes neither the 64 slots' states (2 MiB each) nor their conv states
+    # (3 rows of 8192 channels): 2,502,165,504 - 64 * (2,097,152 + 98,304)
+    assert B.verify_bytes(W.MULTI_SLOT_VERIFY, commit=False) == 2_361_656_320
 
 
 def test_copy_and_prefill_bytes():

@@ -183,3 +183,77 @@ def test_resume_out_of_range_entry_is_skipped():
     now = _snapshot(e, shape.n_tok)
     for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
         np.testing.assert_array_equal(now[k], ref_e[k], err_msg=k)
+
+
+DEFER_CASES = {
+    "tiny_fp32": (W.shape_with(W.TINY_VERIFY, n_pool=4, n_batch=3), 40, 41, 42),
+    "bf16_d128_ten_slots": (W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=12, n_batch=10), 43, 44, 45),
+    "bf16_three_launches_37": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=37, n_pool=3, n_batch=2), 46, 47, 48),
+}
+
+
+@pytest.mark.parametrize("name", list(DEFER_CASES))
+def test_deferred_commit_leaves_the_state_and_matches_the_commit(name):
+    """GDN_F_DEFER_COMMIT: out and capture bit-identical to a committing verify, state and conv
+    state untouched; a rollback afterwards gives the committing path's rollback, bit for bit."""
+    shape, s1, _, _ = DEFER_CASES[name]
+    say(f"[deferred commit] {name}")
+    dev, gdn = _dev(), _gdn()
+    inp = W.make_inputs(shape, s1)
+    acc = _accepted(shape, inp, np.random.default_rng(s1), with_fresh=False)
+    a = dev.upload(shape, inp)
+    dev.verify(a)
+    b = dev.upload(shape, inp, flags=gdn.GDN_F_DEFER_COMMIT)
+    dev.verify(b)
+    torch.cuda.synchronize()
+    ra, rb = _snapshot(a, shape.n_tok), _snapshot(b, shape.n_tok)
+    for k in ("out", "cap_ssm", "cap_conv"):
+        np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
+    np.testing.assert_array_equal(rb["state"], np.asarray(inp["state"], dtype=np.float32))
+    np.testing.assert_array_equal(rb["conv_state"], np.asarray(inp["conv_state"], dtype=np.float32))
+    slots = torch.from_numpy(np.asarray(inp["slot_ids"], dtype=np.int32)).cuda()
+    acc_t = torch.from_numpy(acc).cuda()
+    for d in (a, b):
+        gdn.gdn_rollback_batch(d["capture"], slots, acc_t, shape.n_batch)
+    torch.cuda.synchronize()
+    ra, rb = _snapshot(a, shape.n_tok), _snapshot(b, shape.n_tok)
+    for k in ("state", "conv_state"):
+        np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
+
+
+@pytest.mark.parametrize("name", list(DEFER_CASES))
+def test_deferred_resume_rounds_equal_committed_rounds(name):
+    """Three rounds of the resume protocol with the commit deferred (verify, then verify_resume
+    from each accepted position, a final rollback to materialise the state) against three rounds
+    of verify + rollback: every output, the last capture and the committed state bit-identical."""
+    shape, s1, s2, s3 = DEFER_CASES[name]
+    say(f"[deferred resume rounds] {name}")
+    dev, gdn = _dev(), _gdn()
+    rounds = [W.make_inputs(shape, s) for s in (s1, s2, s3)]
+    accs = [_accepted(shape, r, np.random.default_rng(7 + i), with_fresh=False) for i, r in enumerate(rounds)]
+    slots = torch.from_numpy(np.asarray(rounds[0]["slot_ids"], dtype=np.int32)).cuda()
+    a = dev.upload(shape, rounds[0])
+    b = dev.upload(shape, rounds[0], flags=gdn.GDN_F_DEFER_COMMIT)
+    outs_a, outs_b = [], []
+    for i, inp in enumerate(rounds):
+        acc_t = torch.from_numpy(accs[i]).cuda()
+        if i > 0:
+            _next_round(a, inp)
+            _next_round(b, inp)
+        dev.verify(a)
+        gdn.gdn_rollback_batch(a["capture"], slots, acc_t, shape.n_batch)
+        if i == 0:
+            dev.verify(b)
+        else:
+            dev.verify_resume(b, torch.from_numpy(accs[i - 1]).cuda())
+        torch.cuda.synchronize()
+        outs_a.append(to_np(a["out"].float()))
+        outs_b.append(to_np(b["out"].float()))
+    gdn.gdn_rollback_batch(b["capture"], slots, torch.from_numpy(accs[-1]).cuda(), shape.n_batch)
+    torch.cuda.synchronize()
+    for i in range(len(rounds)):
+        np.testing.assert_array_equal(outs_b[i], outs_a[i], err_msg=f"out of round {i}")
+    ra, rb = _snapshot(a, shape.n_tok), _snapshot(b, shape.n_tok)
+    for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
+        np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
+    say(f"  {W.describe(shape)}: three rounds bit-identical")
