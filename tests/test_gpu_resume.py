@@ -48,7 +48,7 @@ def _snapshot(d, T):
 
 
 def _accepted(shape, inp, rng, with_fresh=True):
-    """Per-entry accepted position of round 1 (K - trim); with_fresh marks a few entries -1 (start
+    """Per-entry accepted position of the first verify round (K - trim); with_fresh marks a few entries -1 (start
     from the slot's state, as after a fully accepted round that was already committed)."""
     K = shape.n_tok - 1
     acc = np.array([K - int(t) for t in inp["trims"]], dtype=np.int32)
@@ -58,7 +58,7 @@ def _accepted(shape, inp, rng, with_fresh=True):
 
 
 RESUME_CASES = {
-    # name: (shape, seed of round 1, seed of round 2)
+    # name: (shape, seed of the first verify round, seed of the second)
     "tiny_fp32": (W.shape_with(W.TINY_VERIFY, n_pool=4, n_batch=3), 0, 1),
     "bf16_d128_ten_slots": (W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=12, n_batch=10), 7, 8),
     "bf16_three_launches_37": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=37, n_pool=3, n_batch=2), 3, 4),
@@ -97,17 +97,18 @@ def test_resume_equals_rollback_then_verify_bitwise(name):
 
 
 def test_resume_against_oracle_from_the_restored_state():
-    """The resumed round equals the oracle's verify of round 2 started from the oracle's capture at
-    each accepted position of round 1 (conv window rows bit exact, the rest within tolerance)."""
+    """The resumed round equals the oracle's verify of the second round started from the oracle's
+    capture at each accepted position of the first (conv window rows bit exact, the rest within
+    tolerance)."""
     shape = W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=6, n_batch=5)
     say("[resume vs oracle] 5 slots, 16 tokens, bf16 d=128")
     dev = _dev()
     inp1, inp2 = W.make_inputs(shape, 11), W.make_inputs(shape, 12)
     acc = _accepted(shape, inp1, np.random.default_rng(3))
     o1 = ref.verify_pool(shape, inp1)
-    # round 2's starting point per slot: the oracle's capture at the accepted position, or its
+    # the second round's starting point per slot: the oracle's capture at the accepted position, or its
     # state after the whole round for entries that start from the slot's state
-    inp_r2 = dict(inp1)  # the layer's parameters and slots stay; the activations are round 2's
+    inp_r2 = dict(inp1)  # the layer's parameters and slots stay; the activations are the second round's
     for k in ACTS:
         inp_r2[k] = inp2[k]
     st = np.array(inp1["state"], dtype=np.float32, copy=True)
