@@ -283,6 +283,22 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
 #pragma unroll
             for (int e = 0; e < 4; ++e) R0[i][4 * c4 + e] = v[e];
         }
+    // z of the nodes this thread's 16-lane group normalises in the epilogue, loaded now: loaded
+    // after the node loop, it would wait behind the whole capture stream on the one memory counter
+    constexpr int EPL = D / 16;                         // z elements per lane and node
+    constexpr int NGRP = NW * 4;                        // 16-lane groups
+    constexpr int NPG = (kTreeMaxNodes + NGRP - 1) / NGRP;  // nodes per group
+    word_t zr[NPG][EPL];
+#pragma unroll
+    for (int k = 0; k < NPG; ++k) {
+        const int zn = min((tid >> 4) + k * NGRP, T - 1);  // past the last node: a valid row, unused
+        const word_t *zp = static_cast<const word_t *>(a.z) + (((size_t)b * T + zn) * a.n_vh + h) * D + cg * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) zr[k][e] = zp[e];
+    }
+    float nwr[EPL];  // the norm weights of this lane's columns, for the same reason
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) nwr[e] = a.norm_w[cg * EPL + e];
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): raw rows landed, registers loaded
     asm volatile("" : "+v"(al_raw), "+v"(be_raw), "+v"(par_raw), "+v"(alog), "+v"(dtb));  // nothing above
     auto word_f32 = [](uint32_t w) -> float {
@@ -421,10 +437,11 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     __syncthreads();
 
     // ================= epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) =================
-    constexpr int EPL = D / 16;
-    const int grp = tid >> 4, ngrp = nthr >> 4;
-#pragma unroll 1
-    for (int n = grp; n < T; n += ngrp) {
+    const int grp = tid >> 4;
+#pragma unroll
+    for (int k = 0; k < NPG; ++k) {
+        const int n = grp + k * NGRP;
+        if (n >= T) break;  // uniform over the 16-lane group
         const float *osrc = os + n * D;
         float ov[EPL];
         float ss = 0.f;
@@ -438,8 +455,8 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         const size_t base = (((size_t)b * T + n) * a.n_vh + h) * D + cg * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const float zz = load_act<ACT_BF16>(a.z, base + e);
-            const float y = ov[e] * inv * a.norm_w[cg * EPL + e] * (zz * sigmoid_f(zz));
+            const float zz = word_f32(zr[k][e]);
+            const float y = ov[e] * inv * nwr[e] * (zz * sigmoid_f(zz));
             if constexpr (OUT_BF16)
                 static_cast<uint16_t *>(a.out)[base + e] = f32_to_bf16(y);
             else
