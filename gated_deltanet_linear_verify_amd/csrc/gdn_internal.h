@@ -30,6 +30,7 @@ struct VerifyArgs {
     int32_t n_batch;
     int32_t defer;  // chain verify with capture: leave state and conv_state untouched (the state
                     // after the last token stays at its capture position)
+    int32_t hpw;    // chain verify: value heads per workgroup, set by the launcher (H_v/H_k, or 1)
 };
 
 struct LaunchCfg {

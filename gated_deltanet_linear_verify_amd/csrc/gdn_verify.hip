@@ -44,7 +44,7 @@ __device__ __forceinline__ void store_cap(float *p, f4 v) { store_stream(p, v); 
 constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr int kTargetWavesPerCu = 8;
 
-// LDS carve-up of one workgroup (R value heads per key head, act_t = activation storage type).
+// LDS carve-up of one workgroup (R value heads in the workgroup, act_t = activation storage type).
 template <int D, typename act_t>
 struct VerifyLds {
     static constexpr int TT = kTokenTile;
@@ -60,16 +60,18 @@ struct VerifyLds {
     }
 };
 
-template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN, bool CAP>
+// NW: waves per value head (4 at d = 128 with all of a key head's value heads in the workgroup,
+// 8 with one value head per workgroup: half the rows per lane, the same arithmetic per row).
+template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN, bool CAP, int NW>
 __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
     using L = VerifyLds<D, act_t>;
-    constexpr int NW = WavesPerHead<D>::value;
     using G = Geo<D, NW>;
     constexpr int TT = kTokenTile;
     constexpr int VEC = 16 / (int)sizeof(act_t);  // activations per 16-byte load
-    const int R = a.n_vh / a.n_kh;
+    const int R = a.n_vh / a.n_kh;  // value heads per key head
+    const int HW = a.hpw;           // value heads of this workgroup: R, or 1 (few batch entries)
     const int nthr = blockDim.x;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -77,9 +79,16 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     const int hl = wave / NW, wih = wave % NW;
     const int rg = lane >> 4, cg = lane & 15;
 
-    const int b = blockIdx.x / a.n_kh;
-    const int hk = blockIdx.x % a.n_kh;
-    const int h = hk * R + hl;
+    const int gpb = a.n_vh / HW;             // workgroups per batch entry
+    const int b = blockIdx.x / gpb;
+    const int h0 = (blockIdx.x % gpb) * HW;  // first value head of the workgroup
+    const int hk = h0 / R;
+    const int h = h0 + hl;
+    // With one value head per workgroup the key head's q / k channels are shared: only its first
+    // workgroup writes them to the conv window, and their conv state is written after the launch
+    // (launch_qk_conv_state), as every workgroup of the key head reads it here.
+    const bool lead = h0 % R == 0;
+    const bool qk_state = HW == R;
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the workgroup
     // A rollback left pending by the previous round: the first launch of the call starts from the
@@ -102,25 +111,25 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     float *ks = reinterpret_cast<float *>(smem_raw);  // [TT][D]
     float *qs = ks + TT * D;                            // [TT][D]
-    float *vs = qs + TT * D;                            // [R][TT][D]   rows in perm order
-    float *os = vs + R * TT * D;                        // [R][TT][D]   rows in perm order
+    float *vs = qs + TT * D;                            // [HW][TT][D]  rows in perm order
+    float *os = vs + HW * TT * D;                       // [HW][TT][D]  rows in perm order
     act_t *raw = reinterpret_cast<act_t *>(os);         // [TT][nch]    staged qkv rows (prologue only)
-    act_t *zs = reinterpret_cast<act_t *>(reinterpret_cast<unsigned char *>(os) + L::region(R));  // [TT][R*D]
-    float *rb = reinterpret_cast<float *>(zs + R * TT * D);  // [R][TT][2]   (rho, beta)
-    float *nws = rb + R * TT * 2 + TT;                         // [D]          norm_w
+    act_t *zs = reinterpret_cast<act_t *>(reinterpret_cast<unsigned char *>(os) + L::region(HW));  // [TT][HW*D]
+    float *rb = reinterpret_cast<float *>(zs + HW * TT * D);  // [HW][TT][2]  (rho, beta)
+    float *nws = rb + HW * TT * 2 + TT;                         // [D]          norm_w
 
     const int C = a.C;
     const int T = a.T;    // tokens of the whole call: the row stride of qkv, z, alpha, beta, out
     const int t0 = a.t0;  // first token of this launch
     const int nt = a.nt;  // tokens of this launch, 1 .. TT
-    const int nch = (2 + R) * D;
-    const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + hk * R * D;
+    const int nch = (2 + HW) * D;
+    const int q0 = hk * D, k0 = a.n_kh * D + hk * D, v0 = 2 * a.n_kh * D + h0 * D;
     float *cs_s = a.conv_state + (size_t)s * 3 * C;
     // conv state the launch starts from: the slot's, or capture window rows ra+1 .. ra+3
     const float *cs_src = ra >= 0 ? a.cap_conv + ((size_t)s * (3 + a.t_cap) + ra + 1) * C : cs_s;
     const size_t hd = (size_t)D * D;
     const act_t *qkv_b = static_cast<const act_t *>(a.qkv) + ((size_t)b * T + t0) * C;
-    const act_t *z_b = static_cast<const act_t *>(a.z) + ((size_t)b * T + t0) * a.n_vh * D + (size_t)hk * R * D;
+    const act_t *z_b = static_cast<const act_t *>(a.z) + ((size_t)b * T + t0) * a.n_vh * D + (size_t)h0 * D;
     auto to_f32 = [](act_t x) -> float {
         if constexpr (ACT_BF16)
             return bf16_to_f32(x);
@@ -138,19 +147,19 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
         const int r = it / nvr, lc = (it % nvr) * VEC;
         lds_dma16(qkv_b + (uint32_t)(r * C + gchan(lc)), raw + it * VEC);
     }
-    // z: [nt][R*D] is contiguous in HBM and in LDS
-    for (int it = tid; it < nt * R * D / VEC; it += nthr) {
-        const int e0 = it * VEC, t = e0 / (R * D), within = e0 % (R * D);
+    // z: [nt][HW*D] is contiguous in HBM and in LDS
+    for (int it = tid; it < nt * HW * D / VEC; it += nthr) {
+        const int e0 = it * VEC, t = e0 / (HW * D), within = e0 % (HW * D);
         lds_dma16(z_b + (uint32_t)(t * a.n_vh * D + within), zs + e0);
     }
     // alpha and beta: at most one (token, head) per thread, with the head's A_log and dt_bias.  The
-    // loads sit outside any branch (threads past nt * R load a valid entry they never use) and
+    // loads sit outside any branch (threads past nt * HW load a valid entry they never use) and
     // nothing is computed from them before the wait below: a bf16 conversion, or a branch join
     // over a loaded register, would make the compiler wait for every load issued so far, the qkv
     // and z transfers included, before the state loads even start.
-    const int ab_i = min(tid, nt * R - 1);
-    const int ab_h = hk * R + ab_i % R;
-    const size_t ab_tok = ((size_t)b * T + t0 + ab_i / R) * a.n_vh + ab_h;
+    const int ab_i = min(tid, nt * HW - 1);
+    const int ab_h = h0 + ab_i % HW;
+    const size_t ab_tok = ((size_t)b * T + t0 + ab_i / HW) * a.n_vh + ab_h;
     using word_t = typename std::conditional<ACT_BF16, uint16_t, uint32_t>::type;  // bf16 or fp32 bits
     uint32_t al_raw = static_cast<const word_t *>(a.alpha)[ab_tok];
     uint32_t be_raw = static_cast<const word_t *>(a.beta)[ab_tok];
@@ -192,8 +201,8 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
             return __builtin_bit_cast(float, w);
     };
     if (tid < D) nws[tid] = nw;
-    if (tid < nt * R) {
-        const int t = tid / R, hh = tid % R;
+    if (tid < nt * HW) {
+        const int t = tid / HW, hh = tid % HW;
         const float g = -expf(alog) * softplus_f(word_f32(al_raw) + dtb);
         rb[(hh * TT + t) * 2 + 0] = expf(g);
         rb[(hh * TT + t) * 2 + 1] = word_f32(be_raw);
@@ -215,8 +224,9 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
                 dst = vs + ((lc - 2 * D) / D) * TT * D + G::perm((lc - 2 * D) % D);
             float x0 = csv[it][0], x1 = csv[it][1], x2 = csv[it][2];
             const f4 w = wv[it];
+            const bool own = lc >= 2 * D || lead;  // this workgroup writes the channel's window
             float *cc = CAP ? a.cap_conv + (size_t)s * (3 + a.t_cap) * C + gc : nullptr;
-            if (CAP && t0 == 0) {  // the window starts with the conv state the call began from
+            if (CAP && t0 == 0 && own) {  // the window starts with the conv state the call began from
                 cc[0] = x0;
                 cc[(size_t)C] = x1;
                 cc[(size_t)2 * C] = x2;
@@ -226,14 +236,14 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
                 float y = conv4(w, x0, x1, x2, x3);
                 if constexpr (QKN) y = y * sigmoid_f(y);
                 dst[t * D] = y;
-                if constexpr (CAP) cc[(size_t)(t0 + t + 3) * C] = x3;
+                if (CAP && own) cc[(size_t)(t0 + t + 3) * C] = x3;
                 x0 = x1;
                 x1 = x2;
                 x2 = x3;
             }
             // conv state after the launch's last token (xext rows nt .. nt+2); this thread was the
             // only reader of these elements
-            if (commit) {
+            if (commit && (lc >= 2 * D || qk_state)) {
                 cs_s[gc] = x0;
                 cs_s[(size_t)C + gc] = x1;
                 cs_s[(size_t)2 * C + gc] = x2;
@@ -291,8 +301,8 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     constexpr int EPL = D / 16;  // 16 lanes per (head, token) row
     const int grp = tid >> 4, ngrp = nthr >> 4;
 #pragma unroll 1
-    for (int row = grp; row < R * nt; row += ngrp) {
-        const int hh = row / nt, t = row % nt, h2 = hk * R + hh;
+    for (int row = grp; row < HW * nt; row += ngrp) {
+        const int hh = row / nt, t = row % nt, h2 = h0 + hh;
         const float *osrc = os + (hh * TT + t) * D;
         float ov[EPL];
         float ss = 0.f;
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
         ss = row16_sum(ss);
         const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
         const size_t base = (((size_t)b * T + t0 + t) * a.n_vh + h2) * D + cg * EPL;
-        const act_t *zrow = zs + t * R * D + hh * D + cg * EPL;
+        const act_t *zrow = zs + t * HW * D + hh * D + cg * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const float zz = to_f32(zrow[e]);
@@ -325,15 +335,60 @@ size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16)
     return act_bf16 ? VerifyLds<64, uint16_t>::total(ratio) : VerifyLds<64, float>::total(ratio);
 }
 
+// Conv state of the key heads' q / k channels after a launch that ran one value head per
+// workgroup: rows nt .. nt+2 of the launch's conv input (the conv state's own rows while nt < 3,
+// then its tokens), the values the verify kernel keeps for the channels it owns.  Rows are
+// written in order: row r takes row nt + r > r, which is still the old one.
+template <bool ACT_BF16>
+__global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
+{
+    using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
+    const int b = blockIdx.y;
+    const int s = a.slot_ids[b];
+    if (s < 0 || s >= a.n_pool) return;  // uniform over the block, as in the verify kernel
+    const int ch = blockIdx.x * blockDim.x + threadIdx.x;  // q | k channels are 0 .. 2 H_k d - 1
+    if (ch >= 2 * a.n_kh * a.d) return;
+    const size_t C = (size_t)a.C;
+    float *cs = a.conv_state + (size_t)s * 3 * C + ch;
+    const act_t *x = static_cast<const act_t *>(a.qkv) + ((size_t)b * a.T + a.t0) * C + ch;
+    for (int r = 0; r < 3; ++r) {
+        const int j = a.nt + r;
+        float v;
+        if (j < 3) {
+            v = cs[(size_t)j * C];
+        } else {
+            if constexpr (ACT_BF16)
+                v = bf16_to_f32(x[(size_t)(j - 3) * C]);
+            else
+                v = x[(size_t)(j - 3) * C];
+        }
+        cs[(size_t)r * C] = v;
+    }
+}
+
+// Value heads per workgroup.  With few batch entries a workgroup per key head leaves most CUs idle
+// and each one streams its heads' whole capture through one store path (~64 B per clock), so then
+// each value head gets its own workgroup.  Not when resuming or deferring the commit: those read the
+// key head's q / k rows of the conv window, which the first workgroup of the key head rewrites.
+constexpr int kSplitMaxWorkgroups = 64;
+static int heads_per_workgroup(const VerifyArgs &a)
+{
+    const int R = a.n_vh / a.n_kh;
+    if (R == 1 || a.resume || a.defer) return R;
+    return (long)a.n_batch * a.n_kh <= kSplitMaxWorkgroups ? 1 : R;
+}
+
 // One launch covers at most kTokenTile tokens; longer chains are consecutive launches on the same
 // stream, each starting from the state and conv state the previous one left.
 template <int D, bool AB, bool OB, bool QKN, bool CAP>
 static hipError_t launch_t(const VerifyArgs &a0, hipStream_t stream)
 {
     const int R = a0.n_vh / a0.n_kh;
-    const int threads = R * WavesPerHead<D>::value * 64;
-    size_t lds = verify_chain_lds_bytes(D, R, AB);
-    const int waves = R * WavesPerHead<D>::value;
+    const int HW = heads_per_workgroup(a0);
+    const int nw = HW < R ? 2 * WavesPerHead<D>::value : WavesPerHead<D>::value;  // waves per value head
+    const int threads = HW * nw * 64;
+    size_t lds = verify_chain_lds_bytes(D, HW, AB);
+    const int waves = HW * nw;
     const int wgs_per_cu = waves >= kTargetWavesPerCu ? 1 : kTargetWavesPerCu / waves;
     const size_t lds_cap = kLdsPerCu / (wgs_per_cu + 1) + 16;  // wgs_per_cu + 1 workgroups no longer fit
     if (CAP && lds < lds_cap) lds = lds_cap;  // without capture stores more resident waves only help
@@ -341,9 +396,19 @@ static hipError_t launch_t(const VerifyArgs &a0, hipStream_t stream)
         VerifyArgs a = a0;
         a.t0 = t0;
         a.nt = a0.T - t0 < kTokenTile ? a0.T - t0 : kTokenTile;
-        hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP>), dim3(a.n_batch * a.n_kh), dim3(threads), lds,
-                           stream, a);
+        a.hpw = HW;
+        if (HW < R)
+            hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP, 2 * WavesPerHead<D>::value>),
+                               dim3(a.n_batch * (a.n_vh / HW)), dim3(threads), lds, stream, a);
+        else
+            hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP, WavesPerHead<D>::value>),
+                               dim3(a.n_batch * (a.n_vh / HW)), dim3(threads), lds, stream, a);
         if (hipError_t e = hipGetLastError()) return e;
+        if (HW < R) {
+            const unsigned blocks = (unsigned)((2 * a.n_kh * D + 255) / 256);
+            hipLaunchKernelGGL(qk_conv_state_kernel<AB>, dim3(blocks, a.n_batch), dim3(256), 0, stream, a);
+            if (hipError_t e = hipGetLastError()) return e;
+        }
     }
     return hipSuccess;
 }
