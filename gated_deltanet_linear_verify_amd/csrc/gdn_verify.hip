@@ -369,12 +369,15 @@ __global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
 // Value heads per workgroup.  With few batch entries a workgroup per key head leaves most CUs idle
 // and each one streams its heads' whole capture through one store path (~64 B per clock), so then
 // each value head gets its own workgroup.  Not when resuming or deferring the commit: those read the
-// key head's q / k rows of the conv window, which the first workgroup of the key head rewrites.
+// key head's q / k rows of the conv window, which the first workgroup of the key head rewrites.  Not
+// below 3 tokens either, where the second launch costs more than the split saves (measured at 1 and
+// 4 slots: even at 2 tokens, 9.4 against 11.1 us at 1).
 constexpr int kSplitMaxWorkgroups = 64;
+constexpr int kSplitMinTokens = 3;
 static int heads_per_workgroup(const VerifyArgs &a)
 {
     const int R = a.n_vh / a.n_kh;
-    if (R == 1 || a.resume || a.defer) return R;
+    if (R == 1 || a.resume || a.defer || a.T < kSplitMinTokens) return R;
     return (long)a.n_batch * a.n_kh <= kSplitMaxWorkgroups ? 1 : R;
 }
 

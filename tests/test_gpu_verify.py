@@ -70,6 +70,11 @@ CASES = {
     "single_slot_verify": (W.SINGLE_SLOT_VERIFY, 0),
     "ragged_three_tiles": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=37, n_pool=3, n_batch=2), 0),
     "one_token": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=1, n_pool=2, n_batch=2), 0),
+    # one value head per workgroup, and a second launch of one token: the key heads' q / k conv
+    # state is rebuilt from the old rows after it
+    "split_tail_of_one_token": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=17, n_pool=2, n_batch=1), 0),
+    "split_gqa4_tail_of_two": (W.shape_with(W.SINGLE_SLOT_VERIFY, n_kh=4, n_vh=16, n_tok=18, n_pool=3,
+                                            n_batch=2), 0),
     "two_tokens_conv_from_state": (W.shape_with(W.TINY_VERIFY, n_tok=2, n_pool=4, n_batch=3), 0),
     "fp32_act_bf16_out": (W.shape_with(W.TINY_VERIFY, out_dtype=W.BF16, n_tok=17), 0),
     "bf16_act_fp32_out": (W.shape_with(W.SINGLE_SLOT_VERIFY, out_dtype=W.F32, n_vh=16, n_kh=16), 0),
