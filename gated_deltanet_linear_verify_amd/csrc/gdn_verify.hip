@@ -86,7 +86,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     const int h = h0 + hl;
     // With one value head per workgroup the key head's q / k channels are shared: only its first
     // workgroup writes them to the conv window, and their conv state is written after the launch
-    // (launch_qk_conv_state), as every workgroup of the key head reads it here.
+    // (qk_conv_state_kernel), as every workgroup of the key head reads it here.
     const bool lead = h0 % R == 0;
     const bool qk_state = HW == R;
     const int s = a.slot_ids[b];
@@ -370,8 +370,8 @@ __global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
 // and each one streams its heads' whole capture through one store path (~64 B per clock), so then
 // each value head gets its own workgroup.  Not when resuming or deferring the commit: those read the
 // key head's q / k rows of the conv window, which the first workgroup of the key head rewrites.  Not
-// below 3 tokens either, where the second launch costs more than the split saves (measured at 1 and
-// 4 slots: even at 2 tokens, 9.4 against 11.1 us at 1).
+// below 3 tokens either: there the second launch costs more than the split saves (one slot: 9.4
+// against 11.1 us at 1 token, even at 2, ahead from 3 on; likewise at 4 slots).
 constexpr int kSplitMaxWorkgroups = 64;
 constexpr int kSplitMinTokens = 3;
 static int heads_per_workgroup(const VerifyArgs &a)
