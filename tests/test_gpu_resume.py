@@ -258,3 +258,26 @@ def test_deferred_resume_rounds_equal_committed_rounds(name):
     for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
         np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
     say(f"  {W.describe(shape)}: three rounds bit-identical")
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("one_slot_16", W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=2, n_batch=1)),
+    ("two_slots_gqa4_37", W.shape_with(W.SINGLE_SLOT_VERIFY, n_kh=4, n_vh=16, n_tok=37, n_pool=3, n_batch=2)),
+    ("one_slot_qk_norm_5", W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=5, n_pool=1, n_batch=1)),
+])
+def test_workgroup_per_value_head_equals_per_key_head(name, shape):
+    """With few batch entries gdn_verify runs a workgroup per value head (8 waves); resuming with
+    every index at -1 is the same verify, always run with a workgroup per key head.  The two must
+    agree bit for bit: out, state, conv state and capture."""
+    say(f"[value-head vs key-head workgroups] {name}")
+    dev, gdn = _dev(), _gdn()
+    flags = gdn.GDN_F_QK_NORM_SILU if "qk_norm" in name else 0
+    inp = W.make_inputs(shape, 61)
+    a = dev.upload(shape, inp, flags=flags)
+    dev.verify(a)
+    b = dev.upload(shape, inp, flags=flags)
+    dev.verify_resume(b, torch.full((shape.n_batch,), -1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    ra, rb = _snapshot(a, shape.n_tok), _snapshot(b, shape.n_tok)
+    for k in ra:
+        np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
