@@ -337,8 +337,8 @@ size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16)
 
 // Conv state of the key heads' q / k channels after a launch that ran one value head per
 // workgroup: rows nt .. nt+2 of the launch's conv input (the conv state's own rows while nt < 3,
-// then its tokens), the values the verify kernel keeps for the channels it owns.  Rows are
-// written in order: row r takes row nt + r > r, which is still the old one.
+// then its tokens), the values the verify kernel keeps for the channels it owns.  All three are
+// read before any is written, so every read sees the old rows and the reads travel together.
 template <bool ACT_BF16>
 __global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
 {
@@ -351,19 +351,28 @@ __global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
     const size_t C = (size_t)a.C;
     float *cs = a.conv_state + (size_t)s * 3 * C + ch;
     const act_t *x = static_cast<const act_t *>(a.qkv) + ((size_t)b * a.T + a.t0) * C + ch;
+    // both candidates of every row are loaded unconditionally (valid rows either way), and picked
+    // after the loads, so no wait sits under a branch
+    float old[3];
+    act_t tok[3];
+#pragma unroll
     for (int r = 0; r < 3; ++r) {
         const int j = a.nt + r;
-        float v;
-        if (j < 3) {
-            v = cs[(size_t)j * C];
-        } else {
-            if constexpr (ACT_BF16)
-                v = bf16_to_f32(x[(size_t)(j - 3) * C]);
-            else
-                v = x[(size_t)(j - 3) * C];
-        }
-        cs[(size_t)r * C] = v;
+        old[r] = cs[(size_t)(j < 2 ? j : 2) * C];
+        tok[r] = x[(size_t)(j - 3 > 0 ? j - 3 : 0) * C];
     }
+    float v[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        float xv;
+        if constexpr (ACT_BF16)
+            xv = bf16_to_f32(tok[r]);
+        else
+            xv = tok[r];
+        v[r] = a.nt + r < 3 ? old[r] : xv;
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) cs[(size_t)r * C] = v[r];
 }
 
 // Value heads per workgroup.  With few batch entries a workgroup per key head leaves most CUs idle
