@@ -84,11 +84,10 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     const int h0 = (blockIdx.x % gpb) * HW;  // first value head of the workgroup
     const int hk = h0 / R;
     const int h = h0 + hl;
-    // With one value head per workgroup the key head's q / k channels are shared: only its first
-    // workgroup writes them to the conv window, and their conv state is written after the launch
-    // (qk_conv_state_kernel), as every workgroup of the key head reads it here.
-    const bool lead = h0 % R == 0;
-    const bool qk_state = HW == R;
+    // With one value head per workgroup the key head's q / k channels are shared, and every
+    // workgroup of the key head reads their starting rows here, so none of them writes those
+    // channels: qk_conv_state_kernel writes their conv window rows and conv state after the launch.
+    const bool own_qk = HW == R;
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the workgroup
     // A rollback left pending by the previous round: the first launch of the call starts from the
@@ -224,7 +223,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
                 dst = vs + ((lc - 2 * D) / D) * TT * D + G::perm((lc - 2 * D) % D);
             float x0 = csv[it][0], x1 = csv[it][1], x2 = csv[it][2];
             const f4 w = wv[it];
-            const bool own = lc >= 2 * D || lead;  // this workgroup writes the channel's window
+            const bool own = lc >= 2 * D || own_qk;  // this workgroup writes the channel's rows
             float *cc = CAP ? a.cap_conv + (size_t)s * (3 + a.t_cap) * C + gc : nullptr;
             if (CAP && t0 == 0 && own) {  // the window starts with the conv state the call began from
                 cc[0] = x0;
@@ -243,7 +242,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
             }
             // conv state after the launch's last token (xext rows nt .. nt+2); this thread was the
             // only reader of these elements
-            if (commit && (lc >= 2 * D || qk_state)) {
+            if (commit && own) {
                 cs_s[gc] = x0;
                 cs_s[(size_t)C + gc] = x1;
                 cs_s[(size_t)2 * C + gc] = x2;
@@ -335,58 +334,73 @@ size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16)
     return act_bf16 ? VerifyLds<64, uint16_t>::total(ratio) : VerifyLds<64, float>::total(ratio);
 }
 
-// Conv state of the key heads' q / k channels after a launch that ran one value head per
-// workgroup: rows nt .. nt+2 of the launch's conv input (the conv state's own rows while nt < 3,
-// then its tokens), the values the verify kernel keeps for the channels it owns.  All three are
-// read before any is written, so every read sees the old rows and the reads travel together.
-template <bool ACT_BF16>
+// The key heads' q / k channels after a launch that ran one value head per workgroup: their conv
+// window rows of the launch (with capture) and their conv state after it (unless the commit is
+// deferred).  The launch's conv input is its starting rows (the slot's conv state, or the capture
+// window rows it resumes from, chosen as in the verify kernel) followed by its tokens.  Every read
+// of a channel precedes its writes, and all of them are issued before the first is used.
+template <bool ACT_BF16, bool CAP>
 __global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
     const int b = blockIdx.y;
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the block, as in the verify kernel
+    int ra = -1;
+    if constexpr (CAP) {
+        if (a.resume) {
+            const int r = a.resume[b];
+            if (r >= a.t_cap) return;  // skipped by the verify kernel too
+            if (a.t0 == 0) ra = r;
+        }
+        if (a.defer && a.t0 > 0) ra = a.t0 - 1;
+    }
+    const bool commit = !(CAP && a.defer);
     const int ch = blockIdx.x * blockDim.x + threadIdx.x;  // q | k channels are 0 .. 2 H_k d - 1
     if (ch >= 2 * a.n_kh * a.d) return;
     const size_t C = (size_t)a.C;
+    const int t0 = a.t0, nt = a.nt;
     float *cs = a.conv_state + (size_t)s * 3 * C + ch;
-    const act_t *x = static_cast<const act_t *>(a.qkv) + ((size_t)b * a.T + a.t0) * C + ch;
-    // both candidates of every row are loaded unconditionally (valid rows either way), and picked
-    // after the loads, so no wait sits under a branch
-    float old[3];
-    act_t tok[3];
+    float *cw = CAP ? a.cap_conv + (size_t)s * (3 + a.t_cap) * C + ch : nullptr;
+    const float *src = ra >= 0 ? cw + (size_t)(ra + 1) * C : cs;
+    const act_t *x = static_cast<const act_t *>(a.qkv) + ((size_t)b * a.T + t0) * C + ch;
+    float xs[3 + kTokenTile];
+    act_t tok[kTokenTile];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        const int j = a.nt + r;
-        old[r] = cs[(size_t)(j < 2 ? j : 2) * C];
-        tok[r] = x[(size_t)(j - 3 > 0 ? j - 3 : 0) * C];
-    }
-    float v[3];
+    for (int r = 0; r < 3; ++r) xs[r] = src[(size_t)r * C];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        float xv;
+    for (int t = 0; t < kTokenTile; ++t) tok[t] = x[(size_t)(t < nt ? t : nt - 1) * C];  // valid rows only
+#pragma unroll
+    for (int t = 0; t < kTokenTile; ++t) {
         if constexpr (ACT_BF16)
-            xv = bf16_to_f32(tok[r]);
+            xs[3 + t] = bf16_to_f32(tok[t]);
         else
-            xv = tok[r];
-        v[r] = a.nt + r < 3 ? old[r] : xv;
+            xs[3 + t] = tok[t];
     }
+    if constexpr (CAP) {
+        if (t0 == 0)
 #pragma unroll
-    for (int r = 0; r < 3; ++r) cs[(size_t)r * C] = v[r];
+            for (int r = 0; r < 3; ++r) cw[(size_t)r * C] = xs[r];
+#pragma unroll
+        for (int t = 0; t < kTokenTile; ++t)
+            if (t < nt) cw[(size_t)(t0 + t + 3) * C] = xs[3 + t];
+    }
+    if (commit)
+#pragma unroll
+        for (int r = 0; r < 3; ++r) cs[(size_t)r * C] = xs[nt + r];
 }
 
 // Value heads per workgroup.  With few batch entries a workgroup per key head leaves most CUs idle
 // and each one streams its heads' whole capture through one store path (~64 B per clock), so then
-// each value head gets its own workgroup.  Not when resuming or deferring the commit: those read the
-// key head's q / k rows of the conv window, which the first workgroup of the key head rewrites.  Not
-// below 3 tokens either: there the second launch costs more than the split saves (one slot: 9.4
-// against 11.1 us at 1 token, even at 2, ahead from 3 on; likewise at 4 slots).
+// each value head gets its own workgroup.  Not below 3 tokens: there the second launch costs more
+// than the split saves (one slot: 9.4 against 11.1 us at 1 token, even at 2, ahead from 3 on;
+// likewise at 4 slots).
 constexpr int kSplitMaxWorkgroups = 64;
 constexpr int kSplitMinTokens = 3;
 static int heads_per_workgroup(const VerifyArgs &a)
 {
     const int R = a.n_vh / a.n_kh;
-    if (R == 1 || a.resume || a.defer || a.T < kSplitMinTokens) return R;
+    if (R == 1 || a.T < kSplitMinTokens) return R;
     return (long)a.n_batch * a.n_kh <= kSplitMaxWorkgroups ? 1 : R;
 }
 
@@ -418,7 +432,7 @@ static hipError_t launch_t(const VerifyArgs &a0, hipStream_t stream)
         if (hipError_t e = hipGetLastError()) return e;
         if (HW < R) {
             const unsigned blocks = (unsigned)((2 * a.n_kh * D + 255) / 256);
-            hipLaunchKernelGGL(qk_conv_state_kernel<AB>, dim3(blocks, a.n_batch), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((qk_conv_state_kernel<AB, CAP>), dim3(blocks, a.n_batch), dim3(256), 0, stream, a);
             if (hipError_t e = hipGetLastError()) return e;
         }
     }

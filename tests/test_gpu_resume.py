@@ -260,24 +260,45 @@ def test_deferred_resume_rounds_equal_committed_rounds(name):
     say(f"  {W.describe(shape)}: three rounds bit-identical")
 
 
-@pytest.mark.parametrize("name,shape", [
-    ("one_slot_16", W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=2, n_batch=1)),
-    ("two_slots_gqa4_37", W.shape_with(W.SINGLE_SLOT_VERIFY, n_kh=4, n_vh=16, n_tok=37, n_pool=3, n_batch=2)),
-    ("one_slot_qk_norm_5", W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=5, n_pool=1, n_batch=1)),
+def _slice(inp: dict, n: int) -> dict:
+    """The first n batch entries of a call's inputs (the pool, parameters and slots stay)."""
+    out = dict(inp)
+    for k in ("qkv", "z", "alpha", "beta", "slot_ids", "trims"):
+        out[k] = np.asarray(inp[k])[:n]
+    return out
+
+
+@pytest.mark.parametrize("name,shape,n_big", [
+    ("one_slot_16", W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=6, n_batch=1), 5),
+    ("two_slots_gqa4_37", W.shape_with(W.SINGLE_SLOT_VERIFY, n_kh=4, n_vh=16, n_tok=37, n_pool=18, n_batch=2), 17),
+    ("one_slot_qk_norm_5", W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=5, n_pool=6, n_batch=1), 5),
 ])
-def test_workgroup_per_value_head_equals_per_key_head(name, shape):
-    """With few batch entries gdn_verify runs a workgroup per value head (8 waves); resuming with
-    every index at -1 is the same verify, always run with a workgroup per key head.  The two must
-    agree bit for bit: out, state, conv state and capture."""
+def test_workgroup_per_value_head_equals_per_key_head(name, shape, n_big):
+    """With few batch entries gdn_verify runs a workgroup per value head (8 waves); the same entries
+    inside a call of n_big entries (more than 64 workgroups per key head) run a workgroup per key
+    head.  Out, state, conv state and capture of the shared entries agree bit for bit, plain and
+    resuming from accepted positions with the commit deferred."""
     say(f"[value-head vs key-head workgroups] {name}")
     dev, gdn = _dev(), _gdn()
     flags = gdn.GDN_F_QK_NORM_SILU if "qk_norm" in name else 0
-    inp = W.make_inputs(shape, 61)
-    a = dev.upload(shape, inp, flags=flags)
-    dev.verify(a)
-    b = dev.upload(shape, inp, flags=flags)
-    dev.verify_resume(b, torch.full((shape.n_batch,), -1, dtype=torch.int32, device="cuda"))
-    torch.cuda.synchronize()
-    ra, rb = _snapshot(a, shape.n_tok), _snapshot(b, shape.n_tok)
-    for k in ra:
-        np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
+    big = W.shape_with(shape, n_batch=n_big)
+    inp_big = W.make_inputs(big, 61)
+    inp = _slice(inp_big, shape.n_batch)
+    n, T = shape.n_batch, shape.n_tok
+    for defer in (False, True):
+        fl = flags | (gdn.GDN_F_DEFER_COMMIT if defer else 0)
+        a = dev.upload(shape, inp, flags=fl)
+        b = dev.upload(big, inp_big, flags=fl)
+        dev.verify(a)
+        dev.verify(b)
+        if defer:  # a second round resuming from each entry's last position
+            acc = np.full(n, T - 1, dtype=np.int32)
+            dev.verify_resume(a, torch.from_numpy(acc).cuda())
+            dev.verify_resume(b, torch.from_numpy(np.full(n_big, T - 1, dtype=np.int32)).cuda())
+        torch.cuda.synchronize()
+        ra, rb = _snapshot(a, T), _snapshot(b, T)
+        np.testing.assert_array_equal(ra["out"], rb["out"][:n], err_msg="out")
+        for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
+            for e in range(n):
+                sl = int(inp["slot_ids"][e])
+                np.testing.assert_array_equal(ra[k][sl], rb[k][sl], err_msg=f"{k} defer={defer}")
