@@ -125,6 +125,16 @@ def components(args) -> dict:
     out["single_slot_verify"] = {"workload": "1 slot x 16 tokens, 16/32 heads, d=128, bf16", "us": us,
                                  "tokens_per_s": s.n_tok / (us * 1e-6),
                                  "hbm_gbps": bytemodel.verify_bytes(s) / (us * 1e-6) / 1e9}
+    # the same slot in the resume loop with the commit deferred: each round starts from the
+    # previous round's accepted capture position
+    device.verify(d)
+    acc = torch.from_numpy(np.array([s.n_tok - 1 - int(W.make_inputs(s, 0)["trims"][0])], dtype=np.int32)).cuda()
+    dims_defer = gdn.make_dims(s, flags=gdn.GDN_F_DEFER_COMMIT)
+    us = time_launches(lambda: device.verify_resume(d, acc, dims=dims_defer), 200)
+    out["single_slot_resume_deferred"] = {
+        "workload": "1 slot x 16 tokens, 16/32 heads, d=128, bf16, gdn_verify_resume with GDN_F_DEFER_COMMIT",
+        "us": us, "tokens_per_s": s.n_tok / (us * 1e-6),
+        "hbm_gbps": bytemodel.verify_bytes(s, commit=False) / (us * 1e-6) / 1e9}
     del d
     # snapshot-and-replay rollback on the 64-slot workload (no per-position capture): a round is
     # snapshot + verify, plus restore + replay of the accepted tokens when some are rejected
