@@ -68,6 +68,15 @@ def cpu_baseline(shape, inp, target_s: float = 10.0) -> dict:
     from oracle import ref
 
     threads = ref.max_threads()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     times = []
     t_all = time.perf_counter()
     while time.perf_counter() - t_all < target_s or len(times) < 3:
@@ -77,7 +86,7 @@ def cpu_baseline(shape, inp, target_s: float = 10.0) -> dict:
     times.sort()
     med = times[len(times) // 2]
     return {"value": shape.n_batch * shape.n_tok / med, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"the whole call ({shape.n_batch} slots x {shape.n_vh} value heads x "
                       f"{shape.n_tok} tokens, fp64, with capture), {len(times)} repetitions in "
                       f"{sum(times):.1f} s, median {med * 1e3:.0f} ms"}
@@ -333,7 +342,7 @@ def main() -> int:
     achieved = vb / (v_avg * 1e-3) / 1e9
     traffic = measured_traffic()
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall_step * 1e6:.1f} us), "
-        f"verify {v_avg * 1e3:.1f} us avg (p10 {np.percentile(verify_ms, 10) * 1e3:.1f}, "
+        f"verify {v_avg * 1e3:.1f} us avg, median {np.median(verify_ms) * 1e3:.1f} (p10 {np.percentile(verify_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(verify_ms, 90) * 1e3:.1f}) -> {achieved:.0f} GB/s, rollback {r_avg * 1e3:.1f} us; "
         f"step {(vb + rb) / (ms_step * 1e-3) / 1e9:.0f} GB/s; resume step {rs_ms_step * 1e3:.1f} us, "
         f"with the commit deferred {rd_ms_step * 1e3:.1f} us")
@@ -371,7 +380,11 @@ def main() -> int:
         "roofline": {"kernel": "verify_chain_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": vb,
-                     "avg_launch_us": v_avg * 1e3},
+                     "avg_launch_us": v_avg * 1e3,
+                     "median_launch_us": float(np.median(verify_ms)) * 1e3,
+                     "p10_launch_us": float(np.percentile(verify_ms, 10)) * 1e3,
+                     "p90_launch_us": float(np.percentile(verify_ms, 90)) * 1e3,
+                     "frac_at_median": vb / (float(np.median(verify_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBPS},
     }
     sets.clear()  # 4 x 2.2 GB of state and capture, not needed by the components
     torch.cuda.empty_cache()

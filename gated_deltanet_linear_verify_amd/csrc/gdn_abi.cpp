@@ -420,7 +420,12 @@ GDN_API int gdn_rollback_trim(const gdn_capture *capture, int32_t slot, int32_t 
     if (trim < 0) return fail(GDN_ERR_RANGE, "gdn_rollback_trim: negative trim %d", trim);
     if (slot < 0 || slot >= capture->dims.n_pool)
         return fail(GDN_ERR_RANGE, "gdn_rollback_trim: slot %d outside [0, %d)", slot, capture->dims.n_pool);
-    if (trim == 0) return ok();  // nothing rejected: the verify already left the final state
+    if (trim == 0) {
+        // Nothing rejected.  A committing verify already left the final state; one that deferred
+        // its commit left it at capture position n_tok - 1, which is restored here.
+        if (!(capture->dims.flags & GDN_F_DEFER_COMMIT)) return ok();
+        return gdn_rollback(capture, slot, n_tok - 1, stream);
+    }
     if (trim >= n_tok)
         return fail(GDN_ERR_RANGE, "gdn_rollback_trim: trim %d >= verified positions %d", trim, n_tok);
     return gdn_rollback(capture, slot, n_tok - 1 - trim, stream);

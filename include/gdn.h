@@ -79,8 +79,11 @@ enum gdn_capture_mode { GDN_CHAIN = 0, GDN_TREE = 1 };
  * position with gdn_rollback / gdn_rollback_batch, or passes it to the next round's
  * gdn_verify_resume, which reads it from the capture; so a round that accepts every token also
  * ends in a commit, unlike the pages' trim-0 early return (hf2q qwen35_target.rs, rollback_kv).
- * A call of more than one launch (n_tok > 16) carries the state between its launches through its
- * own capture positions.  Without a capture it is GDN_ERR_ARG; other calls ignore it. */
+ * gdn_rollback_trim reads this flag from the capture's dims: with it, trim 0 commits position
+ * n_tok - 1 instead of returning at once, so the capture descriptor of a deferred verify must
+ * carry the flag.  A call of more than one launch (n_tok > 16) carries the state between its
+ * launches through its own capture positions.  Without a capture it is GDN_ERR_ARG; other calls
+ * ignore it. */
 #define GDN_F_DEFER_COMMIT 0x4u
 
 typedef struct gdn_dims {
@@ -177,7 +180,7 @@ int gdn_verify_tree(const gdn_dims *dims, const float *state, const float *conv_
  *   capture->state[slot]      <- capture->ssm[slot][accepted_idx]            (bitwise copy)
  *   capture->conv_state[slot] <- capture->conv[slot][accepted_idx+1 .. +3]   (chain)
  *                                capture->conv[slot][accepted_idx]           (tree)
- * Only this slot is touched (hf2q qwen35_target.rs, rollback_kv "mutates ONLY" the slot;
+ * No other slot is read or written (hf2q qwen35_target.rs, rollback_kv: a per-slot rollback;
  * lucebox-hub internal.h, DeltaNetCapture: offset (commit_n-1) and conv slice
  * [commit_n .. commit_n+kernel-2]).  Errors: slot not in [0, n_pool) or accepted_idx not in
  * [0, t_cap) -> GDN_ERR_RANGE (the pages skip silently; here the caller hears of it).
@@ -185,17 +188,25 @@ int gdn_verify_tree(const gdn_dims *dims, const float *state, const float *conv_
 int gdn_rollback(const gdn_capture *capture, int32_t slot, int32_t accepted_idx, void *stream);
 
 /*
- * Batched rollback of n entries in one launch: slots and accepted_idx are device int32 [n].
- * Entries with an out-of-range slot or index are skipped (GDN_F_CHECK_INDICES in
- * capture->dims.flags: validated on the host, GDN_ERR_RANGE).  Slots must be distinct.
+ * Batched rollback of n entries in one launch: slots and accepted_idx are device int32 [n];
+ * entry i does what gdn_rollback(capture, slots[i], accepted_idx[i]) does.  The pages roll back
+ * one slot per call, each slot from its own accepted position (hf2q qwen35_target.rs, rollback_kv
+ * and rollback_la_to, per SlotId); the slots of a verify batch are independent, so their copies
+ * share one launch.  Entries with an out-of-range slot or index are skipped (GDN_F_CHECK_INDICES
+ * in capture->dims.flags: validated on the host, GDN_ERR_RANGE).  Slots must be distinct.
+ * n == 0 is a no-op; n outside [0, min(n_pool, 65535)] is GDN_ERR_RANGE.
  */
 int gdn_rollback_batch(const gdn_capture *capture, const int32_t *slots,
                        const int32_t *accepted_idx, int32_t n, void *stream);
 
 /*
  * The pages' trim form (hf2q qwen35_target.rs, rollback_kv): n_tok positions were verified,
- * the last `trim` are rejected.  trim == 0 -> GDN_OK with nothing enqueued; trim >= n_tok ->
- * GDN_ERR_RANGE; else gdn_rollback(capture, slot, n_tok - 1 - trim).
+ * the last `trim` are rejected.  trim == 0 -> GDN_OK with nothing enqueued, because the verify
+ * already left the state after its last token; but when capture->dims.flags has
+ * GDN_F_DEFER_COMMIT that verify left the state in the capture, and trim 0 is
+ * gdn_rollback(capture, slot, n_tok - 1).  trim >= n_tok -> GDN_ERR_RANGE; else
+ * gdn_rollback(capture, slot, n_tok - 1 - trim).  n_tok outside [1, t_cap], a negative trim or a
+ * slot outside [0, n_pool) -> GDN_ERR_RANGE.
  */
 int gdn_rollback_trim(const gdn_capture *capture, int32_t slot, int32_t trim, int32_t n_tok,
                       void *stream);
@@ -216,11 +227,19 @@ int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, const voi
                 const float *dt_bias, const float *conv_w, const float *norm_w, void *out,
                 int32_t n_tok, int32_t slot, void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace bytes gdn_prefill needs for n_tok tokens (0 on invalid dims). */
+/* Workspace bytes gdn_prefill needs for n_tok tokens (0 on invalid dims or n_tok < 1).  The
+ * pages' prefill keeps its per-call intermediates in the compute graph's own buffers, apart from
+ * the persistent cache (lucebox-hub internal.h, create_target_cache: a prefill-only cache holds no
+ * rollback tensors); here the caller owns that memory and sizes it with this call. */
 size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t n_tok);
 
 /* Bytes of capture->ssm for t_cap positions; *conv_bytes (if not NULL) receives the bytes of
- * capture->conv for the mode (0 on invalid dims). */
+ * capture->conv for the mode (0 on invalid dims, t_cap < 1 or an unknown mode).  The pages size
+ * the capture by the most positions one verify writes (lucebox-hub internal.h, struct TargetCache:
+ * ssm_intermediate [S_v, S_v, H_v, max_q_len] and conv_input_cache [(kernel-1) + max_q_len,
+ * conv_channels] per layer; the create_target_cache comment sets that length from
+ * max_verify_tokens, at least 1 + the tree budget in tree mode): chain P * t_cap * H_v * d_v * d_k
+ * and P * (3 + t_cap) * C floats, tree P * t_cap * 3 * C for the conv. */
 size_t gdn_capture_bytes(const gdn_dims *dims, int32_t t_cap, int32_t mode, size_t *conv_bytes);
 
 /* Zero the recurrent state and conv state of one slot (lucebox-hub internal.h,

@@ -52,3 +52,26 @@ def to_np(t):
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def rel_err_slices(gpu, ref, n_lead: int):
+    """rel_err of every slice over the trailing axes, for arrays whose first n_lead axes index the
+    slices (e.g. [units][T][d_v][d_k] with n_lead = 2: one value per unit and position)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ax = tuple(range(n_lead, ref.ndim))
+    den = np.max(np.abs(ref), axis=ax)
+    num = np.max(np.abs(gpu - ref), axis=ax)
+    return num / np.where(den > 0, den, 1.0)
+
+
+def out_err_slices(shape, gpu, ref, n_lead: int):
+    """out_err of every slice over the trailing axes (bf16 outputs: beyond half an ulp of ref)."""
+    if shape.out_dtype != 1:
+        return rel_err_slices(gpu, ref, n_lead)
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ax = tuple(range(n_lead, ref.ndim))
+    den = np.max(np.abs(ref), axis=ax)
+    ex = np.max(np.maximum(np.abs(gpu - ref) - half_ulp_bf16(ref), 0.0), axis=ax)
+    return ex / np.where(den > 0, den, 1.0)

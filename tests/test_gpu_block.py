@@ -101,12 +101,17 @@ def test_linear_full_size_sampled_rows():
 
 @pytest.mark.parametrize("name", ["small_d128", "small_d64_ratio1"])
 def test_block_against_oracle(name):
-    """Input projections, verify with capture (q / k SiLU + unit length), output projection.
-    The projections are held to the 1e-5 bar beyond their own bf16 rounding.  The block stores
-    its intermediates as bf16 on both sides (projection outputs, the gated output that feeds the
-    output projection); where the GPU's fp32 value and the oracle's fp64 value straddle a bf16
-    rounding boundary the stored values differ by one ulp (2^-8 relative), so the block's output
-    is held to 1e-2 of each entry's largest value, a few such ulps, and the state to 2e-2."""
+    """Input projections, verify with capture (q / k SiLU + unit length), output projection, each
+    stage held to its own bar on the values the previous stage actually stored:
+    * the four input projections against the oracle's fp64 x W^T, 1e-5 beyond their bf16 rounding;
+    * the verify against the oracle run on the GPU's stored bf16 qkv / z / beta / alpha: state and
+      every capture position 2e-3, the gated output 2e-3 beyond its own bf16 rounding, the conv
+      window and conv state bit for bit;
+    * the output projection against the oracle's fp64 product of the GPU's stored bf16 gated
+      output, 1e-5 beyond its bf16 rounding.
+    Chaining the stages on the oracle side alone would compare bf16 intermediates that can sit one
+    rounding apart (a value whose fp32 and fp64 forms straddle a bf16 rounding boundary); the
+    stage-wise form holds every arithmetic step to the stated tolerance instead."""
     from gated_deltanet_linear_verify_amd import device
     base = {"small_d128": W.shape_with(W.MULTI_SLOT_VERIFY, n_kh=2, n_vh=4, n_pool=3, n_batch=2, n_tok=5),
             "small_d64_ratio1": W.shape_with(W.MULTI_SLOT_VERIFY, n_kh=4, n_vh=4, d_k=64, d_v=64, n_pool=2,
@@ -117,21 +122,38 @@ def test_block_against_oracle(name):
     d = device.upload_block(base, inp)
     device.block_step(d)
     torch.cuda.synchronize()
-    r = block.block_verify(base, inp)
-    p = r["proj"]
     B, T, Hv, dv = base.n_batch, base.n_tok, base.n_vh, base.d_v
-    # the projections: beyond their own bf16 rounding, as the product
-    assert _bf16_err(to_np(d["qkv"]), block.linear(inp["x"], inp["w_qkv"])) < TOL_F32
-    assert _bf16_err(to_np(d["beta"]), block.sigmoid(block.linear(inp["x"], inp["w_beta"]))) < TOL_F32
-    flips = np.mean(to_np(d["qkv"]) != p["qkv"])
-    say(f"  qkv elements one bf16 rounding apart: {flips:.4f}")
-    y = to_np(d["y"]).astype(np.float64)
-    for b in range(B):
-        err = rel_err(y[b], r["y"][b])
-        say(f"  entry {b}: block output rel err {err:.2e}")
-        assert err < 1e-2
-    st = to_np(d["state"])
+    # stage 1: the projections, beyond their own bf16 rounding
+    x = inp["x"]
+    assert _bf16_err(to_np(d["qkv"]), block.linear(x, inp["w_qkv"]).reshape(B, T, -1)) < TOL_F32
+    assert _bf16_err(to_np(d["z"]), block.linear(x, inp["w_z"]).reshape(B, T, Hv, dv)) < TOL_F32
+    assert _bf16_err(to_np(d["beta"]), block.sigmoid(block.linear(x, inp["w_beta"])).reshape(B, T, Hv)) < TOL_F32
+    assert _bf16_err(to_np(d["alpha"]), block.linear(x, inp["w_alpha"]).reshape(B, T, Hv)) < TOL_F32
+    # stage 2: the verify, on the inputs the projections stored
+    layer = dict(inp)
+    for k in ("qkv", "z", "alpha", "beta"):
+        layer[k] = to_np(d[k])
+    o = ref.verify_pool(base, layer, flags=ref.F_QK_NORM_SILU)
+    st, cap, out = to_np(d["state"]), to_np(d["cap_ssm"]), to_np(d["out"])
+    worst = {"state": 0.0, "cap": 0.0, "out": 0.0}
     for b in range(B):
         s_ = int(inp["slot_ids"][b])
         for h in range(Hv):
-            assert rel_err(st[s_, h], r["state"][s_, h]) < 2e-2
+            worst["state"] = max(worst["state"], rel_err(st[s_, h], o["state"][s_, h]))
+            worst["out"] = max(worst["out"], _bf16_err(out[b, :, h], o["out"][b, :, h]))
+            for t in range(T):
+                worst["cap"] = max(worst["cap"], rel_err(cap[s_, t, h], o["cap_ssm"][s_, t, h]))
+        np.testing.assert_array_equal(to_np(d["cap_conv"])[s_], o["cap_conv"][s_])
+    np.testing.assert_array_equal(to_np(d["conv_state"]), o["conv_state"])
+    say(f"  verify stage on the stored projections: {worst}")
+    for k, v in worst.items():
+        assert v <= 2e-3, (k, v)
+    # stage 3: the output projection of the stored gated output
+    y = to_np(d["y"])
+    want = block.linear(out.reshape(B * T, Hv * dv), inp["w_out"]).reshape(B, T, -1)
+    err = _bf16_err(y, want)
+    say(f"  output projection beyond bf16 rounding: {err:.2e}")
+    assert err < TOL_F32
+    # for information: the whole block against the oracle's own chain of bf16 intermediates
+    r = block.block_verify(base, inp)
+    say(f"  end to end (bf16 intermediates on each side): {rel_err(y, r['y']):.2e}")

@@ -223,6 +223,34 @@ def test_deferred_commit_leaves_the_state_and_matches_the_commit(name):
 
 
 @pytest.mark.parametrize("name", list(DEFER_CASES))
+def test_deferred_commit_then_trim_equals_the_committing_path(name):
+    """The trim form after a verify whose commit was deferred: trim 0 commits the last position (the
+    committing verify's own final state), trim > 0 restores position n_tok - 1 - trim; both bit for
+    bit what the committing verify followed by the same trim leaves."""
+    shape, s1, _, _ = DEFER_CASES[name]
+    say(f"[deferred commit + trim] {name}")
+    dev, gdn = _dev(), _gdn()
+    inp = W.make_inputs(shape, s1 + 100)
+    trims = [0] + [int(t) for t in np.asarray(inp["trims"])[1:]]
+    a = dev.upload(shape, inp)
+    b = dev.upload(shape, inp, flags=gdn.GDN_F_DEFER_COMMIT)
+    dev.verify(a)
+    dev.verify(b)
+    for b_ in range(shape.n_batch):
+        s = int(inp["slot_ids"][b_])
+        for d in (a, b):
+            gdn.gdn_rollback_trim(d["capture"], s, trims[b_], shape.n_tok)
+    torch.cuda.synchronize()
+    ra, rb = _snapshot(a, shape.n_tok), _snapshot(b, shape.n_tok)
+    for k in ("state", "conv_state"):
+        np.testing.assert_array_equal(rb[k], ra[k], err_msg=k)
+    # the slot with trim 0 holds the state after every token, as the committing verify left it
+    s0 = int(inp["slot_ids"][0])
+    np.testing.assert_array_equal(rb["state"][s0], ra["cap_ssm"][s0, shape.n_tok - 1])
+    say(f"  {W.describe(shape)}: trims {trims} bit-identical")
+
+
+@pytest.mark.parametrize("name", list(DEFER_CASES))
 def test_deferred_resume_rounds_equal_committed_rounds(name):
     """Three rounds of the resume protocol with the commit deferred (verify, then verify_resume
     from each accepted position, a final rollback to materialise the state) against three rounds

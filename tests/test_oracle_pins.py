@@ -312,6 +312,43 @@ def test_rollback_indexing_golden():
             assert list(range(commit_n, commit_n + K - 1)) == c["conv_rows"]
 
 
+def _tagged_window_inputs(n_tok: int) -> tuple:
+    """A tiny call whose conv input window rows are tagged: row r of concat(conv state, qkv) holds
+    the value 1000 r + channel index in every channel, so a restored or advanced conv state names
+    the rows it came from."""
+    shape = W.shape_with(TINY, n_tok=n_tok, n_pool=3, n_batch=1)
+    inp = W.make_inputs(shape, 40)
+    C = shape.conv_channels
+    s = int(inp["slot_ids"][0])
+    row = lambda r: (1000.0 * r + np.arange(C)).astype(np.float32)
+    inp["conv_state"][s] = np.stack([row(r) for r in range(3)])
+    inp["qkv"][0] = np.stack([row(3 + t) for t in range(n_tok)])
+    return shape, inp, s, row
+
+
+@pytest.mark.parametrize("case", [c for c in json.load(open(os.path.join(HERE, "golden", "rollback_indexing.json")))["cases"]
+                                  if c["accepted_idx"] is not None])
+def test_rollback_indexing_golden_through_the_oracle(case):
+    """The golden conv rows, through the oracle's own rollback and its verify: after verifying
+    n_tokens_max tokens, ref.rollback_chain to the golden accepted index restores exactly the golden
+    window rows as the conv state, and so does the final conv state of a verify of the accepted
+    tokens alone (commit_n = accepted_idx + 1 tokens); the restored recurrent state is capture
+    element accepted_idx, which equals that shorter verify's state."""
+    n, a = case["n_tokens_max"], case["accepted_idx"]
+    shape, inp, s, row = _tagged_window_inputs(n)
+    full = ref.verify_pool(shape, inp)
+    st = inp["state"].astype(np.float64).copy()
+    cs = inp["conv_state"].copy()
+    ref.rollback_chain(st, cs, full["cap_ssm"], full["cap_conv"], s, a)
+    want = np.stack([row(r) for r in case["conv_rows"]])
+    np.testing.assert_array_equal(cs[s], want)
+    short = ref.verify_pool(shape, inp, n_tok=a + 1)
+    np.testing.assert_array_equal(short["conv_state"][s], want)
+    np.testing.assert_array_equal(st[s], short["state"][s])
+    # a verify of all n_tokens_max tokens ends on the rows after the last one
+    np.testing.assert_array_equal(full["conv_state"][s], np.stack([row(r) for r in range(n, n + 3)]))
+
+
 @pytest.mark.parametrize("shape_name", ["tiny_verify", "small"])
 def test_verify_then_rollback_equals_shorter_verify(shape_name):
     """verify(T) then rollback(a) leaves exactly what verify(a + 1) leaves (state and conv
