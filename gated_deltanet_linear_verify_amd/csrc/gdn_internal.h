@@ -124,5 +124,11 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs &a, const LaunchCfg &c, hipStream_t stream);
 size_t prefill_workspace_bytes(int d, int n_kh, int n_vh, int T);
 size_t prefill_lds_bytes(int d, bool act_bf16);  // the larger of the two kernels' LDS
+// Every check of a prefill call except the workspace's (sets the last error); on GDN_OK, a holds
+// the launch arguments with ws unset and c the kernel configuration.
+int prefill_prepare(const char *fn, const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
+                    const void *z, const void *alpha, const void *beta, const float *A_log, const float *dt_bias,
+                    const float *conv_w, const float *norm_w, void *out, int32_t n_tok, int32_t slot, PrefillArgs &a,
+                    LaunchCfg &c);
 
 }  // namespace gdn

@@ -22,7 +22,7 @@ GDN_F_CHECK_INDICES = 0x2
 GDN_F_DEFER_COMMIT = 0x4
 
 EXPORTS = ("gdn_verify", "gdn_verify_resume", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch", "gdn_rollback_trim",
-           "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_capture_bytes", "gdn_reset",
+           "gdn_prefill", "gdn_prefill_noalloc", "gdn_prefill_workspace_bytes", "gdn_capture_bytes", "gdn_reset",
            "gdn_snapshot", "gdn_restore", "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch",
            "gdn_graph_destroy", "gdn_linear", "gdn_last_error", "gdn_version")
 
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_rollback_batch.argtypes = [Cp, P, P, I, P]
         L.gdn_rollback_trim.argtypes = [Cp, I, I, I, P]
         L.gdn_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I, I, P, S, P]
+        L.gdn_prefill_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, I, I, P]
         L.gdn_prefill_workspace_bytes.argtypes = [D, I]
         L.gdn_prefill_workspace_bytes.restype = S
         L.gdn_capture_bytes.argtypes = [D, I, I, ctypes.POINTER(S)]
@@ -94,7 +95,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_linear.argtypes = [P, P, I, I, I, ctypes.POINTER(gdn_out_seg), I, P]
         L.gdn_graph_destroy.argtypes = [P]
         for f in ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch",
-                  "gdn_rollback_trim", "gdn_prefill", "gdn_reset", "gdn_snapshot", "gdn_restore",
+                  "gdn_rollback_trim", "gdn_prefill", "gdn_prefill_noalloc", "gdn_reset", "gdn_snapshot", "gdn_restore",
                   "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch", "gdn_graph_destroy",
                   "gdn_linear"):
             getattr(L, f).restype = ctypes.c_int
@@ -248,6 +249,13 @@ def gdn_prefill(dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, co
     _check(lib().gdn_prefill(ctypes.byref(dims), _p(state), _p(conv_state), _p(qkv), _p(z),
                              _p(alpha), _p(beta), _p(A_log), _p(dt_bias), _p(conv_w), _p(norm_w),
                              _p(out), n_tok, slot, _p(workspace), ws_bytes, _stream(stream)))
+
+
+def gdn_prefill_noalloc(dims, state, conv_state, qkv, z, alpha, beta, A_log, dt_bias, conv_w, norm_w,
+                        out, n_tok: int, slot: int, stream=None) -> None:
+    _check(lib().gdn_prefill_noalloc(ctypes.byref(dims), _p(state), _p(conv_state), _p(qkv), _p(z),
+                                     _p(alpha), _p(beta), _p(A_log), _p(dt_bias), _p(conv_w),
+                                     _p(norm_w), _p(out), n_tok, slot, _stream(stream)))
 
 
 def gdn_reset(dims, state, conv_state, slot: int, stream=None) -> None:

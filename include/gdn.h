@@ -227,6 +227,26 @@ int gdn_prefill(const gdn_dims *dims, float *state, float *conv_state, const voi
                 const float *dt_bias, const float *conv_w, const float *norm_w, void *out,
                 int32_t n_tok, int32_t slot, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * gdn_prefill for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments as gdn_prefill without
+ * the workspace, same results: the workspace is a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held from the first call on that GPU
+ * until the process ends; looked up with hipGetSymbolAddress on that first call, which is the
+ * only call that can fail with GDN_ERR_HIP before launching).  The call runs as consecutive
+ * pieces of the most whole 64-token chunks whose workspace fits the array (the state carries over
+ * between pieces as between two gdn_prefill calls); dims whose single chunk needs more than the
+ * array are GDN_ERR_SHAPE.  No hipMalloc, hipFree or allocating library routine is called.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU (on different streams,
+ * or from different host threads without ordering) race and must not be issued.  Every other
+ * error as gdn_prefill; a launch failure (GDN_ERR_HIP) may leave earlier pieces enqueued.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gdn_prefill_noalloc(const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
+                        const void *z, const void *alpha, const void *beta, const float *A_log,
+                        const float *dt_bias, const float *conv_w, const float *norm_w, void *out,
+                        int32_t n_tok, int32_t slot, void *stream);
+
 /* Workspace bytes gdn_prefill needs for n_tok tokens (0 on invalid dims or n_tok < 1).  The
  * pages' prefill keeps its per-call intermediates in the compute graph's own buffers, apart from
  * the persistent cache (lucebox-hub internal.h, create_target_cache: a prefill-only cache holds no

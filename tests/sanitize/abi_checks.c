@@ -85,6 +85,12 @@ int main(void)
     CHECK(gdn_prefill(&d, F, F, F, F, F, F, F, F, F, F, F, 64, 4, F, (size_t)1 << 40, NULL), GDN_ERR_RANGE);
     CHECK(gdn_prefill(&d, F, F, F, F, F, F, F, F, F, F, F, 64, 0, F, 16, NULL), GDN_ERR_ARG);
     CHECK(gdn_prefill(&d, F, F, F, F, F, F, F, F, F, F, F, 64, 0, NULL, (size_t)1 << 40, NULL), GDN_ERR_ARG);
+    /* prefill without a workspace argument: the same validation, before the scratch is looked up */
+    CHECK(gdn_prefill_noalloc(&d, F, F, F, F, F, F, F, F, F, F, F, 0, 0, NULL), GDN_ERR_RANGE);
+    CHECK(gdn_prefill_noalloc(&d, F, F, F, F, F, F, F, F, F, F, F, 64, 4, NULL), GDN_ERR_RANGE);
+    CHECK(gdn_prefill_noalloc(&d, F, F, F, F, F, F, F, F, F, F, NULL, 64, 0, NULL), GDN_ERR_ARG);
+    CHECK(gdn_prefill_noalloc(&d, MIS, F, F, F, F, F, F, F, F, F, F, 64, 0, NULL), GDN_ERR_ARG);
+    CHECK(gdn_prefill_noalloc(NULL, F, F, F, F, F, F, F, F, F, F, F, 64, 0, NULL), GDN_ERR_ARG);
     if (gdn_prefill_workspace_bytes(&d, 0) != 0) { fprintf(stderr, "workspace bytes for 0 tokens\n"); ++failures; }
     if (gdn_prefill_workspace_bytes(&d, 8192) != 541065216u) { fprintf(stderr, "workspace bytes at 8192\n"); ++failures; }
     /* sizes, reset, snapshot */
