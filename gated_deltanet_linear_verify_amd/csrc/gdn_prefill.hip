@@ -39,7 +39,7 @@ namespace gdn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChunk = 64;  // tokens per chunk
-constexpr int kDB = 16;     // value rows per workgroup
+constexpr int kSR = 32;     // value rows per scan workgroup (two 16-row MFMA tiles)
 constexpr int kPThreads = 256;
 constexpr int kCP = kChunk + 4;  // padded row stride of the chunk x chunk matrices
 
@@ -181,6 +181,27 @@ __device__ __forceinline__ f4 mma(const Frag<F32> &a, const Frag<F32> &b, f4 acc
     return acc;
 }
 
+// N independent products acc[n] += a[n] b[n], issued term by term across n, so that consecutive
+// MFMAs never depend on each other (a dependent MFMA waits for its predecessor to finish).  Each
+// accumulator sees exactly the term order of mma().
+template <bool F32, int N>
+__device__ __forceinline__ void mma_n(const Frag<F32> (&a)[N], const Frag<F32> (&b)[N], f4 (&acc)[N])
+{
+    if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int n = 0; n < N; ++n) acc[n] = mfma4f32(a[n].v[e], b[n].v[e], acc[n]);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[n] = mfma16(a[n].lo, b[n].hi, acc[n]);
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[n] = mfma16(a[n].hi, b[n].lo, acc[n]);
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[n] = mfma16(a[n].hi, b[n].hi, acc[n]);
+    }
+}
+
 // A [ROWS][COLS] fp32 matrix kept ready for MFMA operand loads: fp32 (F32), or already split into a
 // bf16 hi plane followed by a bf16 lo plane (both the size of the fp32 matrix together).  Groups
 // of 8 consecutive columns are XOR-swizzled by the row, so the 16 rows one operand load touches
@@ -240,6 +261,26 @@ struct Mat {
             hp[ROWS * COLS + idx(r, c)] = (__bf16)(x - (float)h);
         }
     }
+    // four consecutive columns c0 .. c0 + 3 of row r (c0 a multiple of 4): one 8-byte store per
+    // bf16 plane, or one 16-byte store of fp32
+    __device__ static void put4(float *m, int r, int c0, f4 x)
+    {
+        if constexpr (F32) {
+            *reinterpret_cast<f4 *>(m + idx(r, c0)) = x;
+        } else {
+            uint32_t h[2], l[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const __bf16 h0 = (__bf16)x[2 * j], h1 = (__bf16)x[2 * j + 1];
+                const __bf16 l0 = (__bf16)(x[2 * j] - (float)h0), l1 = (__bf16)(x[2 * j + 1] - (float)h1);
+                h[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                l[j] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+            }
+            __bf16 *hp = reinterpret_cast<__bf16 *>(m);
+            *reinterpret_cast<uint2 *>(hp + idx(r, c0)) = uint2{h[0], h[1]};
+            *reinterpret_cast<uint2 *>(hp + ROWS * COLS + idx(r, c0)) = uint2{l[0], l[1]};
+        }
+    }
     __device__ static void put8(float *m, int r, int c0, const float (&x)[8])
     {
         if constexpr (F32) {
@@ -261,11 +302,11 @@ struct Mat {
 // (q, k, T and P as Mat images: fp32, or split into bf16 hi / lo planes for bf16 activations)
 //   t  [nc][H_v][64 * 64]        T = (I + A)^-1
 //   p  [nc][H_v][64 * 64]        P
-//   v  [nc][H_v][d / 16][64][16] conv'd v, one block of 16 value rows per scan workgroup
 //   g  [nc][H_v][256]            gamma | beta | exp(Gamma_C - Gamma) | 0, 64 each
+// (the scan convolves v itself from the raw activations)
 constexpr int kGateRec = 4 * kChunk;
 struct PrefillWs {
-    size_t o, qk, t, p, v, g, total;
+    size_t o, qk, t, p, g, total;
 };
 __host__ __device__ inline PrefillWs prefill_ws(int d, int n_kh, int n_vh, int T)
 {
@@ -275,8 +316,7 @@ __host__ __device__ inline PrefillWs prefill_ws(int d, int n_kh, int n_vh, int T
     w.qk = w.o + nc * kChunk * n_vh * d;
     w.t = w.qk + nc * n_kh * 2 * kChunk * d;
     w.p = w.t + nc * n_vh * kChunk * kChunk;
-    w.v = w.p + nc * n_vh * kChunk * kChunk;
-    w.g = w.v + nc * n_vh * kChunk * d;
+    w.g = w.p + nc * n_vh * kChunk * kChunk;
     w.total = w.g + nc * n_vh * kGateRec;
     return w;
 }
@@ -297,26 +337,34 @@ struct PrepLds {
 };
 static_assert(2 * PrepLds<128>::total <= 160 * 1024, "two d=128 prep workgroups must fit one CU's LDS");
 
-template <int D>
+// Scan workgroup: kSR value rows of one value head.  Its LDS, in bytes:
+template <int D, bool ACT_BF16>
 struct ScanLds {
     static constexpr int C = kChunk;
-    static constexpr size_t kimg = sizeof(float) * C * D;    // a q or k image
-    static constexpr size_t timg = sizeof(float) * C * C;    // a T or P image
-    static constexpr size_t vimg = sizeof(float) * C * kDB;  // a v block image
+    static constexpr size_t kimg = sizeof(float) * C * D;  // a q or k image
+    static constexpr size_t timg = sizeof(float) * C * C;  // a T or P image
+    // raw v rows of the block's kSR channels, window rows 0 .. C + 2 (token t0 - 3 + row), moved
+    // 1 KiB (one 64-lane 16-byte transfer) at a time
+    static constexpr int vrow = kSR * (ACT_BF16 ? 2 : 4);  // bytes per row
+    static constexpr int vrows_per_dma = 1024 / vrow;
+    static constexpr int vdmas = (C + 3 + vrows_per_dma - 1) / vrows_per_dma;
+    static constexpr size_t vimg = 1024 * vdmas;
     static constexpr size_t gimg = sizeof(float) * kGateRec;
-    static constexpr size_t kb = 0;                          // [2] k images (this chunk, next chunk)
-    static constexpr size_t vb = kb + 2 * kimg;              // [2] v block images
-    static constexpr size_t gb = vb + 2 * vimg;              // [2] gate records
-    static constexpr size_t q = gb + 2 * gimg;               // q image
+    static constexpr size_t kb = 0;                          // k image of the chunk in progress
+    static constexpr size_t q = kb + kimg;                   // q image
     static constexpr size_t tm = q + kimg;                   // T image
-    static constexpr size_t pm = tm + timg;                  // P image
-    static constexpr size_t sp = pm + timg;                  // S block [DB][D]      (operand form)
-    static constexpr size_t yp = sp + sizeof(float) * kDB * D;  // Y^T [DB][C]        (operand form)
-    static constexpr size_t up = yp + sizeof(float) * kDB * C;  // U^T [DB][C]        (operand form)
-    static constexpr size_t dp = up + sizeof(float) * kDB * C;  // U^T diag(dec) [DB][C]
-    static constexpr size_t total = dp + sizeof(float) * kDB * C;
+    static constexpr size_t pm = tm + timg;                  // [2] P images (chunk parity)
+    static constexpr size_t vb = pm + 2 * timg;              // raw v rows
+    static constexpr size_t gb = vb + vimg;                  // [2] gate records (chunk parity)
+    static constexpr size_t yp = gb + 2 * gimg;              // Y^T [kSR][C]  (operand form)
+    static constexpr size_t up = yp + sizeof(float) * kSR * C;  // U^T [kSR][C]  (operand form)
+    // U^T diag(dec) [kSR][C] (operand form; bf16 only: fp32 operands are scaled where they are read)
+    static constexpr size_t dp = up + sizeof(float) * kSR * C;
+    static constexpr size_t sx = dp + (ACT_BF16 ? sizeof(float) * kSR * C : 0);  // S [kSR][D] (operand form)
+    static constexpr size_t total = sx + sizeof(float) * kSR * D;
 };
-static_assert(ScanLds<128>::total <= 160 * 1024, "d=128 scan must fit one CU's LDS");
+static_assert(ScanLds<128, true>::total <= 160 * 1024 && ScanLds<128, false>::total <= 160 * 1024,
+              "the d=128 scan must fit one CU's LDS");
 
 // ============================== kernel 1: per (chunk, key head) ==============================
 // The q | k conv and the Gram products K K^T and Q K^T are shared by the key head's value heads;
@@ -328,7 +376,6 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     using L = PrepLds<D>;
     constexpr bool F32 = !ACT_BF16;
     constexpr int C = kChunk;
-    constexpr int NB = D / kDB;
     constexpr int QKG = 2 * D / 4;  // q | k channel groups of 4 (one per lane of a conv wave)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int R = a.n_vh / a.n_kh;
@@ -338,7 +385,6 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int Cc = a.C;  // conv channels
     const int t0 = c * C, Lc = min(C, T - t0);
     const int q0 = hk * D, k0 = a.n_kh * D + hk * D;
-    int v0 = 2 * a.n_kh * D + hk * R * D;  // v channels of the value head in progress
     const PrefillWs w = prefill_ws(D, a.n_kh, a.n_vh, T);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -351,7 +397,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     auto gate_slot = [&](int hh) { return reinterpret_cast<float *>(smem + L::gate) + (hh % L::heads) * 4 * C; };
 
     const act_t *qkv = static_cast<const act_t *>(a.qkv);
-    auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : (lc < 2 * D ? k0 + (lc - D) : v0 + (lc - 2 * D)); };
+    auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : k0 + (lc - D); };
     // Rows are loaded raw (every load of a conv issued before any is used) and converted after:
     // channels lc .. lc+3 of token t0 + t; before the first chunk the three rows at t < 0 come
     // from the conv state (fp32) instead.
@@ -409,42 +455,6 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         G[C + lane] = expf(x);
         G[2 * C + lane] = b;
         G[3 * C + lane] = expf(__shfl(x, 63) - x);
-    };
-
-    // conv of value head h's v, straight to the workspace: a thread takes 4 channels of TPT
-    // consecutive tokens.  conv_issue loads its taps and rows (the three rows before the call from
-    // the conv state too, whether or not this thread starts the call); conv_finish, issued after
-    // other work, converts them, sums the taps and stores.
-    constexpr int VG = D / 4;                // channel groups of 4
-    constexpr int TPT = C * VG / kPThreads;  // tokens per thread: 8 at d = 128, 4 at d = 64
-    const int vg = tid % VG, tb = (tid / VG) * TPT;
-    const int vlc = 2 * D + 4 * vg;
-    auto conv_issue = [&](f4 (&wv)[4], raw4 (&rw)[TPT + 3], f4 (&hs)[3]) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(vlc + e) * 4);
-#pragma unroll
-        for (int i = 0; i < TPT + 3; ++i) rw[i] = ld_raw(min(max(tb - 3 + i, tmin), Lc - 1), vlc);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) hs[i] = hist4(i - 3, vlc);
-    };
-    auto conv_finish = [&](int h, const f4 (&wv)[4], const raw4 (&rw)[TPT + 3], const f4 (&hs)[3]) {
-        const bool head_rows = c == 0 && tb == 0;  // this thread's first three rows precede the call
-        f4 xs[TPT + 3];
-#pragma unroll
-        for (int i = 0; i < TPT + 3; ++i) xs[i] = (i < 3 && head_rows) ? hs[i < 3 ? i : 0] : cvt(rw[i]);
-        float *vdst = a.ws + w.v + (((size_t)c * a.n_vh + h) * NB + vg / 4) * C * kDB + 4 * (vg % 4);
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int t = tb + i;
-            f4 y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = conv4(wv[e], xs[i][e], xs[i + 1][e], xs[i + 2][e], xs[i + 3][e]);
-                if constexpr (QKN) v = v * sigmoid_f(v);
-                y[e] = t < Lc ? v : 0.f;
-            }
-            *reinterpret_cast<f4 *>(vdst + t * kDB) = y;
-        }
     };
 
     // the first value heads' gate inputs travel with the q | k rows below
@@ -537,17 +547,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll 1
     for (int hh = 0; hh < R; ++hh) {
         const int h = hk * R + hh;
-        v0 = 2 * a.n_kh * D + h * D;
         if (hh > 0) lds_barrier();  // the previous head's T, P and gates are written out
         if (hh > 0 && hh % L::heads == 0) {  // the next group of heads' gates
             if (wave < min(R - hh, L::heads)) gate_put(hh + wave, gate_load(hh + wave));
             lds_barrier();
         }
         const float *Gam = gate_slot(hh), *gam = Gam + C, *bet = gam + C, *dec = bet + C;
-        // this head's v rows are loaded now and convolved once A / P and T are built
-        f4 cwv[4], chs[3];
-        raw4 crw[TPT + 3];
-        conv_issue(cwv, crw, chs);
         {
             float *Dm = wave < 2 ? Tm : Pm;
 #pragma unroll
@@ -626,7 +631,6 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             if (r3 == 3) acc = blk16s(Tm, 48, 48, scr, acc);
             put_neg(16 * r3, 16 * c3, acc);
         }
-        conv_finish(h, cwv, crw, chs);
         lds_barrier();
 
         // ---- T, P and the gates for the scan (T and P as Mat images)
@@ -655,45 +659,41 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // ============================== kernel 2: the chunk chain ==============================
-// Per chunk, for this workgroup's 16 value rows (S block 16 x d):
-//   A: Y^T = beta V^T - (S K^T) diag(beta gamma)        (wave w: tokens 16w .. 16w+15)
+// Per chunk, for this workgroup's kSR = 32 value rows (S block 32 x d, rows i, key columns j):
+//   A: Y^T = beta (V^T - (S K^T) diag(gamma))     V convolved here from the raw activations
 //   B: U^T = Y^T T^T
 //   C: O   = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K
-// Four compute waves run A, B, C; four producer waves move every operand into LDS with
-// global_load_lds while they compute, so the transfers' issue cost stays off the chain (one
-// producer wave alone issues them too slowly: the transfers are 1 KiB per instruction).  Per
-// chunk c the producer waits for k, v, gates and T of c (its q and P may still travel), then for
-// q and P before C, then issues T, k, v, gates of c+1 during C (k, v, gates double-buffered) and
-// q, P of c+1 once C has read this chunk's.  Only producers issue loads and the compute waves only
-// store, so every wait counts transfers of one kind on a producer's own counter.
+// Compute wave w owns tokens 16 w .. 16 w + 15 of A, B and the readout, for both 16-row tiles of the
+// block, so every q, k, T and P element is read from LDS once per chunk; its S' share is key
+// columns 16 (2 w) .. 16 (2 w) + 31 (d = 128).  Each wave reads the whole S block into registers as
+// MFMA operand fragments at the start of a chunk and uses it in A for both products that need it,
+// K S^T and Q S^T (the latter kept until C); it holds its own S' tiles in fp32.  Four producer waves
+// move the next operands in with global_load_lds while the compute waves work: q and k of c + 1 once
+// A has read them (the key columns C needs are held in registers from A on), T, P, v and the gates
+// of c + 1 once B is done; every transfer of c + 1 is waited for before the chunk starts.
+constexpr int kScanCompute = kChunk / 16;  // compute waves: one 16-token tile each
 constexpr int kProducers = 4;
-constexpr int kScanThreads = kPThreads + 64 * kProducers;
+constexpr int kScanThreads = 64 * (kScanCompute + kProducers);
 
-template <int D>
-struct ScanCounts {
-    static constexpr int per_wave(int n16) { return n16 / (64 * kProducers); }  // the minimum over producers
-    static constexpr int qp = per_wave(kChunk * D / 4) + per_wave(kChunk * kChunk / 4);
-    static_assert(qp < 64, "vmcnt holds at most 63");
-};
 // s_waitcnt immediate: wait until at most n vector-memory operations are outstanding (gfx9
 // encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
 
-template <int D, bool F32>
+template <int D, bool ACT_BF16, bool QKN>
 __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs a)
 {
-    using L = ScanLds<D>;
-    using N = ScanCounts<D>;
+    constexpr bool F32 = !ACT_BF16;
+    using L = ScanLds<D, ACT_BF16>;
     constexpr int C = kChunk;
-    constexpr int NB = D / kDB;
+    constexpr int NB = D / kSR;   // row blocks per value head
+    constexpr int KK = D / 32;    // 32-deep steps over the key dimension
     using MK = Mat<F32, C, D>;    // q and k images
     using MT = Mat<F32, C, C>;    // T and P images
-    using MS = Mat<F32, kDB, D>;  // the S block
-    using MU = Mat<F32, kDB, C>;  // Y^T, U^T, U^T diag(dec)
-    constexpr int SCT = D / 16 / 4;  // S column tiles per compute wave
+    using MS = Mat<F32, kSR, D>;  // S block
+    using MY = Mat<F32, kSR, C>;  // Y^T
+    constexpr int SCT = D / 16 / kScanCompute;     // S' column tiles per compute wave
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const bool producer = wave >= 4;
-    const int ptid = tid - kPThreads;  // producer thread index
+    const bool producer = wave >= kScanCompute;
     const int R = a.n_vh / a.n_kh;
     // workgroups are dealt to the 8 XCDs in turn: keep the row blocks of a key head's value heads on
     // one XCD, so the operand images they all read are fetched into that XCD's L2 once
@@ -702,162 +702,279 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
     const int h = idx / NB, blk = idx % NB;
     const int hk = h / R;
     const int T = a.T;
+    const int Cc = a.C;
     const int nchunks = (T + C - 1) / C;
     const PrefillWs w = prefill_ws(D, a.n_kh, a.n_vh, T);
     const int li = lane & 15, lg = lane >> 4;  // fragment row / column, 8-wide k group
+    const int vch0 = 2 * a.n_kh * D + h * D + blk * kSR;  // the block's first v channel
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float *Kb = reinterpret_cast<float *>(smem + L::kb);
-    float *Vb = reinterpret_cast<float *>(smem + L::vb);
-    float *Gb = reinterpret_cast<float *>(smem + L::gb);
+    float *Kc = reinterpret_cast<float *>(smem + L::kb);
     float *Q = reinterpret_cast<float *>(smem + L::q);
     float *Tm = reinterpret_cast<float *>(smem + L::tm);
-    float *Pm = reinterpret_cast<float *>(smem + L::pm);
-    float *Sp = reinterpret_cast<float *>(smem + L::sp);
+    float *Pb = reinterpret_cast<float *>(smem + L::pm);
+    unsigned char *Vr = smem + L::vb;
+    float *Gb = reinterpret_cast<float *>(smem + L::gb);
     float *Yp = reinterpret_cast<float *>(smem + L::yp);
-    float *Up = reinterpret_cast<float *>(smem + L::up);
-    float *Dp = reinterpret_cast<float *>(smem + L::dp);
+    float *Up = reinterpret_cast<float *>(smem + L::up);  // U^T, operand form
+    float *Sx = reinterpret_cast<float *>(smem + L::sx);
 
-    // ---- the producers' transfers (lane i of a global_load_lds lands at the base + 16 i)
-    auto dma = [&](const float *g, float *l, int n16) {
-        for (int i = ptid; i < n16; i += 64 * kProducers) lds_dma16(g + 4 * i, l + 4 * i);
+    // ---- the producers' transfers (lane i of a global_load_lds lands at the base + 16 i).  N16
+    // 16-byte pieces, a multiple of 64 per producer wave: a fixed number of whole-wave transfers per
+    // wave, unrolled, each at a wave-uniform LDS base.
+    const int pw = __builtin_amdgcn_readfirstlane(wave - kScanCompute);  // producer index
+    auto dma = [&](auto n16_c, const float *g, float *l) {
+        constexpr int N16 = decltype(n16_c)::value;
+        static_assert(N16 % (64 * kProducers) == 0, "whole-wave transfers, the same count on every producer");
+#pragma unroll
+        for (int k = 0; k < N16 / (64 * kProducers); ++k) {
+            const int i0 = 64 * (pw + k * kProducers);
+            lds_dma16(g + 4 * (i0 + lane), l + 4 * i0);
+        }
     };
     auto qk_img = [&](int cc, int which) { return a.ws + w.qk + (((size_t)cc * a.n_kh + hk) * 2 + which) * C * D; };
-    auto issue_tkvg = [&](int cc) {  // T, then k, v, gates into buffer cc & 1
-        const int b = cc & 1;
-        const size_t ch = (size_t)cc * a.n_vh + h;
-        dma(a.ws + w.t + ch * C * C, Tm, C * C / 4);
-        dma(qk_img(cc, 1), Kb + b * C * D, C * D / 4);
-        dma(a.ws + w.v + (ch * NB + blk) * C * kDB, Vb + b * C * kDB, C * kDB / 4);
-        dma(a.ws + w.g + ch * kGateRec, Gb + b * kGateRec, kGateRec / 4);
+    auto chunk_rec = [&](int cc) { return (size_t)cc * a.n_vh + h; };
+    using img16 = std::integral_constant<int, C * D / 4>;  // a q or k image in 16-byte pieces
+    using mat16 = std::integral_constant<int, C * C / 4>;  // a T or P image
+    auto issue_k = [&](int cc) { dma(img16{}, qk_img(cc, 1), Kc); };
+    using half16 = std::integral_constant<int, C * D / 8>;
+    auto issue_q = [&](int cc, int half) {  // one half of the q image
+        dma(half16{}, qk_img(cc, 0) + half * (C * D / 2), Q + half * (C * D / 2));
     };
-    auto issue_qp = [&](int cc) {
-        dma(qk_img(cc, 0), Q, C * D / 4);
-        dma(a.ws + w.p + ((size_t)cc * a.n_vh + h) * C * C, Pm, C * C / 4);
-    };
-
-    // ---- prologue: the state block.  Each compute lane keeps the S elements its S' tiles produce,
-    // in fp32 registers (rows i = 4 lg + r, columns j = 16 ct + li of its tiles ct); the LDS copy is
-    // only the operand form.
-    float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kDB * D;
-    f4 sreg[SCT];
-    if (producer) {
-        issue_tkvg(0);
-        issue_qp(0);
-    } else {
-#pragma unroll
-        for (int q2 = 0; q2 < SCT; ++q2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sreg[q2][r] = st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li];
-#pragma unroll
-        for (int q2 = 0; q2 < SCT; ++q2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
-    }
-
-    f4 o_prev = {0.f, 0.f, 0.f, 0.f};
-    auto store_o = [&](int cc) {  // rows t = 16 w + 4 lg + r of chunk cc; whole chunks fit
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = cc * C + 16 * wave + 4 * lg + r;
-            a.ws[w.o + ((size_t)t * a.n_vh + h) * D + blk * kDB + li] = o_prev[r];
+    auto issue_t = [&](int cc) { dma(mat16{}, a.ws + w.t + chunk_rec(cc) * C * C, Tm); };
+    auto issue_pg = [&](int cc) {  // P and the gate record of chunk cc (one transfer per producer each)
+        dma(mat16{}, a.ws + w.p + chunk_rec(cc) * C * C, Pb + (cc & 1) * C * C);
+        if (lane < kGateRec / 4 / kProducers) {
+            const int i0 = pw * (kGateRec / 4 / kProducers);
+            lds_dma16(a.ws + w.g + chunk_rec(cc) * kGateRec + 4 * (i0 + lane), Gb + (cc & 1) * kGateRec + 4 * i0);
         }
     };
+    auto issue_v = [&](int cc) {  // raw v rows of chunk cc
+        constexpr int lpr = L::vrow / 16;  // lanes per raw row
+#pragma unroll
+        for (int k = 0; k < (L::vdmas + kProducers - 1) / kProducers; ++k) {
+            const int j = pw + k * kProducers;
+            if (j < L::vdmas) {
+                const int row = j * L::vrows_per_dma + lane / lpr;
+                const int tok = min(max(cc * C - 3 + row, 0), T - 1);  // rows outside the call are never used
+                const unsigned char *g = static_cast<const unsigned char *>(a.qkv) +
+                                         ((size_t)tok * Cc + vch0) * (ACT_BF16 ? 2 : 4) + 16 * (lane % lpr);
+                lds_dma16(g, Vr + 1024 * j);
+            }
+        }
+    };
+    // transfers per producer wave: T, P (uniform), and one gate transfer each
+    constexpr int NT = C * C / 4 / (64 * kProducers);
+    static_assert(NT * 64 * kProducers == C * C / 4 && NT + NT + 1 < 64, "T and P split evenly over the producers");
+    static_assert(kGateRec / 4 / kProducers <= 64, "a gate record is one partial transfer per producer");
+
+    // The producers and the compute waves run separate loops with the same three barriers per
+    // chunk.  (In one shared loop the compiler would have to assume a transfer into LDS in flight
+    // on the compute waves' path too, and make them wait for all their own vector-memory operations
+    // before touching LDS.)
+    // A buffer is refilled as soon as the phase that reads it is done: P and the gates (double
+    // buffered) of c + 1 during A of c; k, v and half of q of c + 1 during B (A has read k, v and q
+    // of c); the other half of q and T of c + 1 during C.  T is issued last and needed only by B, so
+    // the chunk start waits for everything else and the barrier after A for T.
+    if (producer) {
+        issue_pg(0);
+        issue_k(0);
+        issue_v(0);
+        issue_q(0, 0);
+        issue_q(0, 1);
+        issue_t(0);
+#pragma unroll 1
+        for (int c = 0; c < nchunks; ++c) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NT));  // q, k, v, P, gates of c have landed (T may travel)
+            lds_barrier();                                // chunk start
+            if (c + 1 < nchunks) {
+                issue_pg(c + 1);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(NT + 1));  // T of c (P, gates of c + 1 may travel)
+            } else {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
+            lds_barrier();  // A done: q, k and v of c are consumed; T of c has landed
+            if (c + 1 < nchunks) {
+                issue_k(c + 1);
+                issue_v(c + 1);
+                issue_q(c + 1, 0);
+            }
+            lds_barrier();  // B done: T of c is consumed
+            if (c + 1 < nchunks) {
+                issue_q(c + 1, 1);
+                issue_t(c + 1);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no transfer into LDS outlives the workgroup
+        return;
+    }
+
+    // ---- compute waves.  State: the S block's fp32 elements this wave produces (row 16 rt + li, key
+    // columns 16 (SCT w + q2) + 4 lg .. + 3: S' is computed transposed, so a lane holds four
+    // consecutive columns of one row), the conv taps and the conv-state rows of its v channels
+    float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kSR * D;
+    float *Dp = reinterpret_cast<float *>(smem + L::dp);
+    f4 sreg[2][SCT];
+    f4 wv[2];
+    float hist[2][3];
+    auto s_at = [&](int rt, int q2) { return (size_t)(16 * rt + li) * D + 16 * (SCT * wave + q2) + 4 * lg; };
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int q2 = 0; q2 < SCT; ++q2) sreg[rt][q2] = *reinterpret_cast<const f4 *>(st + s_at(rt, q2));
+        const int vc = vch0 + 16 * rt + li;
+        wv[rt] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)vc * 4);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) hist[rt][m] = a.conv_state[((size_t)a.slot * 3 + m) * Cc + vc];
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int q2 = 0; q2 < SCT; ++q2) MS::put4(Sx, 16 * rt + li, 16 * (SCT * wave + q2) + 4 * lg, sreg[rt][q2]);
+    auto raw_v = [&](int row, int ch) -> float {  // window row of the chunk, block channel
+        if constexpr (ACT_BF16)
+            return bf16_to_f32(reinterpret_cast<const uint16_t *>(Vr)[row * kSR + ch]);
+        else
+            return reinterpret_cast<const float *>(Vr)[row * kSR + ch];
+    };
+    const int t4 = 16 * wave + 4 * lg;  // this lane's four tokens in A and B
+    const int tr = 16 * wave + li;      // this lane's token in the readout (computed transposed)
+
 #pragma unroll 1
     for (int c = 0; c < nchunks; ++c) {
-        const int b = c & 1;
-        const float *K = Kb + b * C * D;
-        const float *Vc = Vb + b * C * kDB;
-        const float *gam = Gb + b * kGateRec;
+        const float *gam = Gb + (c & 1) * kGateRec;
         const float *bet = gam + C;
         const float *dec = bet + C;
-        if (producer) __builtin_amdgcn_s_waitcnt(vmcnt_imm(N::qp));  // T, k, v, gates of c (q, P may travel)
-        lds_barrier();
-        // ---- A: Y^T[i][t] = beta_t (V[t][i] - gamma_t (K S^T)[t][i])
-        if (!producer) {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float *Pm = Pb + (c & 1) * C * C;
+        lds_barrier();  // chunk start: the operands of c and S are in LDS
+        // ---- A: (K S^T)[t][i] for tokens t4 + r, rows 16 rt + li, and the readout's S Q^T [i][t]
+        // for rows 16 rt + 4 lg + r, token tr; then Y^T[i][t] = beta_t (v_t[i] - gamma_t (K S^T)[t][i])
+        Frag<F32> kf[SCT][2];  // K columns of this wave's S' tiles (C's A operand)
+        f4 acc4[4] = {};       // K S^T of tiles 0, 1, then S Q^T of tiles 0, 1
 #pragma unroll
-            for (int kk = 0; kk < D; kk += 32)
-                acc = mma<F32>(MK::load(K, 16 * wave + li, kk + 8 * lg), MS::load(Sp, li, kk + 8 * lg), acc);
+        for (int kk = 0; kk < KK; ++kk) {
+            const Frag<F32> kr = MK::load(Kc, tr, 32 * kk + 8 * lg);
+            const Frag<F32> qr = MK::load(Q, tr, 32 * kk + 8 * lg);
+            const Frag<F32> s0 = MS::load(Sx, li, 32 * kk + 8 * lg);
+            const Frag<F32> s1 = MS::load(Sx, 16 + li, 32 * kk + 8 * lg);
+            const Frag<F32> fa[4] = {kr, kr, s0, s1}, fb[4] = {s0, s1, qr, qr};
+            mma_n<F32, 4>(fa, fb, acc4);
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + 4 * lg + r;
-                MU::put(Yp, li, t, bet[t] * (Vc[t * kDB + li] - gam[t] * acc[r]));
+        for (int q2 = 0; q2 < SCT; ++q2) {
+            const int j0 = 16 * (SCT * wave + q2);
+#pragma unroll
+            for (int kk2 = 0; kk2 < 2; ++kk2) {
+                if constexpr (F32) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) MK::get(Kc, 32 * kk2 + 8 * lg + e, j0 + li, kf[q2][kk2], e);
+                } else {
+                    kf[q2][kk2] = MK::load_col(Kc, 32 * kk2 + 8 * lg, j0, li);
+                }
             }
         }
-        lds_barrier();
-        // ---- B: U = T Y; U^T and U^T diag(dec) in operand form
-        if (!producer) {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+        {
+            const f4 g4 = *reinterpret_cast<const f4 *>(gam + t4);
+            const f4 b4 = *reinterpret_cast<const f4 *>(bet + t4);
+            const bool from_state = c == 0 && t4 == 0;  // window rows 0..2 precede the call
 #pragma unroll
-            for (int kk = 0; kk < C; kk += 32)
-                acc = mma<F32>(MT::load(Tm, 16 * wave + li, kk + 8 * lg), MU::load(Yp, li, kk + 8 * lg), acc);
+            for (int rt = 0; rt < 2; ++rt) {
+                const int ch = 16 * rt + li;
+                float xr[7];  // window rows t4 .. t4 + 6 of channel ch, every read issued before any use
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + 4 * lg + r;
-                MU::put(Up, li, t, acc[r]);
-                MU::put(Dp, li, t, acc[r] * dec[t]);
+                for (int m = 0; m < 7; ++m) xr[m] = raw_v(t4 + m, ch);
+#pragma unroll
+                for (int m = 0; m < 3; ++m) xr[m] = from_state ? hist[rt][m] : xr[m];
+                f4 y;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = conv4(wv[rt], xr[r], xr[r + 1], xr[r + 2], xr[r + 3]);
+                    if constexpr (QKN) v = v * sigmoid_f(v);
+                    y[r] = b4[r] * (v - g4[r] * acc4[rt][r]);
+                }
+                MY::put4(Yp, ch, t4, y);
             }
-        } else {
-            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): q and P of chunk c
         }
-        lds_barrier();  // q and P have landed; every compute wave is done with T
-        if (producer) {
-            if (c + 1 < nchunks) issue_tkvg(c + 1);  // k, v, gates into the buffer chunk c-1 used
-        } else {
-            if (c > 0) store_o(c - 1);
-            // ---- C: O = diag(gamma) Q S^T + P U ;  S' = gamma_C S + (U^T diag(dec)) K
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+        lds_barrier();  // Y^T is in LDS; q, k and the raw v rows are consumed
+        // ---- B: U[t][i] = sum_s T[t][s] Y[s][i]; U^T (and U^T diag(dec)) into LDS in operand form
+        {
+            f4 part[4] = {};  // tile 0 and 1 over tokens 0..31, then over 32..63
+            const Frag<F32> t0 = MT::load(Tm, tr, 8 * lg), t1 = MT::load(Tm, tr, 32 + 8 * lg);
+            const Frag<F32> fa[4] = {t0, t0, t1, t1};
+            const Frag<F32> fb[4] = {MY::load(Yp, li, 8 * lg), MY::load(Yp, 16 + li, 8 * lg),
+                                     MY::load(Yp, li, 32 + 8 * lg), MY::load(Yp, 16 + li, 32 + 8 * lg)};
+            mma_n<F32, 4>(fa, fb, part);
+            const f4 d4 = *reinterpret_cast<const f4 *>(dec + t4);
 #pragma unroll
-            for (int kk = 0; kk < D; kk += 32)
-                acc = mma<F32>(MK::load(Q, 16 * wave + li, kk + 8 * lg), MS::load(Sp, li, kk + 8 * lg), acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= gam[16 * wave + 4 * lg + r];
-#pragma unroll
-            for (int kk = 0; kk < C; kk += 32)
-                acc = mma<F32>(MT::load(Pm, 16 * wave + li, kk + 8 * lg), MU::load(Up, li, kk + 8 * lg), acc);
-            o_prev = acc;
+            for (int rt = 0; rt < 2; ++rt) {
+                const f4 u = part[rt] + part[2 + rt];
+                MY::put4(Up, 16 * rt + li, t4, u);
+                if constexpr (!F32) MY::put4(Dp, 16 * rt + li, t4, u * d4);
+            }
+        }
+        lds_barrier();  // U^T is in LDS; T is consumed
+        // ---- C: O^T = (S Q^T) diag(gamma) + U^T P^T, then S'^T = gamma_C S^T + K^T (U^T diag(dec))^T.
+        // S' goes into LDS for every wave; no wave reads S there before the next chunk.
+        {
             const float gC = gam[C - 1];
+            const float gt = gam[tr];
+            Frag<F32> uf[2][2], udf[2][2], pr[2];  // [tile][token half], [token half]
 #pragma unroll
-            for (int q2 = 0; q2 < SCT; ++q2) {
-                const int j = 16 * (SCT * wave + q2) + li;
-                f4 sa;
+            for (int h2 = 0; h2 < 2; ++h2) {
+                pr[h2] = MT::load(Pm, tr, 32 * h2 + 8 * lg);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sa[r] = gC * sreg[q2][r];
-#pragma unroll
-                for (int kk = 0; kk < C; kk += 32) {
-                    Frag<F32> kf;  // K[s][j] down the column, s = kk + 8 lg + e
+                for (int rt = 0; rt < 2; ++rt) {
+                    uf[rt][h2] = MY::load(Up, 16 * rt + li, 32 * h2 + 8 * lg);
                     if constexpr (F32) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) MK::get(K, kk + 8 * lg + e, j, kf, e);
+                        for (int e = 0; e < 8; ++e) udf[rt][h2].v[e] = uf[rt][h2].v[e] * dec[32 * h2 + 8 * lg + e];
                     } else {
-                        kf = MK::load_col(K, kk + 8 * lg, j - li, li);
+                        udf[rt][h2] = MY::load(Dp, 16 * rt + li, 32 * h2 + 8 * lg);
                     }
-                    sa = mma<F32>(MU::load(Dp, li, kk + 8 * lg), kf, sa);
                 }
-                sreg[q2] = sa;
             }
-        }
-        lds_barrier();  // every compute wave is done reading S, q, P and this chunk's k
-        if (producer) {
-            if (c + 1 < nchunks) issue_qp(c + 1);
-        } else {
+            // accumulators: the readout of tiles 0, 1, then S'^T of (tile, column tile) 00 01 10 11
+            f4 acc6[2 + 2 * SCT];
+            acc6[0] = acc4[2] * gt;
+            acc6[1] = acc4[3] * gt;
 #pragma unroll
-            for (int q2 = 0; q2 < SCT; ++q2)
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) MS::put(Sp, 4 * lg + r, 16 * (SCT * wave + q2) + li, sreg[q2][r]);
+                for (int q2 = 0; q2 < SCT; ++q2) acc6[2 + rt * SCT + q2] = sreg[rt][q2] * gC;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                Frag<F32> fa[2 + 2 * SCT], fb[2 + 2 * SCT];
+                fa[0] = uf[0][h2];
+                fa[1] = uf[1][h2];
+                fb[0] = fb[1] = pr[h2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int q2 = 0; q2 < SCT; ++q2) {
+                        fa[2 + rt * SCT + q2] = kf[q2][h2];
+                        fb[2 + rt * SCT + q2] = udf[rt][h2];
+                    }
+                mma_n<F32, 2 + 2 * SCT>(fa, fb, acc6);
+            }
+            // the readout: rows 16 rt + 4 lg .. + 3 of token tr, four consecutive floats (whole
+            // chunks fit the readout)
+            float *orow = a.ws + w.o + ((size_t)(c * C + tr) * a.n_vh + h) * D + blk * kSR + 4 * lg;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) *reinterpret_cast<f4 *>(orow + 16 * rt) = acc6[rt];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int q2 = 0; q2 < SCT; ++q2) {
+                    sreg[rt][q2] = acc6[2 + rt * SCT + q2];
+                    MS::put4(Sx, 16 * rt + li, 16 * (SCT * wave + q2) + 4 * lg, sreg[rt][q2]);
+                }
         }
     }
-    if (producer) {
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no transfer into LDS outlives the workgroup
-    } else {
-        if (nchunks > 0) store_o(nchunks - 1);
-        // ---- the state block after the last token
+    // ---- the state block after the last token
 #pragma unroll
-        for (int q2 = 0; q2 < SCT; ++q2)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[(size_t)(4 * lg + r) * D + 16 * (SCT * wave + q2) + li] = sreg[q2][r];
-    }
+        for (int q2 = 0; q2 < SCT; ++q2) *reinterpret_cast<f4 *>(st + s_at(rt, q2)) = sreg[rt][q2];
 }
 
 // N consecutive activations (bf16 or fp32) at element offset off, as fp32; off is a multiple of N.
@@ -972,9 +1089,9 @@ size_t prefill_workspace_bytes(int d, int n_kh, int n_vh, int T)
 
 size_t prefill_lds_bytes(int d, bool act_bf16)
 {
-    (void)act_bf16;  // neither kernel stages raw activations in LDS
     const size_t prep = d == 128 ? PrepLds<128>::total : PrepLds<64>::total;
-    const size_t scan = d == 128 ? ScanLds<128>::total : ScanLds<64>::total;  // the same for both dtypes
+    const size_t scan = d == 128 ? (act_bf16 ? ScanLds<128, true>::total : ScanLds<128, false>::total)
+                                 : (act_bf16 ? ScanLds<64, true>::total : ScanLds<64, false>::total);
     return prep > scan ? prep : scan;
 }
 
@@ -985,8 +1102,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     const size_t prep_lds = PrepLds<D>::total;
     hipLaunchKernelGGL((prefill_prep_kernel<D, AB, QKN>), dim3(nchunks * a.n_kh), dim3(kPThreads), prep_lds, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<D, !AB>), dim3(a.n_vh * (D / kDB)), dim3(kScanThreads), ScanLds<D>::total,
-                       stream, a);
+    hipLaunchKernelGGL((prefill_scan_kernel<D, AB, QKN>), dim3(a.n_vh * (D / kSR)), dim3(kScanThreads),
+                       (ScanLds<D, AB>::total), stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     const long rows = (long)a.T * a.n_vh;
     const long row_blocks = (rows + 16 * kNormRows - 1) / (16 * kNormRows);
