@@ -250,7 +250,7 @@ GDN_API int gdn_verify_tree(const gdn_dims *dims, const float *state, const floa
         return fail(GDN_ERR_RANGE, "gdn_verify_tree: n_batch %d outside [1, n_pool = %d]", n_batch, d.n_pool);
     if (int r = check_capture(capture, GDN_TREE, n_tok, dims)) return r;
     if (gdn::verify_tree_lds_bytes(d.d_k, n_tok, d.act_dtype == GDN_BF16) > kMaxLds)
-        return fail(GDN_ERR_SHAPE, "gdn_verify_tree: %d nodes do not fit one workgroup's LDS (at most 64 nodes)", n_tok);
+        return fail(GDN_ERR_SHAPE, "gdn_verify_tree: %d nodes: at most 1024 per call", n_tok);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (d.flags & GDN_F_CHECK_INDICES) {
         if (int r = check_slots(slot_ids, n_batch, d.n_pool, st)) return r;

@@ -7,9 +7,13 @@
 // root.  Every node's state and 3-row conv state are captured so that gdn_rollback can commit any
 // accepted node; the committed state and conv state are left untouched.
 //
-// One workgroup per (batch entry, value head).  A prologue stages the raw q|k|v rows of all nodes
-// in LDS (global_load_lds), computes every node's conv output, gate and beta into LDS, and
-// builds a depth-first processing schedule.  The node loop then runs in DFS order: a node whose
+// One workgroup per (batch entry, value head).  A launch covers up to kTreeMaxNodes nodes (what one
+// workgroup's LDS holds); a larger tree is consecutive launches over consecutive node ranges.  A node
+// whose parent belongs to an earlier launch starts from that parent's captured state, which each
+// lane reads back from exactly the capture elements it stored itself (the launch boundary orders
+// the two), and its conv window reads the raw rows of ancestors outside the launch from qkv.
+// A prologue stages the raw q|k|v rows of the launch's nodes in LDS (global_load_lds), computes
+// every node's conv output, gate and beta into LDS, and builds a depth-first processing schedule.  The node loop then runs in DFS order: a node whose
 // parent is the node just processed continues from the state in registers (each step is
 // Geo::step, the same arithmetic as the chain kernel).  A node with two or more children leaves a
 // register copy of its state in one of kTreeSaved save slots, which its later children restore;
@@ -26,15 +30,18 @@
 
 namespace gdn {
 
-constexpr int kTreeMaxNodes = 64;
+constexpr int kTreeMaxNodes = 64;      // nodes per launch
+constexpr int kTreeMaxTotal = 1024;    // nodes per call
 constexpr int kTreeSaved = 3;  // register save slots for states that later siblings restore
-// Schedule entry: node index (bits 0-7) | restart-from-committed-state flag | capture-and-output
-// flag | 1 + the save slot restored before the step (bits 10-11, 0: none) | 1 + the save slot
-// written after it (bits 12-13, 0: none).
+// Schedule entry: node index within the launch (bits 0-7) | restart-from-committed-state flag |
+// capture-and-output flag | 1 + the save slot restored before the step (bits 10-11, 0: none) |
+// 1 + the save slot written after it (bits 12-13, 0: none) | start-from-the-parent's-capture flag
+// (the parent belongs to an earlier launch).
 constexpr int kSchedRestart = 0x100;
 constexpr int kSchedEmit = 0x200;
 constexpr int kSchedRestoreShift = 10;
 constexpr int kSchedSaveShift = 12;
+constexpr int kSchedLoad = 0x4000;
 constexpr int kSchedMax = kTreeMaxNodes * (kTreeMaxNodes + 1) / 2 + kTreeMaxNodes;
 
 // Waves per head: twice the chain kernel's.  A tree's node steps form one dependent chain per
@@ -75,31 +82,38 @@ struct TreeLds {
 // in its own slot d' mod kTreeSaved); a later child restores the parent's copy unless a node
 // visited in between was saved at depth d' >= d + kTreeSaved, which overwrote it, and then re-runs
 // the parent's root path from the committed state instead (compute only, nothing stored).
-// anc[4 n + 3] holds node n's parent.
-__device__ __forceinline__ void build_schedule(int T, int lane, const int *anc, uint16_t *sched, int *nsched)
+// anc[4 n + 3] holds node n's parent (a node index of the whole call); the launch's nodes start at
+// base.  A node whose parent lies before base is a root of the launch that starts from the parent's
+// capture instead of the committed state.
+__device__ __forceinline__ void build_schedule(int T, int base, int lane, const int *anc, uint16_t *sched, int *nsched)
 {
     auto rl = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };  // v of lane l (uniform l)
     auto from = [](int v, int l) { return __shfl(v, l); };                   // v of lane l (per lane)
     const bool node = lane < T;
     int par = -1;
+    bool ext = false;  // the node's parent is in an earlier launch
     if (node) {
         const int p = anc[lane * 4 + 3];
-        par = (p >= -1 && p < lane) ? p : -1;  // a malformed parent makes a root
+        const int pg = (p >= -1 && p < base + lane) ? p : -1;  // a malformed parent makes a root
+        par = pg >= base ? pg - base : -1;
+        ext = pg >= 0 && pg < base;
     }
     // ancestor-or-self mask (two words) and depth: walk up, one level per round
     uint32_t am_lo = node && lane < 32 ? 1u << lane : 0u, am_hi = node && lane >= 32 ? 1u << (lane - 32) : 0u;
     // The loops below are branch-free (selects, not conditions) and the ones over all lanes run a
     // fixed 64 times, lanes past T standing for no node (parent -1, size 0, no ancestors): they add
     // nothing, and the loops unroll.
-    int depth = 0;
+    int depth = 0, root = lane;  // root: the topmost ancestor within the launch
     for (int a = par; __any(a >= 0);) {
         const bool in = a >= 0;
         const int up = from(par, in ? a : 0);
         am_lo |= in && a < 32 ? 1u << (a & 31) : 0u;
         am_hi |= in && a >= 32 ? 1u << (a & 31) : 0u;
         depth += in ? 1 : 0;
+        root = in ? a : root;
         a = in ? up : -1;
     }
+    const bool root_ext = from((int)ext, root) != 0;  // a re-run of the root path starts from a capture
     // children and subtree sizes
     int kids = 0, size = 0;
 #pragma unroll
@@ -161,15 +175,15 @@ __device__ __forceinline__ void build_schedule(int T, int lane, const int *anc, 
         const int y = __shfl_up(incl, o);
         if (lane >= o) incl += y;
     }
-    const int base = from(incl - cnt_at, pre);
+    const int first = from(incl - cnt_at, pre);  // this node's first schedule entry
     if (node) {
         int e = lane | kSchedEmit;
         if (par < 0)
-            e |= kSchedRestart;
+            e |= ext ? kSchedLoad : kSchedRestart;
         else if (restore && live)
             e |= (dq % kTreeSaved + 1) << kSchedRestoreShift;
         if (kids >= 2) e |= (d % kTreeSaved + 1) << kSchedSaveShift;
-        int at = base;
+        int at = first;
         if (rerun) {  // the parent's root path in index order: ancestors have smaller indices
             uint32_t lo = amq_lo, hi = amq_hi;
             for (int k = 0; lo | hi; ++k) {
@@ -178,7 +192,7 @@ __device__ __forceinline__ void build_schedule(int T, int lane, const int *anc, 
                     lo &= lo - 1;
                 else
                     hi &= hi - 1;
-                sched[at++] = (uint16_t)(x | (k == 0 ? kSchedRestart : 0));
+                sched[at++] = (uint16_t)(x | (k == 0 ? (root_ext ? kSchedLoad : kSchedRestart) : 0));
             }
         }
         sched[at] = (uint16_t)e;
@@ -187,7 +201,9 @@ __device__ __forceinline__ void build_schedule(int T, int lane, const int *anc, 
     if (lane == 0) *nsched = total;
 }
 
-template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN>
+// LATER: the launch follows an earlier one of the same call (its first node is not node 0); only
+// such launches carry the code that reads state and conv rows written or staged before them.
+template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN, bool LATER>
 __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(VerifyArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
@@ -197,7 +213,9 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     constexpr int VEC = 16 / (int)sizeof(act_t);
     constexpr int NCH = 3 * D;  // q | k | v channels of this value head
     const int R = a.n_vh / a.n_kh;
-    const int T = a.T;
+    const int T = a.T;      // nodes of the whole call: the row stride of qkv, z, alpha, beta, parent, out
+    const int base = LATER ? a.t0 : 0;  // first node of this launch
+    const int NT = a.nt;    // nodes of this launch, 1 .. kTreeMaxNodes
     const int tid = threadIdx.x;
     const int nthr = NW * 64;
     const int wave = tid >> 6, lane = tid & 63;
@@ -211,14 +229,16 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     if (s < 0 || s >= a.n_pool) return;  // uniform over the workgroup
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    float *qs = reinterpret_cast<float *>(smem_raw);  // [T][D]
-    float *ks = qs + T * D;                            // [T][D]
-    float *vs = ks + T * D;                            // [T][D]   rows in perm order
-    act_t *raw = reinterpret_cast<act_t *>(vs + T * D);  // [T][3D]  raw q|k|v rows (prologue)
-    float *os = reinterpret_cast<float *>(raw);          // [T][D]   readout, rows in perm order (loop)
-    float *rbk = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(raw) + L::region(T));  // [T][4]
-    int *anc = reinterpret_cast<int *>(rbk + 4 * T);  // [T][4]: ancestors 1..3 (>= 0 node, -1-r conv row r)
-    uint16_t *sched = reinterpret_cast<uint16_t *>(anc + 4 * T);
+    // LDS rows are the launch's nodes, 0 .. NT-1 (node base + i of the call)
+    float *qs = reinterpret_cast<float *>(smem_raw);  // [NT][D]
+    float *ks = qs + NT * D;                           // [NT][D]
+    float *vs = ks + NT * D;                           // [NT][D]   rows in perm order
+    act_t *raw = reinterpret_cast<act_t *>(vs + NT * D);  // [NT][3D]  raw q|k|v rows (prologue)
+    float *os = reinterpret_cast<float *>(raw);           // [NT][D]   readout, rows in perm order (loop)
+    float *rbk = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(raw) + L::region(NT));  // [NT][4]
+    // [NT][4]: ancestors 1..3 (>= 0 node of the call, -1-r conv row r), parent (node of the call)
+    int *anc = reinterpret_cast<int *>(rbk + 4 * NT);
+    uint16_t *sched = reinterpret_cast<uint16_t *>(anc + 4 * NT);
     int *nsched = reinterpret_cast<int *>(sched + kSchedMax);
 
     const int C = a.C;
@@ -233,18 +253,19 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         else
             return x;
     };
-    // a malformed parent (outside [-1, i)) is treated as -1: the node starts from the committed state.
-    // Parents are read from LDS (slot 3 of each node's ancestor record), filled once at staging.
-    auto parent_of = [&](int i) -> int {
-        const int p = anc[i * 4 + 3];
-        return (p >= -1 && p < i) ? p : -1;
+    // a malformed parent (outside [-1, n)) is treated as -1: the node starts from the committed state.
+    // Parents of the launch's nodes are read from LDS (slot 3 of each node's ancestor record, filled
+    // once at staging), those of earlier nodes from the parent array.
+    auto parent_of = [&](int n) -> int {  // n: node of the call
+        const int p = (!LATER || n >= base) ? anc[(n - base) * 4 + 3] : par[n];
+        return (p >= -1 && p < n) ? p : -1;
     };
 
     // ================= stage: raw rows of all nodes into LDS, everything else into registers ====
     const int nvr = NCH / VEC;
-    for (int it = tid; it < T * nvr; it += nthr) {
+    for (int it = tid; it < NT * nvr; it += nthr) {
         const int r = it / nvr, lc = (it % nvr) * VEC;
-        lds_dma16(qkv_b + (uint32_t)(r * C + gchan(lc)), raw + it * VEC);
+        lds_dma16(qkv_b + (uint32_t)((base + r) * C + gchan(lc)), raw + it * VEC);
     }
     // conv channels: thread 64 + lc takes channel lc (wave 0 builds the schedule meanwhile)
     static_assert(NCH <= 64 * (NW - 1) && NCH % 64 == 0, "one conv channel per thread of whole waves 1 ..");
@@ -259,12 +280,12 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         cs1 = cs_s[(uint32_t)(C + gc)];
         cs2 = cs_s[(uint32_t)(2 * C + gc)];
     }
-    // alpha, beta and the parent of node tid.  The loads sit outside any branch (threads past T load
-    // node T-1's) and nothing is computed from them before the wait below: a bf16 conversion, or a
-    // branch join over a loaded register, would make the compiler wait for every load issued so
-    // far before the state loads start.
+    // alpha, beta and the parent of node base + tid.  The loads sit outside any branch (threads past
+    // the launch's nodes load its last node's) and nothing is computed from them before the wait
+    // below: a bf16 conversion, or a branch join over a loaded register, would make the compiler wait
+    // for every load issued so far before the state loads start.
     using word_t = typename std::conditional<ACT_BF16, uint16_t, uint32_t>::type;  // bf16 or fp32 bits
-    const int node = min(tid, T - 1);
+    const int node = base + min(tid, NT - 1);
     const size_t tok = ((size_t)b * T + node) * a.n_vh + h;
     uint32_t al_raw = static_cast<const word_t *>(a.alpha)[tok];
     uint32_t be_raw = static_cast<const word_t *>(a.beta)[tok];
@@ -291,7 +312,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     word_t zr[NPG][EPL];
 #pragma unroll
     for (int k = 0; k < NPG; ++k) {
-        const int zn = min((tid >> 4) + k * NGRP, T - 1);  // past the last node: a valid row, unused
+        const int zn = base + min((tid >> 4) + k * NGRP, NT - 1);  // past the last node: a valid row, unused
         const word_t *zp = static_cast<const word_t *>(a.z) + (((size_t)b * T + zn) * a.n_vh + h) * D + cg * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) zr[k][e] = zp[e];
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         else
             return __builtin_bit_cast(float, w);
     };
-    if (tid < T) {
+    if (tid < NT) {
         const float g = -expf(alog) * softplus_f(word_f32(al_raw) + dtb);
         rbk[tid * 4 + 0] = expf(g);
         rbk[tid * 4 + 1] = word_f32(be_raw);
@@ -316,9 +337,9 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     __syncthreads();
     // ancestors 1..3 of every node (its conv window); where the root path ends, the slot's conv
     // state rows fill in: with L path nodes inside the window, ancestor j > L-1 is conv row 2-(j-L)
-    if (tid < T) {
+    if (tid < NT) {
         int code[3];
-        int m = tid, L = 1;
+        int m = base + tid, L = 1;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             m = m >= 0 ? parent_of(m) : -1;
@@ -335,22 +356,28 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
     __syncthreads();
 
     if (wave == 0) {
-        build_schedule(T, lane, anc, sched, nsched);
+        build_schedule(NT, base, lane, anc, sched, nsched);
     } else if (conv_thread) {
         // ================= conv of every node (one thread per channel) + conv-state capture =====
-        float *cct = a.cap_conv + (size_t)s * a.t_cap * 3 * C;  // [t_cap][3][C] of this slot
+        float *cct = a.cap_conv + ((size_t)s * a.t_cap + base) * 3 * C;  // [t_cap][3][C] of this slot, from node base
         const int gc = gchan(lc);
         const bool own = lc >= 2 * D || lead;
         float *dst = lc < D ? qs + lc : (lc < 2 * D ? ks + (lc - D) : vs + G::perm(lc - 2 * D));
         // the row an ancestor code names; the conv-state rows come in as values, not captures: a
         // select between captured variables becomes a load through a select of their addresses,
         // which keeps them in scratch memory
-        // (the row is read unconditionally, node 0's for a conv-state code, so that no read sits
-        // under a branch and a batch's reads are all in flight together)
-        auto X = [raw, lc, to_f32](int code, float c0, float c1, float c2) -> float {
+        // (the row is read unconditionally, the launch's first node's for a code outside the launch,
+        // so that no read sits under a branch and a batch's reads are all in flight together; a node
+        // of an earlier launch is read from qkv, in launches after the first)
+        auto X = [raw, lc, gc, base, qkv_b, C, to_f32](int code, float c0, float c1, float c2) -> float {
             const float h = code == -1 ? c0 : (code == -2 ? c1 : c2);
-            const float r = to_f32(raw[max(code, 0) * NCH + lc]);
-            return code >= 0 ? r : h;
+            const float r = to_f32(raw[max(code - base, 0) * NCH + lc]);
+            if constexpr (LATER) {
+                const float e = to_f32(qkv_b[(size_t)min(max(code, 0), base - 1) * C + gc]);
+                return code >= base ? r : (code >= 0 ? e : h);
+            } else {
+                return code >= 0 ? r : h;
+            }
         };
         // Nodes in batches of CB = 16: one LDS read brings the batch's ancestor codes, lane 4 j + i
         // holding code i of node n0 + j, and they are taken from there lane by lane (readlane: the
@@ -358,12 +385,12 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         // (the compiler cannot move a read above a store to LDS it may alias).
         constexpr int CB = 16;
 #pragma unroll 1
-        for (int n0 = 0; n0 < T; n0 += CB) {
-            const int codes = anc[min(n0 + (lane >> 2), T - 1) * 4 + (lane & 3)];
+        for (int n0 = 0; n0 < NT; n0 += CB) {
+            const int codes = anc[min(n0 + (lane >> 2), NT - 1) * 4 + (lane & 3)];
             float x[CB][4];
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
-                const int n = min(n0 + j, T - 1);
+                const int n = min(n0 + j, NT - 1);
                 x[j][0] = X(__builtin_amdgcn_readlane(codes, 4 * j + 2), cs0, cs1, cs2);
                 x[j][1] = X(__builtin_amdgcn_readlane(codes, 4 * j + 1), cs0, cs1, cs2);
                 x[j][2] = X(__builtin_amdgcn_readlane(codes, 4 * j), cs0, cs1, cs2);
@@ -372,7 +399,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const int n = n0 + j;
-                if (n >= T) break;
+                if (n >= NT) break;
                 float y = conv4(wv, x[j][0], x[j][1], x[j][2], x[j][3]);
                 if constexpr (QKN) y = y * sigmoid_f(y);
                 dst[n * D] = y;
@@ -393,7 +420,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
 #pragma unroll
         for (int c = 0; c < G::CPL; ++c) S[i][c] = R0[i][c];
     const size_t hd = (size_t)D * D;
-    float *cap_base = a.cap_ssm + ((size_t)s * a.t_cap * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;
+    float *cap_base = a.cap_ssm + ((size_t)s * a.t_cap * a.n_vh + h) * hd + (size_t)row0 * D + cg * 4;  // node 0
     const size_t cap_nstride = (size_t)a.n_vh * hd;
     float SV[kTreeSaved][G::RPL][G::CPL];  // save slots (indexed by constants only: registers)
     auto copy_state = [](float (&dst)[G::RPL][G::CPL], const float (&src)[G::RPL][G::CPL]) {
@@ -409,6 +436,17 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         const int n = e & 0xff;
         const int rs = (e >> kSchedRestoreShift) & 3, sv = (e >> kSchedSaveShift) & 3;
         if (e & kSchedRestart) copy_state(S, R0);
+        if (LATER && (e & kSchedLoad)) {  // the parent's state, from the capture an earlier launch wrote
+            const float *src = cap_base + (size_t)anc[n * 4 + 3] * cap_nstride;
+#pragma unroll
+            for (int i = 0; i < G::RPL; ++i)
+#pragma unroll
+                for (int c4 = 0; c4 < G::NC4; ++c4) {
+                    const f4 v = *reinterpret_cast<const f4 *>(src + (size_t)(4 * i) * D + 64 * c4);
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) S[i][4 * c4 + e4] = v[e4];
+                }
+        }
 #pragma unroll
         for (int j = 0; j < kTreeSaved; ++j)
             if (rs == j + 1) copy_state(S, SV[j]);
@@ -421,7 +459,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
 #pragma unroll
                 for (int i = 0; i < G::RPL; ++i) od[i] = o[i];
             }
-            float *cp = cap_base + (size_t)n * cap_nstride;
+            float *cp = cap_base + (size_t)(base + n) * cap_nstride;
 #pragma unroll
             for (int i = 0; i < G::RPL; ++i)
 #pragma unroll
@@ -441,7 +479,7 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
 #pragma unroll
     for (int k = 0; k < NPG; ++k) {
         const int n = grp + k * NGRP;
-        if (n >= T) break;  // uniform over the 16-lane group
+        if (n >= NT) break;  // uniform over the 16-lane group
         const float *osrc = os + n * D;
         float ov[EPL];
         float ss = 0.f;
@@ -452,33 +490,46 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         }
         ss = row16_sum(ss);
         const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-        const size_t base = (((size_t)b * T + n) * a.n_vh + h) * D + cg * EPL;
+        const size_t ob = (((size_t)b * T + base + n) * a.n_vh + h) * D + cg * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const float zz = word_f32(zr[k][e]);
             const float y = ov[e] * inv * nwr[e] * (zz * sigmoid_f(zz));
             if constexpr (OUT_BF16)
-                static_cast<uint16_t *>(a.out)[base + e] = f32_to_bf16(y);
+                static_cast<uint16_t *>(a.out)[ob + e] = f32_to_bf16(y);
             else
-                static_cast<float *>(a.out)[base + e] = y;
+                static_cast<float *>(a.out)[ob + e] = y;
         }
     }
 }
 
 size_t verify_tree_lds_bytes(int d, int T, bool act_bf16)
 {
-    if (T < 1 || T > kTreeMaxNodes) return (size_t)-1;
+    if (T < 1 || T > kTreeMaxTotal) return (size_t)-1;
+    T = T < kTreeMaxNodes ? T : kTreeMaxNodes;  // one launch's nodes
     if (d == 128) return act_bf16 ? TreeLds<128, uint16_t>::total(T) : TreeLds<128, float>::total(T);
     return act_bf16 ? TreeLds<64, uint16_t>::total(T) : TreeLds<64, float>::total(T);
 }
 
+// Consecutive launches over consecutive ranges of at most kTreeMaxNodes nodes, on one stream: a
+// launch reads the captures of earlier ranges only after their launches have finished.
 template <int D, bool AB, bool OB, bool QKN>
-static hipError_t launch_tree_t(const VerifyArgs &a, hipStream_t stream)
+static hipError_t launch_tree_t(const VerifyArgs &a0, hipStream_t stream)
 {
-    const size_t lds = verify_tree_lds_bytes(D, a.T, AB);
-    hipLaunchKernelGGL((verify_tree_kernel<D, AB, OB, QKN>), dim3(a.n_batch * a.n_vh), dim3(TreeWaves<D>::value * 64),
-                       lds, stream, a);
-    return hipGetLastError();
+    for (int t0 = 0; t0 < a0.T; t0 += kTreeMaxNodes) {
+        VerifyArgs a = a0;
+        a.t0 = t0;
+        a.nt = a0.T - t0 < kTreeMaxNodes ? a0.T - t0 : kTreeMaxNodes;
+        const size_t lds = verify_tree_lds_bytes(D, a.nt, AB);
+        if (t0 == 0)
+            hipLaunchKernelGGL((verify_tree_kernel<D, AB, OB, QKN, false>), dim3(a.n_batch * a.n_vh),
+                               dim3(TreeWaves<D>::value * 64), lds, stream, a);
+        else
+            hipLaunchKernelGGL((verify_tree_kernel<D, AB, OB, QKN, true>), dim3(a.n_batch * a.n_vh),
+                               dim3(TreeWaves<D>::value * 64), lds, stream, a);
+        if (hipError_t e = hipGetLastError()) return e;
+    }
+    return hipSuccess;
 }
 template <int D, bool AB, bool OB>
 static hipError_t launch_tree_q(const VerifyArgs &a, const LaunchCfg &c, hipStream_t s)

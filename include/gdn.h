@@ -166,7 +166,10 @@ int gdn_verify_resume(const gdn_dims *dims, float *state, float *conv_state, con
  * (3-row conv state after node i; capture->mode must be GDN_TREE, t_cap >= n_tok).  state and
  * conv_state are NOT advanced: the caller commits a node with gdn_rollback.  Nodes with a
  * malformed parent are treated as children of the committed state unless GDN_F_CHECK_INDICES
- * is set (then GDN_ERR_RANGE).
+ * is set (then GDN_ERR_RANGE).  n_tok is 1 .. 1024 (more: GDN_ERR_SHAPE).  Trees of more than 64
+ * nodes run as consecutive launches of 64 nodes on `stream`; a node whose parent lies in an
+ * earlier launch starts from that parent's capture, so the capture must not be written by
+ * anything else while the call's launches run.
  */
 int gdn_verify_tree(const gdn_dims *dims, const float *state, const float *conv_state,
                     const void *qkv, const void *z, const void *alpha, const void *beta,

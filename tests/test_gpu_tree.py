@@ -59,6 +59,12 @@ TREE_CASES = {
     "bf16_d128_64_nodes": (W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=1), 8, 0),
     "deep_comb": (W.shape_with(W.TINY_VERIFY, n_tok=30, act_dtype=W.BF16, out_dtype=W.BF16), 64, 0),
     "qk_norm_flag": (W.shape_with(W.TREE_VERIFY, n_pool=1, n_batch=1, n_tok=20), 5, 1),
+    # more nodes than one launch holds (64): consecutive launches, nodes whose parent is in an
+    # earlier launch start from its capture, conv windows reach back into earlier launches
+    "bf16_d128_root_plus_64": (W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=2, n_tok=65), 8, 0),
+    "bf16_d128_128_nodes": (W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=2, n_tok=128), 8, 0),
+    "fp32_d64_200_nodes_depth12": (W.shape_with(W.TINY_VERIFY, n_tok=200, n_pool=2, n_batch=2), 12, 0),
+    "bf16_d64_deep_comb_150": (W.shape_with(W.TINY_VERIFY, n_tok=150, act_dtype=W.BF16, out_dtype=W.BF16), 150, 0),
 }
 
 
@@ -113,8 +119,11 @@ def test_tree_full_size_every_unit():
     assert worst_s <= tol and worst_o <= tol
 
 
-def test_chain_shaped_tree_equals_chain_verify_bitwise():
-    shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=2, n_batch=2, n_tok=16)
+@pytest.mark.parametrize("n_tok", [16, 100])
+def test_chain_shaped_tree_equals_chain_verify_bitwise(n_tok):
+    """A chain-shaped tree gives the chain verify's captures and outputs bit for bit; at 100 nodes
+    the tree runs as two launches and the chain as seven, each carrying its state over."""
+    shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=2, n_batch=2, n_tok=n_tok)
     device, gdn = _mods()
     inp = W.make_inputs(shape, 3)
     inp["parent"] = np.stack([W.chain_parents(shape.n_tok)] * shape.n_batch)
@@ -134,10 +143,11 @@ def test_chain_shaped_tree_equals_chain_verify_bitwise():
             assert torch.equal(t["cap_conv"][s, i], c["cap_conv"][s, i + 1:i + 4])
 
 
-def test_tree_rollback_equals_chain_along_accepted_path():
+@pytest.mark.parametrize("n_tok", [48, 130])
+def test_tree_rollback_equals_chain_along_accepted_path(n_tok):
     """Commit an accepted node with gdn_rollback (tree mode): state and conv state equal a chain
-    verify of the node's root path, bit for bit."""
-    shape = W.shape_with(W.TREE_VERIFY, n_pool=3, n_batch=2, n_tok=48)
+    verify of the node's root path, bit for bit (at 130 nodes, three launches)."""
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=3, n_batch=2, n_tok=n_tok)
     device, gdn = _mods()
     inp = W.make_tree_inputs(shape, 7)
     t = _tree_upload(shape, inp)
@@ -187,7 +197,7 @@ def test_tree_multiple_roots_and_malformed_parents():
 
 
 def test_tree_too_many_nodes_rejected():
-    shape = W.shape_with(W.TREE_VERIFY, n_pool=1, n_batch=1, n_tok=65)
+    shape = W.shape_with(W.TINY_VERIFY, n_pool=1, n_batch=1, n_tok=1025)
     device, gdn = _mods()
     inp = W.make_tree_inputs(shape, 1)
     d = _tree_upload(shape, inp)
@@ -212,6 +222,21 @@ def test_tree_bushy_shapes_beyond_the_save_slots():
     forest = np.concatenate([_kary_parents(31, 2), _kary_parents(32, 2) + np.where(
         _kary_parents(32, 2) >= 0, 31, 0)]).astype(np.int32)
     inp["parent"] = np.stack([binary, ternary, forest])
+    d = _tree_upload(shape, inp)
+    device.verify_tree(d)
+    torch.cuda.synchronize()
+    _check_tree(shape, inp, d)
+
+
+def test_tree_bushy_shapes_over_two_launches():
+    """A complete binary tree of 127 nodes and a ternary one of 121: their second launch holds
+    mostly nodes whose parents are in the first (started from the capture), with branch points
+    and re-run paths inside each launch."""
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=2, n_tok=127)
+    device, _ = _mods()
+    inp = W.make_tree_inputs(shape, 11)
+    ternary = np.concatenate([_kary_parents(121, 3), np.arange(120, 126, dtype=np.int32)])
+    inp["parent"] = np.stack([_kary_parents(127, 2), ternary])
     d = _tree_upload(shape, inp)
     device.verify_tree(d)
     torch.cuda.synchronize()
