@@ -243,6 +243,70 @@ def components(args) -> dict:
     return out
 
 
+COMPONENTS = ("prefill", "tree", "linear", "single_slot")
+
+
+def component_only(name: str, steps: int, warmup: int) -> dict:
+    """One secondary workload alone, for a profiler run: warmup + steps launches of its kernels,
+    then the same count of the snapshot copy of 64 slots (a plain copy of known size, which
+    calibrates byte counters), with the average launch time of each."""
+    import torch
+
+    from gated_deltanet_linear_verify_amd import bytemodel, device, gdn
+    from gated_deltanet_linear_verify_amd import workloads as W
+
+    n = warmup + steps
+    res = {"component": name, "launches": n}
+    if name == "prefill":
+        s = W.CHUNKED_PREFILL
+        d = device.upload(s, W.make_inputs(s, 0), capture=False)
+        res["workload"] = "1 slot x 8192 tokens, 16/32 heads, d=128, bf16, chunk 64"
+        res["us"] = time_launches(lambda: device.prefill(d), steps, warmup)
+        res["algorithmic_flops"] = bytemodel.prefill_flops(s)
+        res["algorithmic_bytes"] = bytemodel.prefill_bytes(s)
+    elif name == "tree":
+        s = W.TREE_VERIFY
+        d = device.upload(s, W.make_tree_inputs(s, 0), mode=gdn.GDN_TREE, fill_capture=0.0)
+        res["workload"] = "8 slots x 64-node trees, 16/32 heads, d=128, bf16"
+        res["us"] = time_launches(lambda: device.verify_tree(d), steps, warmup)
+        res["algorithmic_bytes"] = bytemodel.tree_bytes(s)
+    elif name == "linear":
+        s = W.MULTI_SLOT_VERIFY
+        d = device.upload_block(s, W.make_block_inputs(s, W.HIDDEN, seed=3))
+        M, C, Z, Hv = s.n_batch * s.n_tok, s.conv_channels, s.n_vh * s.d_v, s.n_vh
+        n_in = C + Z + 2 * Hv
+        segs = [(0, C, d["qkv"], C, 0), (C, C + Z, d["z"], Z, 0),
+                (C + Z, C + Z + Hv, d["beta"], Hv, 1), (C + Z + Hv, n_in, d["alpha"], Hv, 0)]
+        res["workload"] = f"64 slots x 16 tokens: {M} x {W.HIDDEN} -> {n_in} (in), {M} x {Z} -> {W.HIDDEN} (out), bf16"
+        res["us_in_proj"] = time_launches(lambda: gdn.gdn_linear(d["x"], d["w_in"], M, n_in, W.HIDDEN, segs),
+                                          steps, warmup)
+        res["us_out_proj"] = time_launches(lambda: gdn.gdn_linear(d["out"], d["w_out"], M, W.HIDDEN, Z,
+                                                                  [(0, W.HIDDEN, d["y"], W.HIDDEN, 0)]), steps, warmup)
+        res["in_proj_flops"] = 2.0 * M * n_in * W.HIDDEN
+        res["out_proj_flops"] = 2.0 * M * W.HIDDEN * Z
+    elif name == "single_slot":
+        s = W.SINGLE_SLOT_VERIFY
+        d = device.upload(s, W.make_inputs(s, 0), fill_capture=0.0)
+        res["workload"] = "1 slot x 16 tokens, 16/32 heads, d=128, bf16"
+        res["us"] = time_launches(lambda: device.verify(d), steps, warmup)
+        res["algorithmic_bytes"] = bytemodel.verify_bytes(s)
+    del d
+    torch.cuda.empty_cache()
+    # calibration: snapshot of all 64 slots of the multi-slot pool, 2 x 140,509,184 B moved
+    s = W.MULTI_SLOT_VERIFY
+    dims = gdn.make_dims(s)
+    st = torch.zeros((s.n_pool, s.n_vh, s.d_v, s.d_k), dtype=torch.float32, device="cuda")
+    cs = torch.zeros((s.n_pool, 3, s.conv_channels), dtype=torch.float32, device="cuda")
+    st2, cs2 = torch.empty_like(st), torch.empty_like(cs)
+    slots = torch.arange(s.n_pool, dtype=torch.int32, device="cuda")
+    res["calibration"] = {"kernel": "slot_copy_kernel (gdn_snapshot of 64 slots)",
+                          "read_bytes": bytemodel.snapshot_bytes(s, s.n_pool) // 2 + 4 * s.n_pool,
+                          "write_bytes": bytemodel.snapshot_bytes(s, s.n_pool) // 2,
+                          "us": time_launches(lambda: gdn.gdn_snapshot(dims, st, cs, st2, cs2, slots, s.n_pool),
+                                              steps, warmup)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +316,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the secondary timings (tree verify, single-slot verify, rollback)")
+    ap.add_argument("--component", choices=COMPONENTS,
+                    help="profiling aid: run only this secondary workload (--warmup + --steps launches) "
+                         "and a calibration copy, and print their launch times instead of the step's line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU code (got --gpus "
@@ -269,6 +336,9 @@ def main() -> int:
         return 2
     gdn.lib()
     torch.cuda.set_device(0)
+    if args.component:
+        print(json.dumps(component_only(args.component, args.steps, args.warmup)), flush=True)
+        return 0
     shape = W.MULTI_SLOT_VERIFY
     B, T = shape.n_batch, shape.n_tok
 

@@ -39,7 +39,13 @@ namespace gdn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChunk = 64;  // tokens per chunk
-constexpr int kSR = 32;     // value rows per scan workgroup (two 16-row MFMA tiles)
+// Value rows per scan workgroup (16-row MFMA tiles).  The scan's step is bound by moving each
+// chunk's q, k, T and P images into the workgroup, the same bytes whatever its share of rows, so
+// the rows are spread as thin as keeps the chip busy: 16 rows give 8 workgroups per d=128 head,
+// 256 for 32 heads, one per CU (32 rows: 128 workgroups, 7% slower over the whole prefill).
+constexpr int kSR = 16;
+constexpr int kRT = kSR / 16;  // row tiles per scan workgroup
+static_assert(kRT == 1 || kRT == 2, "one or two 16-row tiles");
 constexpr int kPThreads = 256;
 constexpr int kCP = kChunk + 4;  // padded row stride of the chunk x chunk matrices
 
@@ -659,11 +665,11 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // ============================== kernel 2: the chunk chain ==============================
-// Per chunk, for this workgroup's kSR = 32 value rows (S block 32 x d, rows i, key columns j):
+// Per chunk, for this workgroup's kSR value rows (S block kSR x d, rows i, key columns j):
 //   A: Y^T = beta (V^T - (S K^T) diag(gamma))     V convolved here from the raw activations
 //   B: U^T = Y^T T^T
 //   C: O   = diag(gamma) Q S^T + P U ;  S' = gamma_C S + U^T diag(dec) K
-// Compute wave w owns tokens 16 w .. 16 w + 15 of A, B and the readout, for both 16-row tiles of the
+// Compute wave w owns tokens 16 w .. 16 w + 15 of A, B and the readout, for every 16-row tile of the
 // block, so every q, k, T and P element is read from LDS once per chunk; its S' share is key
 // columns 16 (2 w) .. 16 (2 w) + 31 (d = 128).  Each wave reads the whole S block into registers as
 // MFMA operand fragments at the start of a chunk and uses it in A for both products that need it,
@@ -814,12 +820,13 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
     // consecutive columns of one row), the conv taps and the conv-state rows of its v channels
     float *st = a.state + ((size_t)a.slot * a.n_vh + h) * D * D + (size_t)blk * kSR * D;
     float *Dp = reinterpret_cast<float *>(smem + L::dp);
-    f4 sreg[2][SCT];
-    f4 wv[2];
-    float hist[2][3];
+    constexpr int RT = kRT;
+    f4 sreg[RT][SCT];
+    f4 wv[RT];
+    float hist[RT][3];
     auto s_at = [&](int rt, int q2) { return (size_t)(16 * rt + li) * D + 16 * (SCT * wave + q2) + 4 * lg; };
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
         for (int q2 = 0; q2 < SCT; ++q2) sreg[rt][q2] = *reinterpret_cast<const f4 *>(st + s_at(rt, q2));
         const int vc = vch0 + 16 * rt + li;
@@ -828,7 +835,7 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
         for (int m = 0; m < 3; ++m) hist[rt][m] = a.conv_state[((size_t)a.slot * 3 + m) * Cc + vc];
     }
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int q2 = 0; q2 < SCT; ++q2) MS::put4(Sx, 16 * rt + li, 16 * (SCT * wave + q2) + 4 * lg, sreg[rt][q2]);
     auto raw_v = [&](int row, int ch) -> float {  // window row of the chunk, block channel
@@ -850,15 +857,21 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
         // ---- A: (K S^T)[t][i] for tokens t4 + r, rows 16 rt + li, and the readout's S Q^T [i][t]
         // for rows 16 rt + 4 lg + r, token tr; then Y^T[i][t] = beta_t (v_t[i] - gamma_t (K S^T)[t][i])
         Frag<F32> kf[SCT][2];  // K columns of this wave's S' tiles (C's A operand)
-        f4 acc4[4] = {};       // K S^T of tiles 0, 1, then S Q^T of tiles 0, 1
+        f4 acc4[2 * RT] = {};  // K S^T of the row tiles, then S Q^T of the row tiles
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const Frag<F32> kr = MK::load(Kc, tr, 32 * kk + 8 * lg);
             const Frag<F32> qr = MK::load(Q, tr, 32 * kk + 8 * lg);
-            const Frag<F32> s0 = MS::load(Sx, li, 32 * kk + 8 * lg);
-            const Frag<F32> s1 = MS::load(Sx, 16 + li, 32 * kk + 8 * lg);
-            const Frag<F32> fa[4] = {kr, kr, s0, s1}, fb[4] = {s0, s1, qr, qr};
-            mma_n<F32, 4>(fa, fb, acc4);
+            Frag<F32> fa[2 * RT], fb[2 * RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const Frag<F32> sf = MS::load(Sx, 16 * rt + li, 32 * kk + 8 * lg);
+                fa[rt] = kr;
+                fb[rt] = sf;
+                fa[RT + rt] = sf;
+                fb[RT + rt] = qr;
+            }
+            mma_n<F32, 2 * RT>(fa, fb, acc4);
         }
 #pragma unroll
         for (int q2 = 0; q2 < SCT; ++q2) {
@@ -878,7 +891,7 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
             const f4 b4 = *reinterpret_cast<const f4 *>(bet + t4);
             const bool from_state = c == 0 && t4 == 0;  // window rows 0..2 precede the call
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
+            for (int rt = 0; rt < RT; ++rt) {
                 const int ch = 16 * rt + li;
                 float xr[7];  // window rows t4 .. t4 + 6 of channel ch, every read issued before any use
 #pragma unroll
@@ -898,16 +911,21 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
         lds_barrier();  // Y^T is in LDS; q, k and the raw v rows are consumed
         // ---- B: U[t][i] = sum_s T[t][s] Y[s][i]; U^T (and U^T diag(dec)) into LDS in operand form
         {
-            f4 part[4] = {};  // tile 0 and 1 over tokens 0..31, then over 32..63
+            f4 part[2 * RT] = {};  // the row tiles over tokens 0..31, then over 32..63
             const Frag<F32> t0 = MT::load(Tm, tr, 8 * lg), t1 = MT::load(Tm, tr, 32 + 8 * lg);
-            const Frag<F32> fa[4] = {t0, t0, t1, t1};
-            const Frag<F32> fb[4] = {MY::load(Yp, li, 8 * lg), MY::load(Yp, 16 + li, 8 * lg),
-                                     MY::load(Yp, li, 32 + 8 * lg), MY::load(Yp, 16 + li, 32 + 8 * lg)};
-            mma_n<F32, 4>(fa, fb, part);
+            Frag<F32> fa[2 * RT], fb[2 * RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                fa[rt] = t0;
+                fa[RT + rt] = t1;
+                fb[rt] = MY::load(Yp, 16 * rt + li, 8 * lg);
+                fb[RT + rt] = MY::load(Yp, 16 * rt + li, 32 + 8 * lg);
+            }
+            mma_n<F32, 2 * RT>(fa, fb, part);
             const f4 d4 = *reinterpret_cast<const f4 *>(dec + t4);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const f4 u = part[rt] + part[2 + rt];
+            for (int rt = 0; rt < RT; ++rt) {
+                const f4 u = part[rt] + part[RT + rt];
                 MY::put4(Up, 16 * rt + li, t4, u);
                 if constexpr (!F32) MY::put4(Dp, 16 * rt + li, t4, u * d4);
             }
@@ -918,12 +936,12 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
         {
             const float gC = gam[C - 1];
             const float gt = gam[tr];
-            Frag<F32> uf[2][2], udf[2][2], pr[2];  // [tile][token half], [token half]
+            Frag<F32> uf[RT][2], udf[RT][2], pr[2];  // [tile][token half], [token half]
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 pr[h2] = MT::load(Pm, tr, 32 * h2 + 8 * lg);
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < RT; ++rt) {
                     uf[rt][h2] = MY::load(Up, 16 * rt + li, 32 * h2 + 8 * lg);
                     if constexpr (F32) {
 #pragma unroll
@@ -933,46 +951,49 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
                     }
                 }
             }
-            // accumulators: the readout of tiles 0, 1, then S'^T of (tile, column tile) 00 01 10 11
-            f4 acc6[2 + 2 * SCT];
-            acc6[0] = acc4[2] * gt;
-            acc6[1] = acc4[3] * gt;
+            // accumulators: the readout of the row tiles, then S'^T of (row tile, column tile)
+            constexpr int NA = RT + RT * SCT;
+            f4 acc6[NA];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt) acc6[rt] = acc4[RT + rt] * gt;
 #pragma unroll
-                for (int q2 = 0; q2 < SCT; ++q2) acc6[2 + rt * SCT + q2] = sreg[rt][q2] * gC;
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int q2 = 0; q2 < SCT; ++q2) acc6[RT + rt * SCT + q2] = sreg[rt][q2] * gC;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                Frag<F32> fa[2 + 2 * SCT], fb[2 + 2 * SCT];
-                fa[0] = uf[0][h2];
-                fa[1] = uf[1][h2];
-                fb[0] = fb[1] = pr[h2];
+                Frag<F32> fa[NA], fb[NA];
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < RT; ++rt) {
+                    fa[rt] = uf[rt][h2];
+                    fb[rt] = pr[h2];
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int q2 = 0; q2 < SCT; ++q2) {
-                        fa[2 + rt * SCT + q2] = kf[q2][h2];
-                        fb[2 + rt * SCT + q2] = udf[rt][h2];
+                        fa[RT + rt * SCT + q2] = kf[q2][h2];
+                        fb[RT + rt * SCT + q2] = udf[rt][h2];
                     }
-                mma_n<F32, 2 + 2 * SCT>(fa, fb, acc6);
+                mma_n<F32, NA>(fa, fb, acc6);
             }
             // the readout: rows 16 rt + 4 lg .. + 3 of token tr, four consecutive floats (whole
             // chunks fit the readout)
             float *orow = a.ws + w.o + ((size_t)(c * C + tr) * a.n_vh + h) * D + blk * kSR + 4 * lg;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) *reinterpret_cast<f4 *>(orow + 16 * rt) = acc6[rt];
+            for (int rt = 0; rt < RT; ++rt) *reinterpret_cast<f4 *>(orow + 16 * rt) = acc6[rt];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int q2 = 0; q2 < SCT; ++q2) {
-                    sreg[rt][q2] = acc6[2 + rt * SCT + q2];
+                    sreg[rt][q2] = acc6[RT + rt * SCT + q2];
                     MS::put4(Sx, 16 * rt + li, 16 * (SCT * wave + q2) + 4 * lg, sreg[rt][q2]);
                 }
         }
     }
     // ---- the state block after the last token
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int q2 = 0; q2 < SCT; ++q2) *reinterpret_cast<f4 *>(st + s_at(rt, q2)) = sreg[rt][q2];
 }
