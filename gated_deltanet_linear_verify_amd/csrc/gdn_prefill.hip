@@ -302,15 +302,39 @@ struct Mat {
     }
 };
 
+// A 64 x 64 lower-triangular operand (T or P) without its upper-right 32 x 32 block, which is all
+// zero: block L = rows 0..63 x columns 0..31, then block R = rows 32..63 x columns 32..63, each a
+// Mat image.  12 KiB instead of 16 per image, in the workspace and in LDS.
+template <bool F32>
+struct Tri {
+    using ML = Mat<F32, kChunk, kChunk / 2>;
+    using MR = Mat<F32, kChunk / 2, kChunk / 2>;
+    static constexpr int floats = ML::floats + MR::floats;
+    // row r, columns c0 .. c0 + 7 (c0 a multiple of 8, not in the zero block)
+    __device__ static Frag<F32> load(const float *m, int r, int c0)
+    {
+        return c0 < kChunk / 2 ? ML::load(m, r, c0) : MR::load(m + ML::floats, r - kChunk / 2, c0 - kChunk / 2);
+    }
+    // row r, columns c0 .. c0 + 7; nothing is stored for the zero block
+    __device__ static void put8(float *m, int r, int c0, const float (&x)[8])
+    {
+        if (c0 < kChunk / 2)
+            ML::put8(m, r, c0, x);
+        else if (r >= kChunk / 2)
+            MR::put8(m + ML::floats, r - kChunk / 2, c0 - kChunk / 2, x);
+    }
+};
+
 // Workspace (floats), nc = number of chunks:
 //   o  [nc * 64][H_v][d]         fp32 readout before the norm (whole chunks: the tail is scratch)
 //   qk [nc][H_k][2][64 * d]      conv'd q then k of the chunk, per key head
 // (q, k, T and P as Mat images: fp32, or split into bf16 hi / lo planes for bf16 activations)
-//   t  [nc][H_v][64 * 64]        T = (I + A)^-1
-//   p  [nc][H_v][64 * 64]        P
+//   t  [nc][H_v][3072]           T = (I + A)^-1   (Tri images: the zero upper-right block left out)
+//   p  [nc][H_v][3072]           P
 //   g  [nc][H_v][256]            gamma | beta | exp(Gamma_C - Gamma) | 0, 64 each
 // (the scan convolves v itself from the raw activations)
 constexpr int kGateRec = 4 * kChunk;
+constexpr int kTriFloats = kChunk * kChunk / 2 + kChunk * kChunk / 4;  // a Tri image
 struct PrefillWs {
     size_t o, qk, t, p, g, total;
 };
@@ -321,8 +345,8 @@ __host__ __device__ inline PrefillWs prefill_ws(int d, int n_kh, int n_vh, int T
     w.o = 0;
     w.qk = w.o + nc * kChunk * n_vh * d;
     w.t = w.qk + nc * n_kh * 2 * kChunk * d;
-    w.p = w.t + nc * n_vh * kChunk * kChunk;
-    w.g = w.p + nc * n_vh * kChunk * kChunk;
+    w.p = w.t + nc * n_vh * kTriFloats;
+    w.g = w.p + nc * n_vh * kTriFloats;
     w.total = w.g + nc * n_vh * kGateRec;
     return w;
 }
@@ -347,8 +371,8 @@ static_assert(2 * PrepLds<128>::total <= 160 * 1024, "two d=128 prep workgroups 
 template <int D, bool ACT_BF16>
 struct ScanLds {
     static constexpr int C = kChunk;
-    static constexpr size_t kimg = sizeof(float) * C * D;  // a q or k image
-    static constexpr size_t timg = sizeof(float) * C * C;  // a T or P image
+    static constexpr size_t kimg = sizeof(float) * C * D;     // a q or k image
+    static constexpr size_t timg = sizeof(float) * kTriFloats;  // a T or P image
     // raw v rows of the block's kSR channels, window rows 0 .. C + 2 (token t0 - 3 + row), moved
     // 1 KiB (one 64-lane 16-byte transfer) at a time
     static constexpr int vrow = kSR * (ACT_BF16 ? 2 : 4);  // bytes per row
@@ -357,8 +381,8 @@ struct ScanLds {
     static constexpr size_t vimg = 1024 * vdmas;
     static constexpr size_t gimg = sizeof(float) * kGateRec;
     static constexpr size_t kb = 0;                          // k image of the chunk in progress
-    static constexpr size_t q = kb + kimg;                   // q image
-    static constexpr size_t tm = q + kimg;                   // T image
+    static constexpr size_t q = kb + kimg;                   // [2] q images (chunk parity)
+    static constexpr size_t tm = q + 2 * kimg;               // T image
     static constexpr size_t pm = tm + timg;                  // [2] P images (chunk parity)
     static constexpr size_t vb = pm + 2 * timg;              // raw v rows
     static constexpr size_t gb = vb + vimg;                  // [2] gate records (chunk parity)
@@ -639,12 +663,13 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         lds_barrier();
 
-        // ---- T, P and the gates for the scan (T and P as Mat images)
+        // ---- T, P and the gates for the scan (T and P as Tri images)
         {
-            using MT = Mat<F32, C, C>;
+            using MT = Tri<F32>;
+            static_assert(MT::floats == kTriFloats, "the workspace holds Tri images");
             const size_t ch = (size_t)c * a.n_vh + h;
-            float *tdst = a.ws + w.t + ch * C * C;
-            float *pdst = a.ws + w.p + ch * C * C;
+            float *tdst = a.ws + w.t + ch * kTriFloats;
+            float *pdst = a.ws + w.p + ch * kTriFloats;
             for (int g = tid; g < C * C / 8; g += kPThreads) {
                 const int r = g / (C / 8), c0 = (g % (C / 8)) * 8;
                 float x[8];
@@ -694,7 +719,7 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
     constexpr int NB = D / kSR;   // row blocks per value head
     constexpr int KK = D / 32;    // 32-deep steps over the key dimension
     using MK = Mat<F32, C, D>;    // q and k images
-    using MT = Mat<F32, C, C>;    // T and P images
+    using MT = Tri<F32>;          // T and P images
     using MS = Mat<F32, kSR, D>;  // S block
     using MY = Mat<F32, kSR, C>;  // Y^T
     constexpr int SCT = D / 16 / kScanCompute;     // S' column tiles per compute wave
@@ -741,15 +766,15 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
     auto qk_img = [&](int cc, int which) { return a.ws + w.qk + (((size_t)cc * a.n_kh + hk) * 2 + which) * C * D; };
     auto chunk_rec = [&](int cc) { return (size_t)cc * a.n_vh + h; };
     using img16 = std::integral_constant<int, C * D / 4>;  // a q or k image in 16-byte pieces
-    using mat16 = std::integral_constant<int, C * C / 4>;  // a T or P image
-    auto issue_k = [&](int cc) { dma(img16{}, qk_img(cc, 1), Kc); };
     using half16 = std::integral_constant<int, C * D / 8>;
-    auto issue_q = [&](int cc, int half) {  // one half of the q image
-        dma(half16{}, qk_img(cc, 0) + half * (C * D / 2), Q + half * (C * D / 2));
+    using tri16 = std::integral_constant<int, kTriFloats / 4>;  // a T or P image
+    auto issue_k = [&](int cc, int half) {  // one half of the k image
+        dma(half16{}, qk_img(cc, 1) + half * (C * D / 2), Kc + half * (C * D / 2));
     };
-    auto issue_t = [&](int cc) { dma(mat16{}, a.ws + w.t + chunk_rec(cc) * C * C, Tm); };
+    auto issue_q = [&](int cc) { dma(img16{}, qk_img(cc, 0), Q + (cc & 1) * C * D); };
+    auto issue_t = [&](int cc) { dma(tri16{}, a.ws + w.t + chunk_rec(cc) * kTriFloats, Tm); };
     auto issue_pg = [&](int cc) {  // P and the gate record of chunk cc (one transfer per producer each)
-        dma(mat16{}, a.ws + w.p + chunk_rec(cc) * C * C, Pb + (cc & 1) * C * C);
+        dma(tri16{}, a.ws + w.p + chunk_rec(cc) * kTriFloats, Pb + (cc & 1) * kTriFloats);
         if (lane < kGateRec / 4 / kProducers) {
             const int i0 = pw * (kGateRec / 4 / kProducers);
             lds_dma16(a.ws + w.g + chunk_rec(cc) * kGateRec + 4 * (i0 + lane), Gb + (cc & 1) * kGateRec + 4 * i0);
@@ -769,25 +794,28 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
             }
         }
     };
-    // transfers per producer wave: T, P (uniform), and one gate transfer each
-    constexpr int NT = C * C / 4 / (64 * kProducers);
-    static_assert(NT * 64 * kProducers == C * C / 4 && NT + NT + 1 < 64, "T and P split evenly over the producers");
+    // transfers per producer wave: T or P, a q image (uniform), and one gate transfer each
+    constexpr int NT = kTriFloats / 4 / (64 * kProducers);
+    constexpr int NQ = C * D / 4 / (64 * kProducers);
+    static_assert(NT * 64 * kProducers == kTriFloats / 4 && NT + NQ + 1 < 64, "T and P split evenly over the producers");
     static_assert(kGateRec / 4 / kProducers <= 64, "a gate record is one partial transfer per producer");
 
     // The producers and the compute waves run separate loops with the same three barriers per
     // chunk.  (In one shared loop the compiler would have to assume a transfer into LDS in flight
     // on the compute waves' path too, and make them wait for all their own vector-memory operations
     // before touching LDS.)
-    // A buffer is refilled as soon as the phase that reads it is done: P and the gates (double
-    // buffered) of c + 1 during A of c; k, v and half of q of c + 1 during B (A has read k, v and q
-    // of c); the other half of q and T of c + 1 during C.  T is issued last and needed only by B, so
-    // the chunk start waits for everything else and the barrier after A for T.
+    // A buffer is refilled as soon as the phase that reads it is done, and the transfers of c + 1
+    // are spread over the three phases of c in proportion to their length, so that no producer
+    // reaches a barrier after the compute waves: P, the gates and q (double buffered) during A;
+    // half of k and v during B (A has read k and v of c); the other half of k and T during C.  T is
+    // issued last and needed only by B, so the chunk start waits for everything else and the
+    // barrier after A for T.
     if (producer) {
         issue_pg(0);
-        issue_k(0);
+        issue_q(0);
+        issue_k(0, 0);
         issue_v(0);
-        issue_q(0, 0);
-        issue_q(0, 1);
+        issue_k(0, 1);
         issue_t(0);
 #pragma unroll 1
         for (int c = 0; c < nchunks; ++c) {
@@ -795,19 +823,19 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
             lds_barrier();                                // chunk start
             if (c + 1 < nchunks) {
                 issue_pg(c + 1);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(NT + 1));  // T of c (P, gates of c + 1 may travel)
+                issue_q(c + 1);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(NT + 1 + NQ));  // T of c (P, gates, q of c + 1 may travel)
             } else {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             lds_barrier();  // A done: q, k and v of c are consumed; T of c has landed
             if (c + 1 < nchunks) {
-                issue_k(c + 1);
+                issue_k(c + 1, 0);
                 issue_v(c + 1);
-                issue_q(c + 1, 0);
             }
             lds_barrier();  // B done: T of c is consumed
             if (c + 1 < nchunks) {
-                issue_q(c + 1, 1);
+                issue_k(c + 1, 1);
                 issue_t(c + 1);
             }
         }
@@ -852,7 +880,8 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
         const float *gam = Gb + (c & 1) * kGateRec;
         const float *bet = gam + C;
         const float *dec = bet + C;
-        const float *Pm = Pb + (c & 1) * C * C;
+        const float *Pm = Pb + (c & 1) * kTriFloats;
+        const float *Qc = Q + (c & 1) * C * D;
         lds_barrier();  // chunk start: the operands of c and S are in LDS
         // ---- A: (K S^T)[t][i] for tokens t4 + r, rows 16 rt + li, and the readout's S Q^T [i][t]
         // for rows 16 rt + 4 lg + r, token tr; then Y^T[i][t] = beta_t (v_t[i] - gamma_t (K S^T)[t][i])
@@ -861,7 +890,7 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const Frag<F32> kr = MK::load(Kc, tr, 32 * kk + 8 * lg);
-            const Frag<F32> qr = MK::load(Q, tr, 32 * kk + 8 * lg);
+            const Frag<F32> qr = MK::load(Qc, tr, 32 * kk + 8 * lg);
             Frag<F32> fa[2 * RT], fb[2 * RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -912,7 +941,8 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
         // ---- B: U[t][i] = sum_s T[t][s] Y[s][i]; U^T (and U^T diag(dec)) into LDS in operand form
         {
             f4 part[2 * RT] = {};  // the row tiles over tokens 0..31, then over 32..63
-            const Frag<F32> t0 = MT::load(Tm, tr, 8 * lg), t1 = MT::load(Tm, tr, 32 + 8 * lg);
+            // tokens 0..31 (waves 0, 1) have no T entries in columns 32..63
+            const Frag<F32> t0 = MT::load(Tm, tr, 8 * lg), t1 = wave >= 2 ? MT::load(Tm, tr, 32 + 8 * lg) : Frag<F32>{};
             Frag<F32> fa[2 * RT], fb[2 * RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -939,7 +969,7 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
             Frag<F32> uf[RT][2], udf[RT][2], pr[2];  // [tile][token half], [token half]
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                pr[h2] = MT::load(Pm, tr, 32 * h2 + 8 * lg);
+                pr[h2] = h2 == 0 || wave >= 2 ? MT::load(Pm, tr, 32 * h2 + 8 * lg) : Frag<F32>{};
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     uf[rt][h2] = MY::load(Up, 16 * rt + li, 32 * h2 + 8 * lg);

@@ -92,7 +92,7 @@ int main(void)
     CHECK(gdn_prefill_noalloc(&d, MIS, F, F, F, F, F, F, F, F, F, F, 64, 0, NULL), GDN_ERR_ARG);
     CHECK(gdn_prefill_noalloc(NULL, F, F, F, F, F, F, F, F, F, F, F, 64, 0, NULL), GDN_ERR_ARG);
     if (gdn_prefill_workspace_bytes(&d, 0) != 0) { fprintf(stderr, "workspace bytes for 0 tokens\n"); ++failures; }
-    if (gdn_prefill_workspace_bytes(&d, 8192) != 406847488u) { fprintf(stderr, "workspace bytes at 8192\n"); ++failures; }
+    if (gdn_prefill_workspace_bytes(&d, 8192) != 373293056u) { fprintf(stderr, "workspace bytes at 8192\n"); ++failures; }
     /* sizes, reset, snapshot */
     size_t cb = 1;
     if (gdn_capture_bytes(&bad, 16, GDN_CHAIN, &cb) != 0 || cb != 0) { fprintf(stderr, "capture bytes of bad dims\n"); ++failures; }

@@ -140,11 +140,12 @@ def test_capture_bytes_match_layout():
 def test_prefill_validation():
     """gdn_prefill rejects bad arguments before any launch.  The workspace holds, per 64-token
     chunk, the fp32 readout (64 H_v d), q and k per key head (2 H_k 64 d), T and P per value head
-    (2 H_v 64 x 64) and a 256-float gate record per value head."""
+    (2 H_v x the 3072 entries of a 64 x 64 lower-triangular matrix outside its zero upper-right
+    32 x 32 block) and a 256-float gate record per value head."""
     L = _lib_or_skip()
     d = gdn.make_dims(W.CHUNKED_PREFILL)
-    per_chunk = 64 * 32 * 128 + 2 * 16 * 64 * 128 + 2 * 32 * 64 * 64 + 32 * 256
-    assert L.gdn_prefill_workspace_bytes(ctypes.byref(d), 8192) == 4 * 128 * per_chunk == 406_847_488
+    per_chunk = 64 * 32 * 128 + 2 * 16 * 64 * 128 + 2 * 32 * (64 * 64 - 32 * 32) + 32 * 256
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(d), 8192) == 4 * 128 * per_chunk == 373_293_056
     assert L.gdn_prefill_workspace_bytes(ctypes.byref(d), 65) == 4 * 2 * per_chunk  # whole chunks
     assert L.gdn_prefill_workspace_bytes(ctypes.byref(d), 0) == 0
     big = 1 << 40
