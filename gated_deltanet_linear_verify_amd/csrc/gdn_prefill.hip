@@ -391,7 +391,8 @@ struct ScanLds {
     // U^T diag(dec) [kSR][C] (operand form; bf16 only: fp32 operands are scaled where they are read)
     static constexpr size_t dp = up + sizeof(float) * kSR * C;
     static constexpr size_t sx = dp + (ACT_BF16 ? sizeof(float) * kSR * C : 0);  // S [kSR][D] (operand form)
-    static constexpr size_t total = sx + sizeof(float) * kSR * D;
+    static constexpr size_t touch = sx + sizeof(float) * kSR * D;  // where the L2 touches land (never read)
+    static constexpr size_t total = touch + 256;
 };
 static_assert(ScanLds<128, true>::total <= 160 * 1024 && ScanLds<128, false>::total <= 160 * 1024,
               "the d=128 scan must fit one CU's LDS");
@@ -794,6 +795,21 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
             }
         }
     };
+    // L2 touch of chunk cc's operands, a chunk before their transfers into LDS: one dword of every
+    // 128-byte line of this workgroup's share of the key head's q and k images and of the value
+    // head's T and P (one 4-byte transfer per producer wave, 16 lines each; slots past the share
+    // repeat its first line).  It only warms the cache: what lands in LDS is never read.
+    auto issue_touch = [&](int cc) {
+        constexpr int qk_lines = 2 * C * D * 4 / 128, tp_lines = kTriFloats * 4 / 128;
+        const int grp = R * NB, j = (h % R) * NB + blk;  // workgroups of the key head, this one's index
+        const int nq = (qk_lines + grp - 1) / grp, ntp = (tp_lines + NB - 1) / NB;
+        const int sl = 16 * pw + (lane & 15);
+        const int in_t = sl - nq, in_p = sl - nq - ntp;
+        const float *src = in_p >= 0 && in_p < ntp ? a.ws + w.p + chunk_rec(cc) * kTriFloats + 32 * min(blk * ntp + in_p, tp_lines - 1)
+                         : in_t >= 0 && in_t < ntp ? a.ws + w.t + chunk_rec(cc) * kTriFloats + 32 * min(blk * ntp + in_t, tp_lines - 1)
+                                                   : qk_img(cc, 0) + 32 * min(sl < nq ? j * nq + sl : j * nq, qk_lines - 1);
+        lds_dma4(src, smem + L::touch);
+    };
     // transfers per producer wave: T or P, a q image (uniform), and one gate transfer each
     constexpr int NT = kTriFloats / 4 / (64 * kProducers);
     constexpr int NQ = C * D / 4 / (64 * kProducers);
@@ -809,13 +825,15 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
     // reaches a barrier after the compute waves: P, the gates and q (double buffered) during A;
     // half of k and v during B (A has read k and v of c); the other half of k and T during C.  T is
     // issued last and needed only by B, so the chunk start waits for everything else and the
-    // barrier after A for T.
+    // barrier after A for T.  The operands of c + 2 are touched into L2 during A of c, so the
+    // transfers of c + 1 that start late in c find them there rather than in HBM.
     if (producer) {
         issue_pg(0);
         issue_q(0);
         issue_k(0, 0);
         issue_v(0);
         issue_k(0, 1);
+        issue_touch(min(1, nchunks - 1));
         issue_t(0);
 #pragma unroll 1
         for (int c = 0; c < nchunks; ++c) {
@@ -824,7 +842,8 @@ __global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs 
             if (c + 1 < nchunks) {
                 issue_pg(c + 1);
                 issue_q(c + 1);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(NT + 1 + NQ));  // T of c (P, gates, q of c + 1 may travel)
+                issue_touch(min(c + 2, nchunks - 1));
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(NT + 1 + NQ + 1));  // T of c (P, gates, q of c + 1, the touch may travel)
             } else {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
