@@ -61,6 +61,34 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def counter_record(name: str):
+    """The committed rocprofv3 counter summary profiles/counters_<name>.json, condensed, or None
+    when it is missing or was taken on different kernel sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", f"counters_{name}.json")) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha256_16") != source_digest(t["kernel_sources"]):
+            return None
+    except (OSError, ValueError, KeyError):
+        return None
+    rec = {"file": f"profiles/counters_{name}.json", "hbm_bytes_per_call": t["hbm_bytes_per_call"]}
+    if "traffic_over_algorithmic" in t:
+        rec["traffic_over_algorithmic"] = t["traffic_over_algorithmic"]
+    kern = {}
+    busy = active = 0.0
+    for k, e in t["kernels"].items():
+        kern[k] = {"hbm_read_bytes": e["hbm_read_bytes"], "hbm_write_bytes": e["hbm_write_bytes"]}
+        if "mfma_util" in e:
+            kern[k]["mfma_util"] = e["mfma_util"]
+            kern[k]["mfma_flops"] = e["mfma_bf16_flops"] + e["mfma_f32_flops"]
+            busy += e["mfma_busy_cycles"]
+            active += e["grbm_gui_active_per_xcd"] * 1024
+    rec["kernels"] = kern
+    if active:
+        rec["mfma_util"] = busy / active  # MFMA busy cycles over active cycles x SIMDs, all kernels
+    return rec
+
+
 def cpu_baseline(shape, inp, target_s: float = 10.0) -> dict:
     """The fp64 oracle (test infrastructure, untuned) on the same workload: every (slot, value
     head) unit with capture, repeated until about target_s seconds of host time; the median
@@ -125,7 +153,8 @@ def components(args) -> dict:
     out["tree_verify"] = {"workload": "8 slots x 64-node trees, 16/32 heads, d=128, bf16",
                           "us": us, "tokens_per_s": s.n_batch * s.n_tok / (us * 1e-6),
                           "hbm_gbps": bytemodel.tree_bytes(s) / (us * 1e-6) / 1e9,
-                          "algorithmic_bytes": bytemodel.tree_bytes(s)}
+                          "algorithmic_bytes": bytemodel.tree_bytes(s),
+                          "counters": counter_record("tree_8x64")}
     del d
     # single-slot verify: 1 slot x 16 tokens
     s = W.SINGLE_SLOT_VERIFY
@@ -226,6 +255,8 @@ def components(args) -> dict:
             "in_proj_tflops": f_in / (us_in * 1e-6) / 1e12, "out_proj_tflops": f_out / (us_out * 1e-6) / 1e12,
             "in_proj_mfma_util_vs_bf16_peak": f_in / (us_in * 1e-6) / PEAK_BF16_FLOPS,
             "out_proj_mfma_util_vs_bf16_peak": f_out / (us_out * 1e-6) / PEAK_BF16_FLOPS}
+        if nb == 64:
+            out[name]["counters"] = counter_record("linear_block_64_slots")
         del d
     torch.cuda.empty_cache()
     # chunked prefill: one 8192-token sequence
@@ -237,7 +268,8 @@ def components(args) -> dict:
                               "us": us, "tokens_per_s": s.n_tok / (us * 1e-6),
                               "hbm_gbps": bytemodel.prefill_bytes(s) / (us * 1e-6) / 1e9,
                               "algorithmic_flops": fl, "tflops": fl / (us * 1e-6) / 1e12,
-                              "mfma_util_vs_bf16_peak": fl / (us * 1e-6) / PEAK_BF16_FLOPS}
+                              "mfma_util_vs_bf16_peak": fl / (us * 1e-6) / PEAK_BF16_FLOPS,
+                              "counters": counter_record("prefill_8192")}
     del d
     torch.cuda.empty_cache()
     return out
