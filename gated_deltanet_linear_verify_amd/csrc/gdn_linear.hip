@@ -10,10 +10,10 @@
 // the concatenated weight.
 //
 // Tiling: a workgroup computes a block of y with a grid of waves, each a grid of 16 x 16 tiles of
-// v_mfma_f32_16x16x32_bf16 (128 x 128 blocks for many rows, 32 x 64 for few).  K advances 64 at a
-// time; the next x and W tiles travel into the other half of a double-buffered LDS by
-// global_load_lds while the current ones are multiplied.  Within
-// an LDS tile row (64 bf16 = 8 chunks of 16 bytes) chunk c of row r sits at position c ^ (r & 7),
+// v_mfma_f32_16x16x32_bf16 (256 x 256 or 128 x 128 blocks for many rows, 32 x 64 for few).  K
+// advances 64 at a time, one barrier per step: the next x and W tiles travel into the other half
+// of a double-buffered LDS by global_load_lds while the current ones are multiplied.  Within an
+// LDS tile row (64 bf16 = 8 chunks of 16 bytes) chunk c of row r sits at position c ^ (r & 7),
 // so the 16 rows an operand load touches spread over the banks; the DMA writes LDS linearly, so
 // the swizzle is applied by choosing the global chunk each lane fetches.
 #include "gdn_device.h"
@@ -36,6 +36,11 @@ __device__ __forceinline__ f4 mfma_bf16(bf16x8_t a, bf16x8_t b, f4 c)
     return c;
 #endif
 }
+
+// Scheduling groups (__builtin_amdgcn_sched_group_barrier): n instructions of one kind, groups
+// placed in the order of the calls within the enclosing block.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // LDS byte offset of chunk c of tile row r
 __device__ __forceinline__ int lchunk(int r, int c) { return (r * kLChunks + (c ^ (r & 7))) * 16; }
@@ -64,11 +69,12 @@ __global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
     const int li = lane & 15, lg = lane >> 4;
     const int wm = wave / GN, wn = wave % GN;  // the wave's place in the GM x GN grid
     // Tiles are numbered n-major, m fastest (t = n_tile * mt + m_tile), and workgroups are dealt
-    // to the 8 XCDs in turn; XCD x takes the contiguous tile range [x T/8, (x+1) T/8), so the
-    // workgroups sharing a weight tile run on one XCD, one after another, and read it from that
-    // XCD's L2 instead of once per XCD.
+    // to the 8 XCDs in turn; XCD x takes a contiguous tile range (the first T mod 8 XCDs one tile
+    // more than the others), so the workgroups sharing a weight tile run on one XCD, one after
+    // another, and read it from that XCD's L2 instead of once per XCD.
     const int mt = (a.M + BM - 1) / BM, ntiles = gridDim.x;
-    const int t = ntiles % 8 == 0 ? (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int xcd = blockIdx.x % 8, q8 = ntiles / 8, r8 = ntiles % 8;
+    const int t = xcd * q8 + min(xcd, r8) + blockIdx.x / 8;
     const int m0 = (t % mt) * BM, n0 = (t / mt) * BN;
     const int K = a.K;
 
@@ -105,31 +111,47 @@ __global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) {
-            issue(kt + 1, buf ^ 1);
-            // all but the next tile's transfers (only loads are in flight: the wait is exact)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | ((TL::XT + TL::WT) & 0xF) | (((TL::XT + TL::WT) >> 4) << 14));
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's transfers of tile kt have landed
+        // Every wave's transfers of tile kt have landed, and every wave is done with tile kt - 1,
+        // so the other buffer takes tile kt + 1: one barrier per k tile.
         lds_barrier();
+        if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
         const unsigned char *xs = lds + buf * BUF, *ws = xs + XB;
+        // every fragment of the tile's 32-deep steps is read before the first product, so the later
+        // steps' reads are in flight while the earlier steps' products run
+        constexpr int KS = kLBK / 32;
+        bf16x8_t af[KS][WM], bf[KS][WN];
 #pragma unroll
-        for (int ks = 0; ks < kLBK / 32; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const int c = 4 * ks + lg;  // this lane's chunk of the 32-deep step
-            bf16x8_t af[WM], bf[WN];
 #pragma unroll
             for (int i = 0; i < WM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t *>(xs + lchunk(16 * WM * wm + 16 * i + li, c));
+                af[ks][i] = *reinterpret_cast<const bf16x8_t *>(xs + lchunk(16 * WM * wm + 16 * i + li, c));
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-                bf[j] = *reinterpret_cast<const bf16x8_t *>(ws + lchunk(16 * WN * wn + 16 * j + li, c));
+                bf[ks][j] = *reinterpret_cast<const bf16x8_t *>(ws + lchunk(16 * WN * wn + 16 * j + li, c));
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int i = 0; i < WM; ++i)
 #pragma unroll
-                for (int j = 0; j < WN; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < WN; ++j) acc[i][j] = mfma_bf16(af[ks][i], bf[ks][j], acc[i][j]);
+        // Instruction order (the compiler would otherwise read each fragment just before its first
+        // product and wait for it there): the first step's reads, then each later step's reads
+        // spread between the previous step's products, so LDS latency hides behind MFMA work.
+        constexpr int NR = WM + WN, NM = WM * WN, PER = NM / NR > 0 ? NM / NR : 1;
+        sched_group(kSchedDsRead, NR);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                sched_group(kSchedMfma, PER);
+                sched_group(kSchedDsRead, 1);
+            }
+            if (NM > PER * NR) sched_group(kSchedMfma, NM - PER * NR);
         }
-        lds_barrier();  // every wave is done with this buffer before the transfer two tiles on
+        sched_group(kSchedMfma, NM);
     }
 
     // ---- epilogue: element (row 4 lg + r, column li) of each 16 x 16 tile to its segment
@@ -170,14 +192,19 @@ static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Tile by rows: many rows take 128 x 128 tiles worked by 16 waves of 32 x 32 (two workgroups per
-// CU: the most resident waves to cover each wave's LDS operand latency; measured against 4 and 8
-// waves per tile and 256-wide tiles, which bring more flops per transferred byte but leave fewer
-// waves); a few rows (one slot's drafted tokens) take 32 x 64 tiles, so the weight stream is spread
-// over enough workgroups.
+// Tile choice.  A k tile brings (BM + BN) x 64 operands into LDS for 2 BM BN x 64 flops, so larger
+// workgroup tiles need fewer bytes per flop from L2; 256 x 256 (16 waves of 64 x 64, one workgroup
+// per CU) is the fastest per CU, and is taken when its tiles fill at least three quarters of the
+// 256 CUs (1024 x 5120 -> 12352: 196 tiles, 134 us against 162 us with 128 x 128).  Otherwise
+// 128 x 128 tiles of 16 waves of 32 x 32, two workgroups per CU, spread a smaller product over
+// every CU (1024 x 4096 -> 5120: 320 tiles, 56 us against 106 us with 80 of 256 x 256); a few rows
+// (one slot's drafted tokens) take 32 x 64 tiles, so the weight stream is spread over enough
+// workgroups.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t stream)
 {
     if (a.M <= 64) return launch_tile<2, 2, 1, 2>(a, stream);
+    const long big = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (big >= 192) return launch_tile<4, 4, 4, 4>(a, stream);
     return launch_tile<4, 4, 2, 2>(a, stream);
 }
 

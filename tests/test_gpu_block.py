@@ -40,9 +40,11 @@ def _bf16_err(gpu, ref_):
     return float(np.max(np.maximum(np.abs(gpu - ref_) - half_ulp_bf16(ref_), 0.0)) / np.max(np.abs(ref_)))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (200, 300, 256), (128, 128, 64), (257, 129, 320), (64, 4160, 512)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (200, 300, 256), (128, 128, 64), (257, 129, 320), (64, 4160, 512),
+                                   (1100, 10000, 320)])
 def test_linear_fp32_out(M, N, K):
-    """Ragged M and N (partial tiles, a single element), several K tiles."""
+    """Ragged M and N (partial tiles, a single element), several K tiles; the last shape has enough
+    256 x 256 tiles (5 x 40) to take that tiling, with partial tiles along both M and N."""
     from gated_deltanet_linear_verify_amd import gdn
     say(f"[linear] M={M} N={N} K={K}")
     x, w = _operands(M, N, K, seed=M + N + K)
@@ -157,3 +159,17 @@ def test_block_against_oracle(name):
     # for information: the whole block against the oracle's own chain of bf16 intermediates
     r = block.block_verify(base, inp)
     say(f"  end to end (bf16 intermediates on each side): {rel_err(y, r['y']):.2e}")
+
+
+def test_linear_out_projection_full_size_sampled_rows():
+    """The 64-slot block's output projection at full size (1024 tokens x 4096 -> 5120, the
+    128 x 128 tiling): 32 sampled rows against the oracle, bf16 outputs."""
+    from gated_deltanet_linear_verify_amd import gdn
+    s = W.MULTI_SLOT_VERIFY
+    M, K, N = s.n_batch * s.n_tok, s.n_vh * s.d_v, W.HIDDEN
+    x, w = _operands(M, N, K, seed=22)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_linear(_bf16_dev(x), _bf16_dev(w), M, N, K, [(0, N, y, N, 0)])
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(6).choice(M, 32, replace=False)
+    assert _bf16_err(to_np(y)[rows], block.linear(x[rows], w)) < TOL_F32
