@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["gdn_abi.cpp", "gdn_prefill_abi.cpp", "gdn_graph.cpp", "gdn_linear_abi.cpp", "gdn_linear.hip", "gdn_verify.hip", "gdn_rollback.hip", "gdn_tree.hip",
-           "gdn_prefill.hip", "gdn_noalloc.hip"]
+           "gdn_prefill.hip", "gdn_noalloc.hip", "gdn_scratch.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

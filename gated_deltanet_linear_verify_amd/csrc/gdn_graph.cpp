@@ -18,6 +18,7 @@ struct gdn_graph {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     hipEvent_t done = nullptr;  // recorded after every replay, so destroy can wait for the last
+    void *oscr = nullptr;       // the row-split verify's readout scratch the recorded kernels use
 };
 
 namespace {
@@ -28,6 +29,7 @@ void release(gdn_graph *g)
     if (g->exec) (void)hipGraphExecDestroy(g->exec);
     if (g->graph) (void)hipGraphDestroy(g->graph);
     if (g->done) (void)hipEventDestroy(g->done);
+    if (g->oscr) (void)hipFree(g->oscr);
     delete g;
 }
 
@@ -87,6 +89,9 @@ GDN_API int gdn_graph_create(const gdn_dims *dims, const gdn_layer *layers, int3
         return gdn::abi_fail(GDN_ERR_HIP, "gdn_graph_create: stream: %s", hipGetErrorString(e));
     gdn_graph *g = new gdn_graph;
     int rc = GDN_OK;
+    // A readout scratch for the capture stream, kept by the graph: row-split verify launches under
+    // the capture use it (without one they take the unsplit path).
+    (void)gdn::split_scratch(st, true);
     if (hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal)) {
         rc = gdn::abi_fail(GDN_ERR_HIP, "gdn_graph_create: begin capture: %s", hipGetErrorString(e));
     } else {
@@ -95,6 +100,7 @@ GDN_API int gdn_graph_create(const gdn_dims *dims, const gdn_layer *layers, int3
         if (rc == GDN_OK && ee != hipSuccess)
             rc = gdn::abi_fail(GDN_ERR_HIP, "gdn_graph_create: end capture: %s", hipGetErrorString(ee));
     }
+    g->oscr = gdn::split_scratch_take(st);
     if (rc == GDN_OK)
         if (hipError_t e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0))
             rc = gdn::abi_fail(GDN_ERR_HIP, "gdn_graph_create: instantiate: %s", hipGetErrorString(e));

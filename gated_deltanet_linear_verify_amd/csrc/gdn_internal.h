@@ -31,7 +31,15 @@ struct VerifyArgs {
     int32_t defer;  // chain verify with capture: leave state and conv_state untouched (the state
                     // after the last token stays at its capture position)
     int32_t hpw;    // chain verify: value heads per workgroup, set by the launcher (H_v/H_k, or 1)
+    float *oscr;    // chain verify, row split: the launch's readout [n_batch][16][H_v][d] (set by the launcher)
 };
+
+// The row-split verify's readout scratch for stream st on the current device: the buffer kept for
+// the stream, else (allocate, and st not capturing) a new one of kSplitScratchBytes, else NULL.
+constexpr size_t kSplitScratchBytes = size_t(4) << 20;
+void *split_scratch(hipStream_t st, bool allocate);
+// Remove the buffer kept for st and hand it to the caller (who frees it), or NULL.
+void *split_scratch_take(hipStream_t st);
 
 struct LaunchCfg {
     bool act_bf16, out_bf16, qk_norm;

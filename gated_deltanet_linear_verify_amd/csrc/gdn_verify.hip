@@ -60,34 +60,76 @@ struct VerifyLds {
     }
 };
 
+// One (token, value head) row of the output, out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z),
+// worked by 16 lanes: lane cg holds o at rows cg EPL .. cg EPL + EPL - 1 (ov), the matching z and
+// norm weights.  Shared by the fused epilogue and the row-split norm kernel, which therefore give
+// the same bits.
+template <bool ACT_BF16, bool OUT_BF16, int D>
+__device__ __forceinline__ void norm_gate_row(const float (&ov)[D / 16], const float *nwr,
+                                              const typename std::conditional<ACT_BF16, uint16_t, float>::type *zrow,
+                                              float eps, void *out, size_t base)
+{
+    constexpr int EPL = D / 16;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ss += ov[e] * ov[e];
+    ss = row16_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        float zz;
+        if constexpr (ACT_BF16)
+            zz = bf16_to_f32(zrow[e]);
+        else
+            zz = zrow[e];
+        const float y = ov[e] * inv * nwr[e] * (zz * sigmoid_f(zz));
+        if constexpr (OUT_BF16)
+            static_cast<uint16_t *>(out)[base + e] = f32_to_bf16(y);
+        else
+            static_cast<float *>(out)[base + e] = y;
+    }
+}
+
+// Row split (SPLIT): kRowSplit workgroups per value head, each with NW waves that hold its share of
+// the head's rows in the layout of NW * kRowSplit waves (so every row sees the same arithmetic as
+// in one workgroup).  A workgroup writes its rows' state, capture and v conv; its readout goes to
+// the scratch, and verify_norm_kernel applies the norm and gate, and writes the q / k conv, after
+// the launch.  One token's state update over a d x d head is ~d^2 fused multiply-adds per
+// contraction, which one CU's vector units take ~1000 clocks for at d = 128: splitting the rows
+// over CUs is what shortens the token chain when few heads are in flight.
+constexpr int kRowSplit = 4;
+
 // NW: waves per value head (4 at d = 128 with all of a key head's value heads in the workgroup,
-// 8 with one value head per workgroup: half the rows per lane, the same arithmetic per row).
-template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN, bool CAP, int NW>
+// 8 with one value head per workgroup: half the rows per lane, the same arithmetic per row), or
+// per workgroup of a row split.
+template <int D, bool ACT_BF16, bool OUT_BF16, bool QKN, bool CAP, int NW, bool SPLIT>
 __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
     using L = VerifyLds<D, act_t>;
-    using G = Geo<D, NW>;
+    using G = Geo<D, SPLIT ? NW * kRowSplit : NW>;
     constexpr int TT = kTokenTile;
     constexpr int VEC = 16 / (int)sizeof(act_t);  // activations per 16-byte load
     const int R = a.n_vh / a.n_kh;  // value heads per key head
-    const int HW = a.hpw;           // value heads of this workgroup: R, or 1 (few batch entries)
+    const int HW = SPLIT ? 1 : a.hpw;  // value heads of this workgroup: R, or 1 (few batch entries)
     const int nthr = blockDim.x;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int nwaves = nthr >> 6;
-    const int hl = wave / NW, wih = wave % NW;
+    const int rj = SPLIT ? blockIdx.x % kRowSplit : 0;  // this workgroup's share of a split head
+    const int wgi = SPLIT ? blockIdx.x / kRowSplit : blockIdx.x;
+    const int hl = SPLIT ? 0 : wave / NW, wih = SPLIT ? rj * NW + wave : wave % NW;
     const int rg = lane >> 4, cg = lane & 15;
 
-    const int gpb = a.n_vh / HW;             // workgroups per batch entry
-    const int b = blockIdx.x / gpb;
-    const int h0 = (blockIdx.x % gpb) * HW;  // first value head of the workgroup
+    const int gpb = a.n_vh / HW;       // workgroups (sets of a split) per batch entry
+    const int b = wgi / gpb;
+    const int h0 = (wgi % gpb) * HW;  // first value head of the workgroup
     const int hk = h0 / R;
     const int h = h0 + hl;
     // With one value head per workgroup the key head's q / k channels are shared, and every
     // workgroup of the key head reads their starting rows here, so none of them writes those
     // channels: qk_conv_state_kernel writes their conv window rows and conv state after the launch.
-    const bool own_qk = HW == R;
+    const bool own_qk = HW == R && !SPLIT;
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the workgroup
     // A rollback left pending by the previous round: the first launch of the call starts from the
@@ -163,13 +205,19 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     uint32_t al_raw = static_cast<const word_t *>(a.alpha)[ab_tok];
     uint32_t be_raw = static_cast<const word_t *>(a.beta)[ab_tok];
     float alog = a.A_log[ab_h], dtb = a.dt_bias[ab_h];
+    // The channels this workgroup convolves: q, k and its heads' v; in a row split only the v
+    // channels of its own rows, which no other workgroup of the split reads or writes (the others'
+    // v rows are written during the launch, as its own are).
+    auto conv_chan = [&](int lc) {
+        return lc < nch && (!SPLIT || lc < 2 * D || (lc - 2 * D) / (D / kRowSplit) == rj);
+    };
     // conv taps and the slot's conv state (xext rows 0..2 of the launch) of this thread's channels
     f4 wv[2];
     float csv[2][3];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int lc = tid + it * nthr;
-        if (lc < nch) {
+        if (conv_chan(lc)) {
             const int gc = gchan(lc);
             wv[it] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gc * 4);
 #pragma unroll
@@ -212,7 +260,7 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int lc = tid + it * nthr;
-        if (lc < nch) {
+        if (conv_chan(lc)) {
             const int gc = gchan(lc);
             float *dst;
             if (lc < D)
@@ -296,6 +344,15 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     }
     lds_barrier();  // o of every head is in LDS; the capture stores stay in flight
 
+    if constexpr (SPLIT) {
+        // ================= the readout of this workgroup's rows, natural row order, to the scratch
+        constexpr int RW = D / kRowSplit;
+        for (int i = tid; i < nt * RW; i += nthr) {
+            const int t = i / RW, r = rj * RW + i % RW;
+            a.oscr[(((size_t)b * TT + t) * a.n_vh + h) * D + r] = os[t * D + G::perm(r)];
+        }
+        return;
+    }
     // ================= epilogue: out = o / sqrt(mean(o^2) + eps) * norm_w * silu(z) =================
     constexpr int EPL = D / 16;  // 16 lanes per (head, token) row
     const int grp = tid >> 4, ngrp = nthr >> 4;
@@ -304,25 +361,11 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
         const int hh = row / nt, t = row % nt, h2 = h0 + hh;
         const float *osrc = os + (hh * TT + t) * D;
         float ov[EPL];
-        float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            ov[e] = osrc[G::perm(cg * EPL + e)];
-            ss += ov[e] * ov[e];
-        }
-        ss = row16_sum(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+        for (int e = 0; e < EPL; ++e) ov[e] = osrc[G::perm(cg * EPL + e)];
         const size_t base = (((size_t)b * T + t0 + t) * a.n_vh + h2) * D + cg * EPL;
-        const act_t *zrow = zs + t * HW * D + hh * D + cg * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const float zz = to_f32(zrow[e]);
-            const float y = ov[e] * inv * nws[cg * EPL + e] * (zz * sigmoid_f(zz));
-            if constexpr (OUT_BF16)
-                static_cast<uint16_t *>(a.out)[base + e] = f32_to_bf16(y);
-            else
-                static_cast<float *>(a.out)[base + e] = y;
-        }
+        norm_gate_row<ACT_BF16, OUT_BF16, D>(ov, nws + cg * EPL, zs + t * HW * D + hh * D + cg * EPL, a.eps, a.out,
+                                             base);
     }
 }
 
@@ -340,10 +383,9 @@ size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16)
 // window rows it resumes from, chosen as in the verify kernel) followed by its tokens.  Every read
 // of a channel precedes its writes, and all of them are issued before the first is used.
 template <bool ACT_BF16, bool CAP>
-__global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
+__device__ __forceinline__ void qk_conv_channel(const VerifyArgs &a, int b, int ch)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
-    const int b = blockIdx.y;
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the block, as in the verify kernel
     int ra = -1;
@@ -356,8 +398,7 @@ __global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
         if (a.defer && a.t0 > 0) ra = a.t0 - 1;
     }
     const bool commit = !(CAP && a.defer);
-    const int ch = blockIdx.x * blockDim.x + threadIdx.x;  // q | k channels are 0 .. 2 H_k d - 1
-    if (ch >= 2 * a.n_kh * a.d) return;
+    if (ch >= 2 * a.n_kh * a.d) return;  // q | k channels are 0 .. 2 H_k d - 1
     const size_t C = (size_t)a.C;
     const int t0 = a.t0, nt = a.nt;
     float *cs = a.conv_state + (size_t)s * 3 * C + ch;
@@ -389,6 +430,43 @@ __global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
 #pragma unroll
         for (int r = 0; r < 3; ++r) cs[(size_t)r * C] = xs[nt + r];
 }
+template <bool ACT_BF16, bool CAP>
+__global__ __launch_bounds__(256) void qk_conv_state_kernel(VerifyArgs a)
+{
+    qk_conv_channel<ACT_BF16, CAP>(a, blockIdx.y, blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// After a row-split launch: its first blocks write the key heads' q / k conv as qk_conv_state_kernel
+// does (per batch entry, 256 channels a block), the others apply the norm and gate to the readout
+// in the scratch, 16 lanes per (batch entry, token, value head) row, as the fused epilogue does.
+template <int D, bool ACT_BF16, bool OUT_BF16, bool CAP>
+__global__ __launch_bounds__(256) void verify_norm_kernel(VerifyArgs a)
+{
+    using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
+    constexpr int EPL = D / 16;
+    const int conv_blocks = (2 * a.n_kh * D + 255) / 256;
+    const int nconv = conv_blocks * a.n_batch;
+    if ((int)blockIdx.x < nconv) {
+        qk_conv_channel<ACT_BF16, CAP>(a, blockIdx.x / conv_blocks, (blockIdx.x % conv_blocks) * 256 + threadIdx.x);
+        return;
+    }
+    // every lane of a 16-lane group takes the same row, so the returns below are uniform per group
+    const int row = ((int)blockIdx.x - nconv) * 16 + (int)(threadIdx.x >> 4), cg = threadIdx.x & 15;
+    if (row >= a.n_batch * a.nt * a.n_vh) return;
+    const int h = row % a.n_vh, t = (row / a.n_vh) % a.nt, b = row / (a.n_vh * a.nt);
+    const int s = a.slot_ids[b];
+    if (s < 0 || s >= a.n_pool) return;  // skipped by the verify kernel too
+    if (CAP && a.resume && a.resume[b] >= a.t_cap) return;
+    const float *o = a.oscr + (((size_t)b * kTokenTile + t) * a.n_vh + h) * D + cg * EPL;
+    float ov[EPL], nwr[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        ov[e] = o[e];
+        nwr[e] = a.norm_w[cg * EPL + e];
+    }
+    const size_t base = (((size_t)b * a.T + a.t0 + t) * a.n_vh + h) * D + cg * EPL;
+    norm_gate_row<ACT_BF16, OUT_BF16, D>(ov, nwr, static_cast<const act_t *>(a.z) + base, a.eps, a.out, base);
+}
 
 // Value heads per workgroup.  With few batch entries a workgroup per key head leaves most CUs idle
 // and each one streams its heads' whole capture through one store path (~64 B per clock), so then
@@ -402,6 +480,15 @@ static int heads_per_workgroup(const VerifyArgs &a)
     const int R = a.n_vh / a.n_kh;
     if (R == 1 || a.T < kSplitMinTokens) return R;
     return (long)a.n_batch * a.n_kh <= kSplitMaxWorkgroups ? 1 : R;
+}
+
+// Row split: when the call's value heads times kRowSplit fit one workgroup per CU (one slot of 32
+// heads: 128 workgroups), from kSplitMinTokens tokens, and the readout fits the scratch.
+constexpr int kCus = 256;
+static bool row_split(const VerifyArgs &a)
+{
+    if (a.T < kSplitMinTokens || (long)a.n_batch * a.n_vh * kRowSplit > kCus) return false;
+    return (size_t)a.n_batch * kTokenTile * a.n_vh * a.d * sizeof(float) <= kSplitScratchBytes;
 }
 
 // One launch covers at most kTokenTile tokens; longer chains are consecutive launches on the same
@@ -418,16 +505,33 @@ static hipError_t launch_t(const VerifyArgs &a0, hipStream_t stream)
     const int wgs_per_cu = waves >= kTargetWavesPerCu ? 1 : kTargetWavesPerCu / waves;
     const size_t lds_cap = kLdsPerCu / (wgs_per_cu + 1) + 16;  // wgs_per_cu + 1 workgroups no longer fit
     if (CAP && lds < lds_cap) lds = lds_cap;  // without capture stores more resident waves only help
+    float *oscr = row_split(a0) ? static_cast<float *>(split_scratch(stream, true)) : nullptr;
     for (int t0 = 0; t0 < a0.T; t0 += kTokenTile) {
         VerifyArgs a = a0;
         a.t0 = t0;
         a.nt = a0.T - t0 < kTokenTile ? a0.T - t0 : kTokenTile;
+        if (oscr) {
+            constexpr int NWS = 2 * WavesPerHead<D>::value;  // waves per workgroup of the split
+            a.hpw = 1;
+            a.oscr = oscr;
+            size_t lds1 = verify_chain_lds_bytes(D, 1, AB);
+            const size_t cap1 = kLdsPerCu / (kTargetWavesPerCu / NWS + 1) + 16;
+            if (CAP && lds1 < cap1) lds1 = cap1;
+            hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP, NWS, true>),
+                               dim3(a.n_batch * a.n_vh * kRowSplit), dim3(NWS * 64), lds1, stream, a);
+            if (hipError_t e = hipGetLastError()) return e;
+            const unsigned blocks = (unsigned)(((2 * a.n_kh * D + 255) / 256) * a.n_batch +
+                                               (a.n_batch * a.nt * a.n_vh + 15) / 16);
+            hipLaunchKernelGGL((verify_norm_kernel<D, AB, OB, CAP>), dim3(blocks), dim3(256), 0, stream, a);
+            if (hipError_t e = hipGetLastError()) return e;
+            continue;
+        }
         a.hpw = HW;
         if (HW < R)
-            hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP, 2 * WavesPerHead<D>::value>),
+            hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP, 2 * WavesPerHead<D>::value, false>),
                                dim3(a.n_batch * (a.n_vh / HW)), dim3(threads), lds, stream, a);
         else
-            hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP, WavesPerHead<D>::value>),
+            hipLaunchKernelGGL((verify_chain_kernel<D, AB, OB, QKN, CAP, WavesPerHead<D>::value, false>),
                                dim3(a.n_batch * (a.n_vh / HW)), dim3(threads), lds, stream, a);
         if (hipError_t e = hipGetLastError()) return e;
         if (HW < R) {

@@ -15,7 +15,7 @@ objs=()
 DEV="--offload-arch=gfx950 -Xclang -target-feature -Xclang -packed-fp32-ops"
 pids=()
 for f in gdn_abi.cpp gdn_prefill_abi.cpp gdn_linear_abi.cpp gdn_graph.cpp gdn_verify.hip gdn_rollback.hip \
-         gdn_tree.hip gdn_prefill.hip gdn_linear.hip gdn_noalloc.hip; do
+         gdn_tree.hip gdn_prefill.hip gdn_linear.hip gdn_noalloc.hip gdn_scratch.cpp; do
     o="$OUT/${f%.*}.o"
     lang=""
     case "$f" in *.hip) lang="-x hip" ;; esac
