@@ -262,9 +262,11 @@ def components(args) -> dict:
     # chunked prefill: one 8192-token sequence
     s = W.CHUNKED_PREFILL
     d = device.upload(s, W.make_inputs(s, 0), capture=False)
-    us = time_launches(lambda: device.prefill(d), 20)
+    # steady state: a process's first few dozen prefills run up to ~15% slower
+    us = time_launches(lambda: device.prefill(d), 20, warmup=40)
     fl = bytemodel.prefill_flops(s)
     out["chunked_prefill"] = {"workload": "1 slot x 8192 tokens, 16/32 heads, d=128, bf16, chunk 64",
+                              "timing": "20 calls after 40 warm-up calls",
                               "us": us, "tokens_per_s": s.n_tok / (us * 1e-6),
                               "hbm_gbps": bytemodel.prefill_bytes(s) / (us * 1e-6) / 1e9,
                               "algorithmic_flops": fl, "tflops": fl / (us * 1e-6) / 1e12,
