@@ -120,8 +120,10 @@ def cpu_baseline(shape, inp, target_s: float = 10.0) -> dict:
                       f"{sum(times):.1f} s, median {med * 1e3:.0f} ms"}
 
 
-def time_launches(fn, n: int, warmup: int = 3) -> float:
-    """Average duration in microseconds of fn() over n launches, HIP events on the current stream."""
+def time_launches(fn, n: int, warmup: int = 20) -> float:
+    """Average duration in microseconds of fn() over n launches, HIP events on the current stream,
+    after `warmup` untimed launches (each component starts after host-side input generation has
+    left the GPU idle, and its first launches run slower)."""
     import torch
 
     for _ in range(warmup):
