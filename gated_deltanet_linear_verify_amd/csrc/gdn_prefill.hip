@@ -1074,6 +1074,35 @@ __device__ __forceinline__ void load_n(const void *p, size_t off, float (&x)[N])
     }
 }
 
+// load_n with non-temporal loads, for data read once (the norm kernel's readout and z: 1.5 us of
+// the prefill's 397 at 8192 tokens)
+template <bool BF16, int N>
+__device__ __forceinline__ void load_n_nt(const void *p, size_t off, float (&x)[N])
+{
+    typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+    if constexpr (BF16) {
+        const uint16_t *q = static_cast<const uint16_t *>(p) + off;
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const u2v u = __builtin_nontemporal_load(reinterpret_cast<const u2v *>(q + e));
+            x[e] = bf16_to_f32((uint16_t)(u.x & 0xffffu));
+            x[e + 1] = bf16_to_f32((uint16_t)(u.x >> 16));
+            x[e + 2] = bf16_to_f32((uint16_t)(u.y & 0xffffu));
+            x[e + 3] = bf16_to_f32((uint16_t)(u.y >> 16));
+        }
+    } else {
+        const float *q = static_cast<const float *>(p) + off;
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(q + e));
+            x[e] = v[0];
+            x[e + 1] = v[1];
+            x[e + 2] = v[2];
+            x[e + 3] = v[3];
+        }
+    }
+}
+
 template <bool BF16, int N>
 __device__ __forceinline__ void store_n(void *p, size_t off, const float (&y)[N])
 {
@@ -1110,8 +1139,8 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillArgs a)
             const int row = row0 + 16 * k;
             if (row < nrows) {  // the same for the 16 lanes of a row
                 const size_t base = (size_t)row * D + cg * EPL;
-                load_n<false, EPL>(a.ws, base, ov[k]);  // the readout sits at the start of the workspace
-                load_n<ACT_BF16, EPL>(a.z, base, zv[k]);
+                load_n_nt<false, EPL>(a.ws, base, ov[k]);  // the readout sits at the start of the workspace
+                load_n_nt<ACT_BF16, EPL>(a.z, base, zv[k]);
             }
         }
         float nw[EPL];
