@@ -153,6 +153,48 @@ def test_prefill_in_pieces_equals_one_call():
     assert torch.equal(d["conv_state"], one["conv_state"])
 
 
+def test_prefill_more_scan_workgroups_than_cus():
+    """36 value heads: the scan's 288 workgroups (one per CU at most, by their LDS) exceed the CUs,
+    so some start only when others have finished; held to the same bar."""
+    shape = W.shape_with(W.CHUNKED_PREFILL, n_tok=100, n_kh=9, n_vh=36)
+    say("[prefill parity] 36 heads, 288 scan workgroups")
+    assert shape.n_vh * (shape.d_v // 16) > torch.cuda.get_device_properties(0).multi_processor_count
+    inp = W.make_inputs(shape, 0, weak_decay=True)
+    d = _run_prefill(shape, inp)
+    _check(shape, inp, d)
+
+
+def test_prefill_captured_in_a_graph_matches_eager():
+    """The prefill recorded under stream capture: every replay of the graph, with eager work and
+    synchronisation between replays, gives the eager call's output, state and conv state bit for
+    bit (the same kernels on the same inputs)."""
+    device, gdn = _mods()
+    shape = W.shape_with(W.CHUNKED_PREFILL, n_tok=200)
+    say("[prefill graph] 200 tokens, eager vs three replays")
+    inp = W.make_inputs(shape, 3, weak_decay=True)
+    d = device.upload(shape, inp, capture=False)
+    st0, cs0 = d["state"].clone(), d["conv_state"].clone()
+    device.prefill(d)
+    torch.cuda.synchronize()
+    _check(shape, inp, d)
+    ref = [d["out"].clone(), d["state"].clone(), d["conv_state"].clone()]
+    d["state"].copy_(st0)
+    d["conv_state"].copy_(cs0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        device.prefill(d)
+    for rep in range(3):
+        d["state"].copy_(st0)
+        d["conv_state"].copy_(cs0)
+        d["out"].fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "state", "conv_state"), (d["out"], d["state"], d["conv_state"]), ref):
+            assert torch.equal(got, want), (rep, name)
+
+
 def test_prefill_beta_zero_is_pure_decay():
     """beta = 0 and an identity conv (w = e_3): nothing is written, so S_t = exp(Gamma_t) S_0 and
     o_t = exp(Gamma_t) S_0 q_t with Gamma_t the running sum of g = -exp(A_log) softplus(alpha +
