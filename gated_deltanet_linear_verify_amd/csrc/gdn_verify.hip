@@ -269,31 +269,40 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
                 dst = ks + (lc - D);
             else
                 dst = vs + ((lc - 2 * D) / D) * TT * D + G::perm((lc - 2 * D) % D);
-            float x0 = csv[it][0], x1 = csv[it][1], x2 = csv[it][2];
+            // the window: the starting rows, then the launch's raw rows, every LDS read issued before
+            // any tap sum (rows past nt lie inside the staging area and are never used)
+            float x[TT + 3];
+            x[0] = csv[it][0];
+            x[1] = csv[it][1];
+            x[2] = csv[it][2];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) x[t + 3] = to_f32(raw[t * nch + lc]);
             const f4 w = wv[it];
             const bool own = lc >= 2 * D || own_qk;  // this workgroup writes the channel's rows
             float *cc = CAP ? a.cap_conv + (size_t)s * (3 + a.t_cap) * C + gc : nullptr;
             if (CAP && t0 == 0 && own) {  // the window starts with the conv state the call began from
-                cc[0] = x0;
-                cc[(size_t)C] = x1;
-                cc[(size_t)2 * C] = x2;
+                cc[0] = x[0];
+                cc[(size_t)C] = x[1];
+                cc[(size_t)2 * C] = x[2];
             }
-            for (int t = 0; t < nt; ++t) {
-                const float x3 = to_f32(raw[t * nch + lc]);
-                float y = conv4(w, x0, x1, x2, x3);
-                if constexpr (QKN) y = y * sigmoid_f(y);
-                dst[t * D] = y;
-                if (CAP && own) cc[(size_t)(t0 + t + 3) * C] = x3;
-                x0 = x1;
-                x1 = x2;
-                x2 = x3;
+            float e0 = x[0], e1 = x[1], e2 = x[2];  // window rows nt .. nt + 2: the conv state after the launch
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                if (t < nt) {
+                    float y = conv4(w, x[t], x[t + 1], x[t + 2], x[t + 3]);
+                    if constexpr (QKN) y = y * sigmoid_f(y);
+                    dst[t * D] = y;
+                    if (CAP && own) cc[(size_t)(t0 + t + 3) * C] = x[t + 3];
+                    e0 = x[t + 1];
+                    e1 = x[t + 2];
+                    e2 = x[t + 3];
+                }
             }
-            // conv state after the launch's last token (xext rows nt .. nt+2); this thread was the
-            // only reader of these elements
+            // this thread was the only reader of these elements
             if (commit && own) {
-                cs_s[gc] = x0;
-                cs_s[(size_t)C + gc] = x1;
-                cs_s[(size_t)2 * C + gc] = x2;
+                cs_s[gc] = e0;
+                cs_s[(size_t)C + gc] = e1;
+                cs_s[(size_t)2 * C + gc] = e2;
             }
         }
     }
