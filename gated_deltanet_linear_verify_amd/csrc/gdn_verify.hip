@@ -193,12 +193,14 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
         const int e0 = it * VEC, t = e0 / (HW * D), within = e0 % (HW * D);
         lds_dma16(z_b + (uint32_t)(t * a.n_vh * D + within), zs + e0);
     }
-    // alpha and beta: at most one (token, head) per thread, with the head's A_log and dt_bias.  The
-    // loads sit outside any branch (threads past nt * HW load a valid entry they never use) and
-    // nothing is computed from them before the wait below: a bf16 conversion, or a branch join
-    // over a loaded register, would make the compiler wait for every load issued so far, the qkv
-    // and z transfers included, before the state loads even start.
-    const int ab_i = min(tid, nt * HW - 1);
+    // alpha and beta: at most one (token, head) per thread of the last nt * HW threads (with one
+    // value head per workgroup their wave has no conv channel, so the gates overlap the conv), with
+    // the head's A_log and dt_bias.  The loads sit outside any branch (the other threads load a
+    // valid entry they never use) and nothing is computed from them before the wait below: a bf16
+    // conversion, or a branch join over a loaded register, would make the compiler wait for every
+    // load issued so far, the qkv and z transfers included, before the state loads even start.
+    const int gate_t0 = nthr - nt * HW;  // the first gate thread
+    const int ab_i = min(max(tid - gate_t0, 0), nt * HW - 1);
     const int ab_h = h0 + ab_i % HW;
     const size_t ab_tok = ((size_t)b * T + t0 + ab_i / HW) * a.n_vh + ab_h;
     using word_t = typename std::conditional<ACT_BF16, uint16_t, uint32_t>::type;  // bf16 or fp32 bits
@@ -248,13 +250,13 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
             return __builtin_bit_cast(float, w);
     };
     if (tid < D) nws[tid] = nw;
-    if (tid < nt * HW) {
-        const int t = tid / HW, hh = tid % HW;
+    __syncthreads();  // the staged rows of every wave have landed
+    if (tid >= gate_t0) {  // rho and beta per (token, head), read only after the conv's barrier
+        const int t = ab_i / HW, hh = ab_i % HW;
         const float g = -expf(alog) * softplus_f(word_f32(al_raw) + dtb);
         rb[(hh * TT + t) * 2 + 0] = expf(g);
         rb[(hh * TT + t) * 2 + 1] = word_f32(be_raw);
     }
-    __syncthreads();
 
     // ================= depthwise causal conv (one thread per channel) =================
 #pragma unroll
