@@ -287,18 +287,24 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
                 cc[(size_t)C] = x[1];
                 cc[(size_t)2 * C] = x[2];
             }
-            float e0 = x[0], e1 = x[1], e2 = x[2];  // window rows nt .. nt + 2: the conv state after the launch
+            // every row of the tile is convolved and written (rows past nt are never read)
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                if (t < nt) {
-                    float y = conv4(w, x[t], x[t + 1], x[t + 2], x[t + 3]);
-                    if constexpr (QKN) y = y * sigmoid_f(y);
-                    dst[t * D] = y;
-                    if (CAP && own) cc[(size_t)(t0 + t + 3) * C] = x[t + 3];
-                    e0 = x[t + 1];
-                    e1 = x[t + 2];
-                    e2 = x[t + 3];
-                }
+                float y = conv4(w, x[t], x[t + 1], x[t + 2], x[t + 3]);
+                if constexpr (QKN) y = y * sigmoid_f(y);
+                dst[t * D] = y;
+            }
+            if (CAP && own) {
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+                    if (t < nt) cc[(size_t)(t0 + t + 3) * C] = x[t + 3];
+            }
+            float e0 = x[0], e1 = x[1], e2 = x[2];  // window rows nt .. nt + 2: the conv state after the launch
+#pragma unroll
+            for (int t = 1; t <= TT; ++t) {
+                e0 = t == nt ? x[t] : e0;
+                e1 = t == nt ? x[t + 1] : e1;
+                e2 = t == nt ? x[t + 2] : e2;
             }
             // this thread was the only reader of these elements
             if (commit && own) {
