@@ -388,13 +388,26 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
         for (int n0 = 0; n0 < NT; n0 += CB) {
             const int codes = anc[min(n0 + (lane >> 2), NT - 1) * 4 + (lane & 3)];
             float x[CB][4];
+            // Past the first levels of a tree every ancestor of a batch's nodes is staged in this
+            // launch: then the rows are read straight, without X's selects (the same values).
+            if (__all((lane & 3) == 3 || codes >= base)) {
 #pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                const int n = min(n0 + j, NT - 1);
-                x[j][0] = X(__builtin_amdgcn_readlane(codes, 4 * j + 2), cs0, cs1, cs2);
-                x[j][1] = X(__builtin_amdgcn_readlane(codes, 4 * j + 1), cs0, cs1, cs2);
-                x[j][2] = X(__builtin_amdgcn_readlane(codes, 4 * j), cs0, cs1, cs2);
-                x[j][3] = to_f32(raw[n * NCH + lc]);
+                for (int j = 0; j < CB; ++j) {
+                    const int n = min(n0 + j, NT - 1);
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+                        x[j][i] = to_f32(raw[(__builtin_amdgcn_readlane(codes, 4 * j + 2 - i) - base) * NCH + lc]);
+                    x[j][3] = to_f32(raw[n * NCH + lc]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int n = min(n0 + j, NT - 1);
+                    x[j][0] = X(__builtin_amdgcn_readlane(codes, 4 * j + 2), cs0, cs1, cs2);
+                    x[j][1] = X(__builtin_amdgcn_readlane(codes, 4 * j + 1), cs0, cs1, cs2);
+                    x[j][2] = X(__builtin_amdgcn_readlane(codes, 4 * j), cs0, cs1, cs2);
+                    x[j][3] = to_f32(raw[n * NCH + lc]);
+                }
             }
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
