@@ -64,10 +64,9 @@ struct VerifyLds {
 // worked by 16 lanes: lane cg holds o at rows cg EPL .. cg EPL + EPL - 1 (ov), the matching z and
 // norm weights.  Shared by the fused epilogue and the row-split norm kernel, which therefore give
 // the same bits.
-template <bool ACT_BF16, bool OUT_BF16, int D>
-__device__ __forceinline__ void norm_gate_row(const float (&ov)[D / 16], const float *nwr,
-                                              const typename std::conditional<ACT_BF16, uint16_t, float>::type *zrow,
-                                              float eps, void *out, size_t base)
+template <bool OUT_BF16, int D>
+__device__ __forceinline__ void norm_gate_vals(const float (&ov)[D / 16], const float *nwr, const float (&zv)[D / 16],
+                                               float eps, void *out, size_t base)
 {
     constexpr int EPL = D / 16;
     float ss = 0.f;
@@ -77,17 +76,28 @@ __device__ __forceinline__ void norm_gate_row(const float (&ov)[D / 16], const f
     const float inv = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-        float zz;
-        if constexpr (ACT_BF16)
-            zz = bf16_to_f32(zrow[e]);
-        else
-            zz = zrow[e];
+        const float zz = zv[e];
         const float y = ov[e] * inv * nwr[e] * (zz * sigmoid_f(zz));
         if constexpr (OUT_BF16)
             static_cast<uint16_t *>(out)[base + e] = f32_to_bf16(y);
         else
             static_cast<float *>(out)[base + e] = y;
     }
+}
+template <bool ACT_BF16, bool OUT_BF16, int D>
+__device__ __forceinline__ void norm_gate_row(const float (&ov)[D / 16], const float *nwr,
+                                              const typename std::conditional<ACT_BF16, uint16_t, float>::type *zrow,
+                                              float eps, void *out, size_t base)
+{
+    float zv[D / 16];
+#pragma unroll
+    for (int e = 0; e < D / 16; ++e) {
+        if constexpr (ACT_BF16)
+            zv[e] = bf16_to_f32(zrow[e]);
+        else
+            zv[e] = zrow[e];
+    }
+    norm_gate_vals<OUT_BF16, D>(ov, nwr, zv, eps, out, base);
 }
 
 // Row split (SPLIT): kRowSplit workgroups per value head, each with NW waves that hold its share of
@@ -98,6 +108,13 @@ __device__ __forceinline__ void norm_gate_row(const float (&ov)[D / 16], const f
 // contraction, which one CU's vector units take ~1000 clocks for at d = 128: splitting the rows
 // over CUs is what shortens the token chain when few heads are in flight.
 constexpr int kRowSplit = 4;
+
+// The row split's scratch: its readout [n_batch][16][H_v][d], then the q / k channels' starting rows
+// (the three conv rows a launch begins from) [n_batch][3][2 H_k d].
+__device__ __forceinline__ float *split_qk_rows(const VerifyArgs &a, int b)
+{
+    return a.oscr + (size_t)a.n_batch * kTokenTile * a.n_vh * a.d + (size_t)b * 3 * 2 * a.n_kh * a.d;
+}
 
 // NW: waves per value head (4 at d = 128 with all of a key head's value heads in the workgroup,
 // 8 with one value head per workgroup: half the rows per lane, the same arithmetic per row), or
@@ -243,6 +260,15 @@ __global__ __launch_bounds__(1024) void verify_chain_kernel(VerifyArgs a)
     float nw = a.norm_w[min(tid, D - 1)];
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): registers loaded, LDS rows landed
     asm volatile("" : "+v"(al_raw), "+v"(be_raw), "+v"(alog), "+v"(dtb), "+v"(nw));  // nothing above
+    if constexpr (SPLIT) {
+        // the key head's q / k starting rows, for the kernel after the launch (split_qk_rows): written
+        // by one workgroup of the key head, indexed by batch entry so that it reads them unconditionally
+        if (rj == 0 && h % R == 0 && tid < 2 * D) {
+            float *qk = split_qk_rows(a, b) + gchan(tid);
+#pragma unroll
+            for (int r = 0; r < 3; ++r) qk[(size_t)r * 2 * a.n_kh * D] = csv[0][r];
+        }
+    }
     auto word_f32 = [](uint32_t w) -> float {
         if constexpr (ACT_BF16)
             return bf16_to_f32((uint16_t)w);
@@ -399,10 +425,25 @@ size_t verify_chain_lds_bytes(int d, int ratio, bool act_bf16)
 // deferred).  The launch's conv input is its starting rows (the slot's conv state, or the capture
 // window rows it resumes from, chosen as in the verify kernel) followed by its tokens.  Every read
 // of a channel precedes its writes, and all of them are issued before the first is used.
-template <bool ACT_BF16, bool CAP>
+// STASH (after a row split): the starting rows come from split_qk_rows, written by the launch, and
+// every load is issued before the batch entry's slot is known, so the kernel waits for memory once.
+template <bool ACT_BF16, bool CAP, bool STASH = false>
 __device__ __forceinline__ void qk_conv_channel(const VerifyArgs &a, int b, int ch)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
+    if (ch >= 2 * a.n_kh * a.d) return;  // q | k channels are 0 .. 2 H_k d - 1
+    const size_t C = (size_t)a.C;
+    const int t0 = a.t0, nt = a.nt;
+    const act_t *x = static_cast<const act_t *>(a.qkv) + ((size_t)b * a.T + t0) * C + ch;
+    float xs[3 + kTokenTile];
+    act_t tok[kTokenTile];
+    if constexpr (STASH) {
+        const float *st = split_qk_rows(a, b) + ch;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) xs[r] = st[(size_t)r * 2 * a.n_kh * a.d];
+#pragma unroll
+        for (int t = 0; t < kTokenTile; ++t) tok[t] = x[(size_t)(t < nt ? t : nt - 1) * C];  // valid rows only
+    }
     const int s = a.slot_ids[b];
     if (s < 0 || s >= a.n_pool) return;  // uniform over the block, as in the verify kernel
     int ra = -1;
@@ -415,19 +456,15 @@ __device__ __forceinline__ void qk_conv_channel(const VerifyArgs &a, int b, int 
         if (a.defer && a.t0 > 0) ra = a.t0 - 1;
     }
     const bool commit = !(CAP && a.defer);
-    if (ch >= 2 * a.n_kh * a.d) return;  // q | k channels are 0 .. 2 H_k d - 1
-    const size_t C = (size_t)a.C;
-    const int t0 = a.t0, nt = a.nt;
     float *cs = a.conv_state + (size_t)s * 3 * C + ch;
     float *cw = CAP ? a.cap_conv + (size_t)s * (3 + a.t_cap) * C + ch : nullptr;
-    const float *src = ra >= 0 ? cw + (size_t)(ra + 1) * C : cs;
-    const act_t *x = static_cast<const act_t *>(a.qkv) + ((size_t)b * a.T + t0) * C + ch;
-    float xs[3 + kTokenTile];
-    act_t tok[kTokenTile];
+    if constexpr (!STASH) {
+        const float *src = ra >= 0 ? cw + (size_t)(ra + 1) * C : cs;
 #pragma unroll
-    for (int r = 0; r < 3; ++r) xs[r] = src[(size_t)r * C];
+        for (int r = 0; r < 3; ++r) xs[r] = src[(size_t)r * C];
 #pragma unroll
-    for (int t = 0; t < kTokenTile; ++t) tok[t] = x[(size_t)(t < nt ? t : nt - 1) * C];  // valid rows only
+        for (int t = 0; t < kTokenTile; ++t) tok[t] = x[(size_t)(t < nt ? t : nt - 1) * C];  // valid rows only
+    }
 #pragma unroll
     for (int t = 0; t < kTokenTile; ++t) {
         if constexpr (ACT_BF16)
@@ -464,25 +501,31 @@ __global__ __launch_bounds__(256) void verify_norm_kernel(VerifyArgs a)
     const int conv_blocks = (2 * a.n_kh * D + 255) / 256;
     const int nconv = conv_blocks * a.n_batch;
     if ((int)blockIdx.x < nconv) {
-        qk_conv_channel<ACT_BF16, CAP>(a, blockIdx.x / conv_blocks, (blockIdx.x % conv_blocks) * 256 + threadIdx.x);
+        qk_conv_channel<ACT_BF16, CAP, true>(a, blockIdx.x / conv_blocks, (blockIdx.x % conv_blocks) * 256 + threadIdx.x);
         return;
     }
     // every lane of a 16-lane group takes the same row, so the returns below are uniform per group
     const int row = ((int)blockIdx.x - nconv) * 16 + (int)(threadIdx.x >> 4), cg = threadIdx.x & 15;
     if (row >= a.n_batch * a.nt * a.n_vh) return;
     const int h = row % a.n_vh, t = (row / a.n_vh) % a.nt, b = row / (a.n_vh * a.nt);
-    const int s = a.slot_ids[b];
-    if (s < 0 || s >= a.n_pool) return;  // skipped by the verify kernel too
-    if (CAP && a.resume && a.resume[b] >= a.t_cap) return;
+    // everything the row needs is indexed by batch entry: loaded before its slot is checked
     const float *o = a.oscr + (((size_t)b * kTokenTile + t) * a.n_vh + h) * D + cg * EPL;
-    float ov[EPL], nwr[EPL];
+    const size_t base = (((size_t)b * a.T + a.t0 + t) * a.n_vh + h) * D + cg * EPL;
+    const act_t *zrow = static_cast<const act_t *>(a.z) + base;
+    float ov[EPL], nwr[EPL], zv[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
         ov[e] = o[e];
         nwr[e] = a.norm_w[cg * EPL + e];
+        if constexpr (ACT_BF16)
+            zv[e] = bf16_to_f32(zrow[e]);
+        else
+            zv[e] = zrow[e];
     }
-    const size_t base = (((size_t)b * a.T + a.t0 + t) * a.n_vh + h) * D + cg * EPL;
-    norm_gate_row<ACT_BF16, OUT_BF16, D>(ov, nwr, static_cast<const act_t *>(a.z) + base, a.eps, a.out, base);
+    const int s = a.slot_ids[b];
+    if (s < 0 || s >= a.n_pool) return;  // skipped by the verify kernel too
+    if (CAP && a.resume && a.resume[b] >= a.t_cap) return;
+    norm_gate_vals<OUT_BF16, D>(ov, nwr, zv, a.eps, a.out, base);
 }
 
 // Value heads per workgroup.  With few batch entries a workgroup per key head leaves most CUs idle
@@ -505,7 +548,7 @@ constexpr int kCus = 256;
 static bool row_split(const VerifyArgs &a)
 {
     if (a.T < kSplitMinTokens || (long)a.n_batch * a.n_vh * kRowSplit > kCus) return false;
-    return (size_t)a.n_batch * kTokenTile * a.n_vh * a.d * sizeof(float) <= kSplitScratchBytes;
+    return (size_t)a.n_batch * (kTokenTile * a.n_vh + 3 * 2 * a.n_kh) * a.d * sizeof(float) <= kSplitScratchBytes;
 }
 
 // One launch covers at most kTokenTile tokens; longer chains are consecutive launches on the same
