@@ -182,6 +182,116 @@ __global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
     }
 }
 
+// At most 16 rows (one slot's drafted tokens) and a narrow product: the product is a stream of the
+// weight, read once, and the 32 x 64 tiles leave most CUs idle (N = 5120: 80 workgroups).  Here a
+// workgroup takes 16 output columns (N / 16 workgroups), its four waves a quarter of the 32-deep k
+// steps each, and each wave keeps the fragments of kPF steps in flight while it multiplies the
+// previous ones.  No LDS staging: a lane loads its own 16-byte x and W fragments.  The waves'
+// partial 16 x 16 tiles are summed in wave order through LDS, and the sums go through the same
+// epilogue as the tiled kernel.
+constexpr int kSkinnyWaves = 4;
+constexpr int kPF = 4;  // k steps of fragments in flight per wave
+
+template <int MT>  // 16-row tiles of x (M <= 16 MT; launched with MT = 1)
+__global__ __launch_bounds__(64 * kSkinnyWaves) void linear_skinny_kernel(LinearArgs a)
+{
+    __shared__ f4 part[kSkinnyWaves - 1][MT][64];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int K = a.K;
+    // columns n0 .. n0 + 15; workgroups are dealt to the 8 XCDs in turn, each XCD taking a
+    // contiguous column range (x, read by every workgroup, then sits once in each XCD's L2)
+    const int ntiles = gridDim.x, xcd = blockIdx.x % 8, q8 = ntiles / 8, r8 = ntiles % 8;
+    const int n0 = 16 * (xcd * q8 + min(xcd, r8) + (int)blockIdx.x / 8);
+    // this lane's fragment sources: x row m (rows past M re-read the last one), W row n0 + li
+    // (past N the last one); chunk lg of every 32-deep step
+    const bf16x8_t *xs[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+        xs[i] = reinterpret_cast<const bf16x8_t *>(a.x + (size_t)min(16 * i + li, a.M - 1) * K + 8 * lg);
+    const bf16x8_t *ws = reinterpret_cast<const bf16x8_t *>(a.w + (size_t)min(n0 + li, a.N - 1) * K + 8 * lg);
+    const int steps = K / 32;
+    const int s0 = wave * steps / kSkinnyWaves, mine = (wave + 1) * steps / kSkinnyWaves - s0;
+    const int groups = (mine + kPF - 1) / kPF;
+    f4 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+    // step j of this wave is global step wave + 4 j: 16-byte element offset 4 (wave + 4 j); steps
+    // past the wave's count (a wave may have none) load the last step of the row, which is valid,
+    // and are not multiplied
+    auto at = [&](int j) { return 4 * min(s0 + j, steps - 1); };
+    bf16x8_t xa[kPF][MT], wa[kPF];
+#pragma unroll
+    for (int u = 0; u < kPF; ++u) {
+        wa[u] = ws[at(u)];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) xa[u][i] = xs[i][at(u)];
+    }
+#pragma unroll 1
+    for (int g = 0; g < groups; ++g) {
+        bf16x8_t xn[kPF][MT], wn[kPF];
+        const int j1 = (g + 1) * kPF;
+#pragma unroll
+        for (int u = 0; u < kPF; ++u) {  // the next group travels while this one is multiplied
+            wn[u] = ws[at(j1 + u)];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xn[u][i] = xs[i][at(j1 + u)];
+        }
+#pragma unroll
+        for (int u = 0; u < kPF; ++u)
+            if (g * kPF + u < mine)  // uniform over the wave
+#pragma unroll
+                for (int i = 0; i < MT; ++i) acc[i] = mfma_bf16(xa[u][i], wa[u], acc[i]);
+#pragma unroll
+        for (int u = 0; u < kPF; ++u) {
+            wa[u] = wn[u];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xa[u][i] = xn[u][i];
+        }
+    }
+    // the waves' partial tiles, summed in wave order by wave 0
+    if (wave > 0)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) part[wave - 1][i][lane] = acc[i];
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves - 1; ++w)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i] += part[w][i][lane];
+    // ---- epilogue: element (row 4 lg + r, column li) of each 16 x 16 tile to its segment
+    const int n = n0 + li;
+    if (n >= a.N) return;
+    int sgi = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxLinearSegs; ++q)
+        if (q < a.n_segs && n >= a.seg[q].n0) sgi = q;
+    const LinearSeg &sg = a.seg[sgi];
+    const int nc = n - sg.n0;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * i + 4 * lg + r;
+            if (m >= a.M) continue;
+            float v = acc[i][r];
+            if (sg.sigmoid) v = 1.0f / (1.0f + expf(-v));
+            const size_t o = (size_t)m * sg.ld + nc;
+            if (sg.bf16)
+                static_cast<uint16_t *>(sg.ptr)[o] = f32_to_bf16(v);
+            else
+                static_cast<float *>(sg.ptr)[o] = v;
+        }
+}
+
+template <int MT>
+static hipError_t launch_skinny(const LinearArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((linear_skinny_kernel<MT>), dim3((unsigned)((a.N + 15) / 16)), dim3(64 * kSkinnyWaves), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
 template <int GM, int GN, int WM, int WN>
 static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
 {
@@ -202,6 +312,10 @@ static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
 // workgroups.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t stream)
 {
+    // At most 16 rows: 16-column workgroups when the 32 x 64 tiles would not give each CU of
+    // three quarters of the chip one (16 x 4096 -> 5120: 19 us against 31 us; 16 x 5120 -> 12352,
+    // 193 tiles: the tiles, 40 us against 42 us).
+    if (a.M <= 16 && (a.N + 63) / 64 < 192) return launch_skinny<1>(a, stream);
     if (a.M <= 64) return launch_tile<2, 2, 1, 2>(a, stream);
     const long big = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (big >= 192) return launch_tile<4, 4, 4, 4>(a, stream);

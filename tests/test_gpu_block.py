@@ -41,7 +41,11 @@ def _bf16_err(gpu, ref_):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (200, 300, 256), (128, 128, 64), (257, 129, 320), (64, 4160, 512),
-                                   (1100, 10000, 320)])
+                                   (1100, 10000, 320),
+                                   # at most 16 rows and a narrow product: 16-column workgroups, the k
+                                   # steps split over four waves (unevenly at K = 192; two idle at 64);
+                                   # 16 x 12352 has enough 32 x 64 tiles and takes them
+                                   (7, 1000, 192), (16, 17, 128), (16, 5120, 4096), (16, 12352, 512)])
 def test_linear_fp32_out(M, N, K):
     """Ragged M and N (partial tiles, a single element), several K tiles; the last shape has enough
     256 x 256 tiles (5 x 40) to take that tiling, with partial tiles along both M and N."""
@@ -54,11 +58,13 @@ def test_linear_fp32_out(M, N, K):
     assert rel_err(to_np(y), block.linear(x, w)) < TOL_F32
 
 
-def test_linear_segments_sigmoid_strides_and_types():
+@pytest.mark.parametrize("M", [70, 12])
+def test_linear_segments_sigmoid_strides_and_types(M):
     """Four segments (bf16, bf16 with a row stride wider than the segment, sigmoid fp32, fp32):
-    each holds its columns of the product; the padding between rows stays untouched."""
+    each holds its columns of the product; the padding between rows stays untouched.  At 12 rows
+    the product runs on 16-column workgroups."""
     from gated_deltanet_linear_verify_amd import gdn
-    M, K = 70, 192
+    K = 192
     widths = [128, 100, 32, 37]
     N = sum(widths)
     x, w = _operands(M, N, K, seed=9)
