@@ -10,9 +10,10 @@
 // the concatenated weight.
 //
 // Tiling: a workgroup computes a block of y with a grid of waves, each a grid of 16 x 16 tiles of
-// v_mfma_f32_16x16x32_bf16 (256 x 256 or 128 x 128 blocks for many rows, 32 x 64 for few).  K
-// advances 64 at a time, one barrier per step: the next x and W tiles travel into the other half
-// of a double-buffered LDS by global_load_lds while the current ones are multiplied.  Within an
+// v_mfma_f32_16x16x32_bf16 (256 x 256 or 128 x 128 blocks for many rows, 16 x 16 to 32 x 64 for
+// few).  K advances 64 at a time, one barrier per step: the next x and W tiles travel into a
+// buffer of the LDS (two, or four for few rows) by global_load_lds while the current ones are
+// multiplied.  Within an
 // LDS tile row (64 bf16 = 8 chunks of 16 bytes) chunk c of row r sits at position c ^ (r & 7),
 // so the 16 rows an operand load touches spread over the banks; the DMA writes LDS linearly, so
 // the swizzle is applied by choosing the global chunk each lane fetches.
@@ -24,6 +25,10 @@ namespace gdn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kLBK = 64;  // k depth of a tile
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding (vmcnt bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
 constexpr int kLChunks = kLBK / 8;  // 16-byte chunks per tile row
 
 __device__ __forceinline__ f4 mfma_bf16(bf16x8_t a, bf16x8_t b, f4 c)
@@ -47,21 +52,39 @@ __device__ __forceinline__ int lchunk(int r, int c) { return (r * kLChunks + (c 
 
 // Workgroup tile (16 WM GM) x (16 WN GN): GM x GN waves, each (16 WM) x (16 WN) = WM x WN MFMA
 // tiles.
-template <int GM, int GN, int WM, int WN>
+template <int GM, int GN, int WM, int WN, int NBUF = 2>
 struct LinTile {
     static constexpr int THREADS = 64 * GM * GN;
     static constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
     static constexpr int XT = BM * kLChunks / THREADS;  // x transfers per thread and k tile
     static constexpr int WT = BN * kLChunks / THREADS;  // W transfers per thread and k tile
-    static constexpr size_t lds = 2 * (size_t)(BM + BN) * kLBK * 2;  // two buffers of x and W tiles
-    static_assert(XT >= 1 && WT >= 1 && XT + WT < 64, "tile transfer counts");
+    static constexpr size_t lds = NBUF * (size_t)(BM + BN) * kLBK * 2;  // NBUF buffers of x and W tiles
+    static_assert(XT >= 1 && WT >= 1 && (NBUF - 1) * (XT + WT) < 64, "tile transfer counts");
     static_assert(BM * kLChunks % THREADS == 0 && BN * kLChunks % THREADS == 0, "even transfers");
 };
 
-template <int GM, int GN, int WM, int WN>
+// Wait until at most `later` k tiles of TPT transfers each are in flight (s_waitcnt takes an
+// immediate, so one instruction per count; later <= MAXL).
+template <int TPT, int MAXL>
+__device__ __forceinline__ void wait_tiles(int later)
+{
+    static_assert(MAXL <= 6 && MAXL * TPT < 64, "vmcnt range");
+    switch (MAXL > 0 ? later : 0) {
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * TPT)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * TPT)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * TPT)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * TPT)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * TPT)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(TPT)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    }
+}
+
+// NBUF k tiles are buffered: NBUF - 1 of them travel while one is multiplied.
+template <int GM, int GN, int WM, int WN, int NBUF>
 __global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
 {
-    using TL = LinTile<GM, GN, WM, WN>;
+    using TL = LinTile<GM, GN, WM, WN, NBUF>;
     constexpr int BM = TL::BM, BN = TL::BN, kLThreads = TL::THREADS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [buffer][x tile | W tile]
     constexpr int XB = BM * kLBK * 2, BUF = (BM + BN) * kLBK * 2;
@@ -107,15 +130,20 @@ __global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
         for (int j = 0; j < WN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / kLBK;
-    issue(0, 0);
+#pragma unroll
+    for (int p = 0; p < NBUF - 1; ++p)
+        if (p < nk) issue(p, p);
+    constexpr int TPT = TL::XT + TL::WT;  // transfers per thread and k tile
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's transfers of tile kt have landed
+        const int buf = kt % NBUF;
+        // this thread's transfers of tile kt have landed; those of the (up to NBUF - 2) later tiles
+        // already issued may travel
+        wait_tiles<TPT, NBUF - 2>(min(nk - 1 - kt, NBUF - 2));
         // Every wave's transfers of tile kt have landed, and every wave is done with tile kt - 1,
-        // so the other buffer takes tile kt + 1: one barrier per k tile.
+        // so its buffer takes tile kt + NBUF - 1: one barrier per k tile.
         lds_barrier();
-        if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+        if (kt + NBUF - 1 < nk) issue(kt + NBUF - 1, (kt + NBUF - 1) % NBUF);
         const unsigned char *xs = lds + buf * BUF, *ws = xs + XB;
         // every fragment of the tile's 32-deep steps is read before the first product, so the later
         // steps' reads are in flight while the earlier steps' products run
@@ -182,123 +210,13 @@ __global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
     }
 }
 
-// At most 16 rows (one slot's drafted tokens) and a narrow product: the product is a stream of the
-// weight, read once, and the 32 x 64 tiles leave most CUs idle (N = 5120: 80 workgroups).  Here a
-// workgroup takes 16 output columns (N / 16 workgroups), its four waves a quarter of the 32-deep k
-// steps each, and each wave keeps the fragments of kPF steps in flight while it multiplies the
-// previous ones.  No LDS staging: a lane loads its own 16-byte x and W fragments.  The waves'
-// partial 16 x 16 tiles are summed in wave order through LDS, and the sums go through the same
-// epilogue as the tiled kernel.
-constexpr int kSkinnyWaves = 4;
-constexpr int kPF = 4;  // k steps of fragments in flight per wave
-
-template <int MT>  // 16-row tiles of x (M <= 16 MT; launched with MT = 1)
-__global__ __launch_bounds__(64 * kSkinnyWaves) void linear_skinny_kernel(LinearArgs a)
-{
-    __shared__ f4 part[kSkinnyWaves - 1][MT][64];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 15, lg = lane >> 4;
-    const int K = a.K;
-    // columns n0 .. n0 + 15; workgroups are dealt to the 8 XCDs in turn, each XCD taking a
-    // contiguous column range (x, read by every workgroup, then sits once in each XCD's L2)
-    const int ntiles = gridDim.x, xcd = blockIdx.x % 8, q8 = ntiles / 8, r8 = ntiles % 8;
-    const int n0 = 16 * (xcd * q8 + min(xcd, r8) + (int)blockIdx.x / 8);
-    // this lane's fragment sources: x row m (rows past M re-read the last one), W row n0 + li
-    // (past N the last one); chunk lg of every 32-deep step
-    const bf16x8_t *xs[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-        xs[i] = reinterpret_cast<const bf16x8_t *>(a.x + (size_t)min(16 * i + li, a.M - 1) * K + 8 * lg);
-    const bf16x8_t *ws = reinterpret_cast<const bf16x8_t *>(a.w + (size_t)min(n0 + li, a.N - 1) * K + 8 * lg);
-    const int steps = K / 32;
-    const int s0 = wave * steps / kSkinnyWaves, mine = (wave + 1) * steps / kSkinnyWaves - s0;
-    const int groups = (mine + kPF - 1) / kPF;
-    f4 acc[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-    // step j of this wave is global step wave + 4 j: 16-byte element offset 4 (wave + 4 j); steps
-    // past the wave's count (a wave may have none) load the last step of the row, which is valid,
-    // and are not multiplied
-    auto at = [&](int j) { return 4 * min(s0 + j, steps - 1); };
-    bf16x8_t xa[kPF][MT], wa[kPF];
-#pragma unroll
-    for (int u = 0; u < kPF; ++u) {
-        wa[u] = ws[at(u)];
-#pragma unroll
-        for (int i = 0; i < MT; ++i) xa[u][i] = xs[i][at(u)];
-    }
-#pragma unroll 1
-    for (int g = 0; g < groups; ++g) {
-        bf16x8_t xn[kPF][MT], wn[kPF];
-        const int j1 = (g + 1) * kPF;
-#pragma unroll
-        for (int u = 0; u < kPF; ++u) {  // the next group travels while this one is multiplied
-            wn[u] = ws[at(j1 + u)];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) xn[u][i] = xs[i][at(j1 + u)];
-        }
-#pragma unroll
-        for (int u = 0; u < kPF; ++u)
-            if (g * kPF + u < mine)  // uniform over the wave
-#pragma unroll
-                for (int i = 0; i < MT; ++i) acc[i] = mfma_bf16(xa[u][i], wa[u], acc[i]);
-#pragma unroll
-        for (int u = 0; u < kPF; ++u) {
-            wa[u] = wn[u];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) xa[u][i] = xn[u][i];
-        }
-    }
-    // the waves' partial tiles, summed in wave order by wave 0
-    if (wave > 0)
-#pragma unroll
-        for (int i = 0; i < MT; ++i) part[wave - 1][i][lane] = acc[i];
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 0; w < kSkinnyWaves - 1; ++w)
-#pragma unroll
-        for (int i = 0; i < MT; ++i) acc[i] += part[w][i][lane];
-    // ---- epilogue: element (row 4 lg + r, column li) of each 16 x 16 tile to its segment
-    const int n = n0 + li;
-    if (n >= a.N) return;
-    int sgi = 0;
-#pragma unroll
-    for (int q = 1; q < kMaxLinearSegs; ++q)
-        if (q < a.n_segs && n >= a.seg[q].n0) sgi = q;
-    const LinearSeg &sg = a.seg[sgi];
-    const int nc = n - sg.n0;
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 16 * i + 4 * lg + r;
-            if (m >= a.M) continue;
-            float v = acc[i][r];
-            if (sg.sigmoid) v = 1.0f / (1.0f + expf(-v));
-            const size_t o = (size_t)m * sg.ld + nc;
-            if (sg.bf16)
-                static_cast<uint16_t *>(sg.ptr)[o] = f32_to_bf16(v);
-            else
-                static_cast<float *>(sg.ptr)[o] = v;
-        }
-}
-
-template <int MT>
-static hipError_t launch_skinny(const LinearArgs &a, hipStream_t stream)
-{
-    hipLaunchKernelGGL((linear_skinny_kernel<MT>), dim3((unsigned)((a.N + 15) / 16)), dim3(64 * kSkinnyWaves), 0,
-                       stream, a);
-    return hipGetLastError();
-}
-
-template <int GM, int GN, int WM, int WN>
+template <int GM, int GN, int WM, int WN, int NBUF = 2>
 static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
 {
-    using TL = LinTile<GM, GN, WM, WN>;
+    using TL = LinTile<GM, GN, WM, WN, NBUF>;
     const unsigned tiles = (unsigned)((a.N + TL::BN - 1) / TL::BN) * (unsigned)((a.M + TL::BM - 1) / TL::BM);
     const dim3 grid(tiles);
-    hipLaunchKernelGGL((linear_kernel<GM, GN, WM, WN>), grid, dim3(TL::THREADS), TL::lds, stream, a);
+    hipLaunchKernelGGL((linear_kernel<GM, GN, WM, WN, NBUF>), grid, dim3(TL::THREADS), TL::lds, stream, a);
     return hipGetLastError();
 }
 
@@ -307,16 +225,17 @@ static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
 // per CU) is the fastest per CU, and is taken when its tiles fill at least three quarters of the
 // 256 CUs (1024 x 5120 -> 12352: 196 tiles, 134 us against 162 us with 128 x 128).  Otherwise
 // 128 x 128 tiles of 16 waves of 32 x 32, two workgroups per CU, spread a smaller product over
-// every CU (1024 x 4096 -> 5120: 320 tiles, 56 us against 106 us with 80 of 256 x 256); a few rows
-// (one slot's drafted tokens) take 32 x 64 tiles, so the weight stream is spread over enough
-// workgroups.
+// every CU (1024 x 4096 -> 5120: 320 tiles, 56 us against 106 us with 80 of 256 x 256).  A few rows
+// (one slot's drafted tokens) make the product a stream of the weight, read once: one-wave tiles
+// 16 (M <= 16) or 32 (M <= 32) rows by 16 columns spread it over N / 16 workgroups, and four
+// buffered k tiles keep three in flight per workgroup (16 x 5120 -> 12352: 20 us, 6.2 TB/s of
+// weight, against 40 us with double-buffered 32 x 64 tiles; 16 x 4096 -> 5120: 14.5 against
+// 31 us).  Up to 64 rows, four-buffered 32 x 64 tiles (64 x 4096 -> 5120: 21 against 32 us).
 hipError_t launch_linear(const LinearArgs &a, hipStream_t stream)
 {
-    // At most 16 rows: 16-column workgroups when the 32 x 64 tiles would not give each CU of
-    // three quarters of the chip one (16 x 4096 -> 5120: 19 us against 31 us; 16 x 5120 -> 12352,
-    // 193 tiles: the tiles, 40 us against 42 us).
-    if (a.M <= 16 && (a.N + 63) / 64 < 192) return launch_skinny<1>(a, stream);
-    if (a.M <= 64) return launch_tile<2, 2, 1, 2>(a, stream);
+    if (a.M <= 16) return launch_tile<1, 1, 1, 1, 4>(a, stream);
+    if (a.M <= 32) return launch_tile<1, 1, 2, 1, 4>(a, stream);
+    if (a.M <= 64) return launch_tile<2, 2, 1, 2, 4>(a, stream);
     const long big = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (big >= 192) return launch_tile<4, 4, 4, 4>(a, stream);
     return launch_tile<4, 4, 2, 2>(a, stream);

@@ -42,10 +42,10 @@ def _bf16_err(gpu, ref_):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (200, 300, 256), (128, 128, 64), (257, 129, 320), (64, 4160, 512),
                                    (1100, 10000, 320),
-                                   # at most 16 rows and a narrow product: 16-column workgroups, the k
-                                   # steps split over four waves (unevenly at K = 192; two idle at 64);
-                                   # 16 x 12352 has enough 32 x 64 tiles and takes them
-                                   (7, 1000, 192), (16, 17, 128), (16, 5120, 4096), (16, 12352, 512)])
+                                   # few rows: one-wave 16 x 16 or 32 x 16 tiles, four buffered k
+                                   # tiles (one k tile at K = 64, three at 192)
+                                   (7, 1000, 192), (16, 17, 128), (16, 5120, 4096), (16, 12352, 512),
+                                   (24, 700, 320), (48, 5120, 4096)])
 def test_linear_fp32_out(M, N, K):
     """Ragged M and N (partial tiles, a single element), several K tiles; the last shape has enough
     256 x 256 tiles (5 x 40) to take that tiling, with partial tiles along both M and N."""
@@ -61,8 +61,8 @@ def test_linear_fp32_out(M, N, K):
 @pytest.mark.parametrize("M", [70, 12])
 def test_linear_segments_sigmoid_strides_and_types(M):
     """Four segments (bf16, bf16 with a row stride wider than the segment, sigmoid fp32, fp32):
-    each holds its columns of the product; the padding between rows stays untouched.  At 12 rows
-    the product runs on 16-column workgroups."""
+    each holds its columns of the product; the padding between rows stays untouched (at 70 rows on
+    32 x 64 tiles, at 12 on 16 x 16)."""
     from gated_deltanet_linear_verify_amd import gdn
     K = 192
     widths = [128, 100, 32, 37]
