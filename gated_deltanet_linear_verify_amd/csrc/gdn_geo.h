@@ -68,8 +68,8 @@ struct Geo {
         kq = row16_sum(kq);
         float sk = 1.f;  // scale of the raw k row in the update
         if constexpr (QKN) {
-            sk = 1.0f / sqrtf(row16_sum(nk) + 1e-6f);
-            const float sq = 1.0f / sqrtf(row16_sum(nq) + 1e-6f) / sqrtf((float)D);
+            sk = rsqrt_f(row16_sum(nk) + 1e-6f);
+            const float sq = rsqrt_f(row16_sum(nq) + 1e-6f) * (1.0f / sqrtf((float)D));
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 pk[i] *= sk;

@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
                 ss = row16_sum(ss);
                 if constexpr (D == 128) ss += __shfl_xor(ss, 16);
-                const float sc = 1.0f / sqrtf(ss + 1e-6f) / (isq ? sqrtf((float)D) : 1.0f);
+                const float sc = rsqrt_f(ss + 1e-6f) * (isq ? 1.0f / sqrtf((float)D) : 1.0f);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) y[j] *= sc;
             }
