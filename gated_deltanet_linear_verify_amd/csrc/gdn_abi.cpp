@@ -415,6 +415,8 @@ GDN_API int gdn_rollback_layers(const gdn_capture *layers, int32_t n_layers, con
 GDN_API int gdn_rollback_trim(const gdn_capture *capture, int32_t slot, int32_t trim, int32_t n_tok, void *stream)
 {
     if (int r = check_rollback_capture(capture)) return r;
+    if (capture->mode != GDN_CHAIN)  // tree node indices are not positions along one path
+        return fail(GDN_ERR_ARG, "gdn_rollback_trim: the trim form needs a GDN_CHAIN capture");
     if (n_tok < 1 || n_tok > capture->t_cap)
         return fail(GDN_ERR_RANGE, "gdn_rollback_trim: n_tok %d outside [1, t_cap = %d]", n_tok, capture->t_cap);
     if (trim < 0) return fail(GDN_ERR_RANGE, "gdn_rollback_trim: negative trim %d", trim);

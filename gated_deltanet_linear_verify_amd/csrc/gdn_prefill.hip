@@ -17,13 +17,15 @@
 // Everything that does not depend on S (conv, gates, A -> T, P) is the same for every value-row
 // block and every chunk can compute it at once, so it runs first, chunk-parallel; only Y, U, O
 // and S' remain on the sequential chain of chunks.
-// Kernel 1 (prep): one workgroup per (chunk, value head): conv of the chunk's q | k | v channels,
-// the gates, A and P on MFMA, T by blocked fp32 forward substitution.  It writes the operands of
-// the scan to the workspace as LDS images (the layouts the scan reads), so the scan copies them
-// with flat global_load_lds transfers.
+// Kernel 1 (prep): one workgroup per (chunk, key head): conv of the chunk's q | k channels and the
+// Gram products K K^T and Q K^T on MFMA, shared by the key head's value heads; then per value head
+// the gates, A and P, and T by blocked fp32 forward substitution.  It writes the operands of the
+// scan to the workspace as LDS images (the layouts the scan reads), so the scan copies them with
+// flat global_load_lds transfers.
 // Kernel 2 (scan): one workgroup per (value head, block of 16 value rows).  Rows of S are
-// independent given the keys, so the blocks never communicate; each walks the chunks in order with
-// its S block in LDS while the next chunk's operands travel in.  Dense products run on
+// independent given the keys, so the blocks never communicate; each walks the chunks in order,
+// convolving its own v channels and keeping its S block in fp32 registers (LDS holds only its
+// MFMA operand form) while the next chunk's operands travel in.  Dense products run on
 // v_mfma_f32_16x16x32_bf16 with each fp32 operand split into bf16 hi + lo parts (a b ~ a_hi b_hi +
 // a_hi b_lo + a_lo b_hi, ~2^-16 relative), so the fp32 state is not rounded to bf16; with fp32
 // activations the products run on the fp32 MFMA.

@@ -215,7 +215,9 @@ int gdn_rollback_batch(const gdn_capture *capture, const int32_t *slots,
  * GDN_F_DEFER_COMMIT that verify left the state in the capture, and trim 0 is
  * gdn_rollback(capture, slot, n_tok - 1).  trim >= n_tok -> GDN_ERR_RANGE; else
  * gdn_rollback(capture, slot, n_tok - 1 - trim).  n_tok outside [1, t_cap], a negative trim or a
- * slot outside [0, n_pool) -> GDN_ERR_RANGE.
+ * slot outside [0, n_pool) -> GDN_ERR_RANGE.  Chain captures only: a tree's node indices are not
+ * positions along one path (a GDN_TREE capture -> GDN_ERR_ARG; roll a tree back with gdn_rollback
+ * at the accepted node).
  */
 int gdn_rollback_trim(const gdn_capture *capture, int32_t slot, int32_t trim, int32_t n_tok,
                       void *stream);

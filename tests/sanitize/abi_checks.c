@@ -71,6 +71,9 @@ int main(void)
     CHECK(gdn_rollback_trim(&cap, 0, 0, 16, NULL), GDN_OK);
     CHECK(gdn_rollback_trim(&cap, 0, 16, 16, NULL), GDN_ERR_RANGE);
     CHECK(gdn_rollback_trim(&cap, 0, 3, 17, NULL), GDN_ERR_RANGE);
+    cap.mode = GDN_TREE;
+    CHECK(gdn_rollback_trim(&cap, 0, 3, 16, NULL), GDN_ERR_ARG); /* trim counts chain positions */
+    cap.mode = GDN_CHAIN;
     gdn_capture two[2];
     two[0] = cap; two[1] = cap;
     CHECK(gdn_rollback_layers(two, 2, F, F, 1, NULL), GDN_ERR_ARG); /* shared state buffer */

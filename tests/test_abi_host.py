@@ -118,6 +118,10 @@ def test_rollback_validation():
     assert L.gdn_rollback_trim(ctypes.byref(cap), 0, 0, 16, None) == gdn.GDN_OK
     assert L.gdn_rollback_trim(ctypes.byref(cap), 0, 16, 16, None) == gdn.GDN_ERR_RANGE
     assert L.gdn_rollback_trim(ctypes.byref(cap), 0, 3, 17, None) == gdn.GDN_ERR_RANGE
+    # the trim form counts positions along a chain; a tree capture is rejected
+    tcap = gdn.gdn_capture(d, 0x1000, 0x1000, 0x1000, 0x1000, 16, gdn.GDN_TREE)
+    assert L.gdn_rollback_trim(ctypes.byref(tcap), 0, 3, 16, None) == gdn.GDN_ERR_ARG
+    assert "CHAIN" in gdn.last_error()
     assert L.gdn_rollback_batch(ctypes.byref(cap), None, None, 0, None) == gdn.GDN_OK
     assert L.gdn_rollback_batch(ctypes.byref(cap), None, None, 2, None) == gdn.GDN_ERR_ARG
     assert L.gdn_rollback_batch(ctypes.byref(cap), FAKE, FAKE, 5, None) == gdn.GDN_ERR_RANGE
