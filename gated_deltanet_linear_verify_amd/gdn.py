@@ -94,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_graph_launch.argtypes = [P, P]
         L.gdn_linear.argtypes = [P, P, I, I, I, ctypes.POINTER(gdn_out_seg), I, P]
         L.gdn_graph_destroy.argtypes = [P]
-        for f in ("gdn_verify", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch",
+        for f in ("gdn_verify", "gdn_verify_resume", "gdn_verify_tree", "gdn_rollback", "gdn_rollback_batch",
                   "gdn_rollback_trim", "gdn_prefill", "gdn_prefill_noalloc", "gdn_reset", "gdn_snapshot", "gdn_restore",
                   "gdn_rollback_layers", "gdn_graph_create", "gdn_graph_launch", "gdn_graph_destroy",
                   "gdn_linear"):
