@@ -113,39 +113,6 @@ __device__ __forceinline__ void load8(const float *p, float (&x)[8])
     }
 }
 
-// One 32-deep step of a 16x16 product.  Lane l holds a[e] = A[l % 16][8 (l / 16) + e] and
-// b[e] = B[8 (l / 16) + e][l % 16] of the 16x32 and 32x16 operands; the result rows are
-// 4 (l / 16) + r, columns l % 16.
-// F32: eight v_mfma_f32_16x16x4_f32, step e taking k index 8 kk + e for the instruction's kk = l / 16
-// (fp32 products, the precision of the all-fp32 path).  Otherwise one 16x16x32 bf16 MFMA per
-// pair of bf16 parts: a b ~ a_lo b_hi + a_hi b_lo + a_hi b_hi (the a_lo b_lo term, ~2^-16 of a b,
-// is dropped), smallest terms first.
-template <bool F32>
-__device__ __forceinline__ f4 mma8(const float (&a)[8], const float (&b)[8], f4 acc)
-{
-    if constexpr (F32) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = mfma4f32(a[e], b[e], acc);
-    } else {
-        bf16x8 ah, al, bh, bl;
-        split8(a, ah, al);
-        split8(b, bh, bl);
-        acc = mfma16(al, bh, acc);
-        acc = mfma16(ah, bl, acc);
-        acc = mfma16(ah, bh, acc);
-    }
-    return acc;
-}
-
-// Row-major [rows][D] fp32 matrix with its 8-float groups XOR-swizzled by the row index, so the
-// 16 rows that one MFMA operand load touches fall on different LDS banks.
-template <int D>
-__device__ __forceinline__ int swz(int r, int c)
-{
-    constexpr int NG = D / 8;
-    return r * D + ((((c >> 3) ^ r) & (NG - 1)) << 3) + (c & 7);
-}
-
 // 16x16 fp32 block product on the fp32 MFMA: acc += X(16x16 at ld, rows r0, cols c0) *
 // Y(16x16, rows k0.., cols n0..), both in kCP-padded LDS matrices.  Lane l supplies X[l%16][4s + l/16]
 // and Y[4s + l/16][l%16] for step s; the result is in the usual layout (rows 4 (l/16) + i, col l%16).
@@ -175,13 +142,20 @@ struct Frag<false> {
     bf16x8 hi, lo;
 };
 
+// One 32-deep step of a 16x16 product.  Lane l holds a = A[l % 16][8 (l / 16) + e] and
+// b = B[8 (l / 16) + e][l % 16], e = 0 .. 7, of the 16x32 and 32x16 operands; the result rows are
+// 4 (l / 16) + r, columns l % 16.
+// F32: eight v_mfma_f32_16x16x4_f32, step e taking k index 8 kk + e for the instruction's kk = l / 16
+// (fp32 products, the precision of the all-fp32 path).  Otherwise one 16x16x32 bf16 MFMA per
+// pair of bf16 parts: a b ~ a_lo b_hi + a_hi b_lo + a_hi b_hi (the a_lo b_lo term, ~2^-16 of a b,
+// is dropped), smallest terms first.
 template <bool F32>
 __device__ __forceinline__ f4 mma(const Frag<F32> &a, const Frag<F32> &b, f4 acc)
 {
     if constexpr (F32) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = mfma4f32(a.v[e], b.v[e], acc);
-    } else {  // the same three products, in the same order, as mma8
+    } else {
         acc = mfma16(a.lo, b.hi, acc);
         acc = mfma16(a.hi, b.lo, acc);
         acc = mfma16(a.hi, b.hi, acc);
@@ -358,8 +332,8 @@ struct PrepLds {
     static constexpr int C = kChunk;
     static constexpr size_t qk_bytes = sizeof(float) * 2 * C * D;
     static constexpr size_t tp_bytes = sizeof(float) * (2 * C * kCP + 4 * 256);
-    static constexpr size_t q = 0;                               // [C][D] swizzled
-    static constexpr size_t k = q + sizeof(float) * C * D;       // [C][D] swizzled
+    static constexpr size_t q = 0;                               // [C][D] as a Mat image
+    static constexpr size_t k = q + sizeof(float) * C * D;       // [C][D] as a Mat image
     static constexpr size_t tm = 0;                              // once q, k are consumed: [C][kCP] A, then T
     static constexpr size_t pm = tm + sizeof(float) * C * kCP;   //                         [C][kCP] P
     static constexpr size_t scr = pm + sizeof(float) * C * kCP;  //                         [4][16][16] scratch
@@ -499,12 +473,16 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // the first value heads' gate inputs travel with the q | k rows below
     GateIn gin = gate_load(wave);
 
-    // ---- conv of q | k into LDS: wave w takes tokens 16w .. 16w+15, a lane 4 channels; every row
-    // it reads is loaded before the first tap sum
+    // ---- conv of q | k into LDS and into the scan's q and k images: wave w takes tokens 16w ..
+    // 16w+15, a lane 4 channels; every row it reads is loaded before the first tap sum.  The image
+    // stores go out token by token, so they travel while the conv and the Gram products run.
+    using MQ = Mat<F32, C, D>;
+    float *const qdst = a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D;
     if (lane < QKG) {
         const int lc = 4 * lane;
         const bool isq = lc < D;
         float *M = isq ? Q : K;
+        float *img = isq ? qdst : qdst + C * D;
         const int mc = isq ? lc : lc - D;
         f4 wqk[4];
 #pragma unroll
@@ -538,29 +516,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) y[j] *= sc;
             }
-            *reinterpret_cast<f4 *>(M + swz<D>(t, mc)) = y;
+            MQ::put4(M, t, mc, y);  // in LDS already in operand form: the Gram products split nothing
+            MQ::put4(img, t, mc, y);
         }
     }
     asm volatile("" : "+v"(gin.al), "+v"(gin.be), "+v"(gin.alog), "+v"(gin.dtb));  // loaded by now
     if (wave < min(R, L::heads)) gate_put(wave, gin);
     lds_barrier();  // q, k and the first heads' gates are in LDS
 
-    // ---- the q and k images, then the lower 16 x 16 tiles of K K^T (waves 0, 1) and Q K^T (waves
-    // 2, 3) into registers (MFMA; row tiles {0,3} or {1,2}: 5 tiles per wave).  Each value head's
-    // A = strictly-lower(beta e^{G_t-G_s} K K^T) and P = lower(e^{G_t-G_s} Q K^T) scale them.
-    {
-        using MQ = Mat<F32, C, D>;
-        float *qdst = a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D;
-        float *kdst = qdst + C * D;
-        for (int g = tid; g < C * D / 8; g += kPThreads) {
-            const int r = g / (D / 8), c0 = (g % (D / 8)) * 8;
-            float x[8];
-            load8(Q + swz<D>(r, c0), x);
-            MQ::put8(qdst, r, c0, x);
-            load8(K + swz<D>(r, c0), x);
-            MQ::put8(kdst, r, c0, x);
-        }
-    }
+    // ---- the lower 16 x 16 tiles of K K^T (waves 0, 1) and Q K^T (waves 2, 3) into registers (MFMA;
+    // row tiles {0,3} or {1,2}: 5 tiles per wave).  Each value head's A = strictly-lower(beta
+    // e^{G_t-G_s} K K^T) and P = lower(e^{G_t-G_s} Q K^T) scale them.
     const int pair = wave & 1;
     auto tile_rt = [&](int jt) { return pair == 0 ? (jt == 0 ? 0 : 3) : (jt < 2 ? 1 : 2); };
     auto tile_ct = [&](int jt) { return pair == 0 ? (jt == 0 ? 0 : jt - 1) : (jt < 2 ? jt : jt - 2); };
@@ -574,10 +540,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D; kk += 32) {
-                float av[8], bv[8];
-                load8(Am + swz<D>(16 * rt + (lane & 15), kk + (lane >> 4) * 8), av);
-                load8(K + swz<D>(16 * ct + (lane & 15), kk + (lane >> 4) * 8), bv);
-                acc = mma8<F32>(av, bv, acc);
+                const Frag<F32> fa = MQ::load(Am, 16 * rt + (lane & 15), kk + (lane >> 4) * 8);
+                const Frag<F32> fb = MQ::load(K, 16 * ct + (lane & 15), kk + (lane >> 4) * 8);
+                acc = mma<F32>(fa, fb, acc);
             }
             tiles[jt] = acc;
         }
@@ -594,6 +559,20 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const float *Gam = gate_slot(hh), *gam = Gam + C, *bet = gam + C, *dec = bet + C;
         {
             float *Dm = wave < 2 ? Tm : Pm;
+            // Every gate this lane's 20 entries use is read before any entry is formed, and the
+            // entries are selected, not branched to: a read under a lane condition would cost an
+            // LDS round trip per entry.
+            float gt[5][4], bt[5][4], gs[5];
+#pragma unroll
+            for (int jt = 0; jt < 5; ++jt) {
+                gs[jt] = Gam[16 * tile_ct(jt) + (lane & 15)];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tile_rt(jt) + (lane >> 4) * 4 + r;
+                    gt[jt][r] = Gam[t];
+                    bt[jt][r] = bet[t];
+                }
+            }
 #pragma unroll
             for (int jt = 0; jt < 5; ++jt) {
                 const int rt = tile_rt(jt), ct = tile_ct(jt);
@@ -601,9 +580,10 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * rt + (lane >> 4) * 4 + r;
-                    const float ratio = exp_decay(Gam[t] - Gam[s_]);
-                    Dm[t * kCP + s_] = wave < 2 ? (s_ < t ? bet[t] * ratio * tiles[jt][r] : 0.f)
-                                                : (s_ <= t ? ratio * tiles[jt][r] : 0.f);
+                    const float ratio = exp_decay(gt[jt][r] - gs[jt]);
+                    const float av = s_ < t ? bt[jt][r] * ratio * tiles[jt][r] : 0.f;
+                    const float pv = s_ <= t ? ratio * tiles[jt][r] : 0.f;
+                    Dm[t * kCP + s_] = wave < 2 ? av : pv;
                 }
             }
             // the six 16 x 16 blocks above the diagonal are zero
