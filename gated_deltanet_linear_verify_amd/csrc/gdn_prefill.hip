@@ -330,10 +330,14 @@ __host__ __device__ inline PrefillWs prefill_ws(int d, int n_kh, int n_vh, int T
 template <int D>
 struct PrepLds {
     static constexpr int C = kChunk;
-    static constexpr size_t qk_bytes = sizeof(float) * 2 * C * D;
+    // q and k are convolved in NH passes over their channels, D / NH channels in LDS at a time, so
+    // that three d = 128 workgroups share a CU (their phases are latency-bound: more of them hide it)
+    static constexpr int NH = D == 128 ? 2 : 1;
+    static constexpr int DH = D / NH;
+    static constexpr size_t qk_bytes = sizeof(float) * 2 * C * DH;
     static constexpr size_t tp_bytes = sizeof(float) * (2 * C * kCP + 4 * 256);
-    static constexpr size_t q = 0;                               // [C][D] as a Mat image
-    static constexpr size_t k = q + sizeof(float) * C * D;       // [C][D] as a Mat image
+    static constexpr size_t q = 0;                               // [C][DH] as a Mat image
+    static constexpr size_t k = q + sizeof(float) * C * DH;      // [C][DH] as a Mat image
     static constexpr size_t tm = 0;                              // once q, k are consumed: [C][kCP] A, then T
     static constexpr size_t pm = tm + sizeof(float) * C * kCP;   //                         [C][kCP] P
     static constexpr size_t scr = pm + sizeof(float) * C * kCP;  //                         [4][16][16] scratch
@@ -341,7 +345,8 @@ struct PrepLds {
     static constexpr size_t gate = qk_bytes > tp_bytes ? qk_bytes : tp_bytes;  // per head: Gamma, gamma, beta, decay [4][C]
     static constexpr size_t total = gate + sizeof(float) * heads * 4 * C;
 };
-static_assert(2 * PrepLds<128>::total <= 160 * 1024, "two d=128 prep workgroups must fit one CU's LDS");
+static_assert(3 * PrepLds<128>::total <= 160 * 1024 && 3 * PrepLds<64>::total <= 160 * 1024,
+              "three prep workgroups must fit one CU's LDS");
 
 // Scan workgroup: kSR value rows of one value head.  Its LDS, in bytes:
 template <int D, bool ACT_BF16>
@@ -383,7 +388,7 @@ __device__ __forceinline__ float exp_decay(float x) { return __builtin_amdgcn_ex
 // The q | k conv and the Gram products K K^T and Q K^T are shared by the key head's value heads;
 // the gates, A / P, T and the v conv are per value head, in a loop.
 template <int D, bool ACT_BF16, bool QKN>
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_prep_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_prep_kernel(PrefillArgs a)
 {
     using act_t = typename std::conditional<ACT_BF16, uint16_t, float>::type;
     using L = PrepLds<D>;
@@ -473,79 +478,163 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // the first value heads' gate inputs travel with the q | k rows below
     GateIn gin = gate_load(wave);
 
-    // ---- conv of q | k into LDS and into the scan's q and k images: wave w takes tokens 16w ..
-    // 16w+15, a lane 4 channels; every row it reads is loaded before the first tap sum.  The image
-    // stores go out token by token, so they travel while the conv and the Gram products run.
-    using MQ = Mat<F32, C, D>;
+    // ---- conv of q | k into LDS and into the scan's q and k images.  Every row a lane reads is
+    // loaded before the first tap sum; the image stores go out as the values are formed, so they
+    // travel while the conv and the Gram products run.  LDS holds q and k in operand form (bf16 hi /
+    // lo planes), so the Gram products split nothing.
+    constexpr int NH = L::NH, DH = L::DH;
+    using MQ = Mat<F32, C, D>;   // the scan's q / k images
+    using MH = Mat<F32, C, DH>;  // this pass's channels of q and k in LDS
     float *const qdst = a.ws + w.qk + ((size_t)c * a.n_kh + hk) * 2 * C * D;
-    if (lane < QKG) {
-        const int lc = 4 * lane;
-        const bool isq = lc < D;
-        float *M = isq ? Q : K;
-        float *img = isq ? qdst : qdst + C * D;
-        const int mc = isq ? lc : lc - D;
-        f4 wqk[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wqk[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + j) * 4);
-        raw4 rw[19];
-#pragma unroll
-        for (int i = 0; i < 19; ++i) rw[i] = ld_raw(min(max(16 * wave - 3 + i, tmin), Lc - 1), lc);
-        const bool head_rows = c == 0 && wave == 0;  // the wave's first three rows precede the call
-        f4 hs[3] = {};
-        if (head_rows)
-#pragma unroll
-            for (int i = 0; i < 3; ++i) hs[i] = hist4(i - 3, lc);
-        f4 xs[19];
-#pragma unroll
-        for (int i = 0; i < 19; ++i) xs[i] = (i < 3 && head_rows) ? hs[i < 3 ? i : 0] : cvt(rw[i]);
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-            const int t = 16 * wave + tt;
-            f4 y;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float v = conv4(wqk[j], xs[tt][j], xs[tt + 1][j], xs[tt + 2][j], xs[tt + 3][j]);
-                if constexpr (QKN) v = v * sigmoid_f(v);
-                y[j] = t < Lc ? v : 0.f;
-            }
-            if constexpr (QKN) {  // unit length (+1e-6) over the head's 128 channels; q also / sqrt(d)
-                float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
-                ss = row16_sum(ss);
-                if constexpr (D == 128) ss += __shfl_xor(ss, 16);
-                const float sc = rsqrt_f(ss + 1e-6f) * (isq ? 1.0f / sqrtf((float)D) : 1.0f);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] *= sc;
-            }
-            MQ::put4(M, t, mc, y);  // in LDS already in operand form: the Gram products split nothing
-            MQ::put4(img, t, mc, y);
-        }
-    }
-    asm volatile("" : "+v"(gin.al), "+v"(gin.be), "+v"(gin.alog), "+v"(gin.dtb));  // loaded by now
-    if (wave < min(R, L::heads)) gate_put(wave, gin);
-    lds_barrier();  // q, k and the first heads' gates are in LDS
 
-    // ---- the lower 16 x 16 tiles of K K^T (waves 0, 1) and Q K^T (waves 2, 3) into registers (MFMA;
-    // row tiles {0,3} or {1,2}: 5 tiles per wave).  Each value head's A = strictly-lower(beta
-    // e^{G_t-G_s} K K^T) and P = lower(e^{G_t-G_s} Q K^T) scale them.
+    // The lower 16 x 16 tiles of K K^T (waves 0, 1) and Q K^T (waves 2, 3), accumulated in registers
+    // pass by pass (MFMA; row tiles {0,3} or {1,2}: 5 tiles per wave), the k index in increasing
+    // order over the passes.  Each value head's A = strictly-lower(beta e^{G_t-G_s} K K^T) and
+    // P = lower(e^{G_t-G_s} Q K^T) scale them.
     const int pair = wave & 1;
     auto tile_rt = [&](int jt) { return pair == 0 ? (jt == 0 ? 0 : 3) : (jt < 2 ? 1 : 2); };
     auto tile_ct = [&](int jt) { return pair == 0 ? (jt == 0 ? 0 : jt - 1) : (jt < 2 ? jt : jt - 2); };
     f4 tiles[5];
-    {
+#pragma unroll
+    for (int jt = 0; jt < 5; ++jt) tiles[jt] = f4{0.f, 0.f, 0.f, 0.f};
+    auto gram = [&]() {
         const float *Am = wave < 2 ? K : Q;
 #pragma unroll
         for (int jt = 0; jt < 5; ++jt) {
             // pair 0: (0,0) (3,0) (3,1) (3,2) (3,3);  pair 1: (1,0) (1,1) (2,0) (2,1) (2,2)
             const int rt = tile_rt(jt), ct = tile_ct(jt);
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < D; kk += 32) {
-                const Frag<F32> fa = MQ::load(Am, 16 * rt + (lane & 15), kk + (lane >> 4) * 8);
-                const Frag<F32> fb = MQ::load(K, 16 * ct + (lane & 15), kk + (lane >> 4) * 8);
-                acc = mma<F32>(fa, fb, acc);
+            for (int kk = 0; kk < DH; kk += 32) {
+                const Frag<F32> fa = MH::load(Am, 16 * rt + (lane & 15), kk + (lane >> 4) * 8);
+                const Frag<F32> fb = MH::load(K, 16 * ct + (lane & 15), kk + (lane >> 4) * 8);
+                tiles[jt] = mma<F32>(fa, fb, tiles[jt]);
             }
-            tiles[jt] = acc;
         }
+    };
+
+    if constexpr (NH == 1) {
+        // wave w takes tokens 16w .. 16w+15, a lane 4 channels
+        if (lane < QKG) {
+            const int lc = 4 * lane;
+            const bool isq = lc < D;
+            float *M = isq ? Q : K;
+            float *img = isq ? qdst : qdst + C * D;
+            const int mc = isq ? lc : lc - D;
+            f4 wqk[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wqk[j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + j) * 4);
+            raw4 rw[19];
+#pragma unroll
+            for (int i = 0; i < 19; ++i) rw[i] = ld_raw(min(max(16 * wave - 3 + i, tmin), Lc - 1), lc);
+            const bool head_rows = c == 0 && wave == 0;  // the wave's first three rows precede the call
+            f4 hs[3] = {};
+            if (head_rows)
+#pragma unroll
+                for (int i = 0; i < 3; ++i) hs[i] = hist4(i - 3, lc);
+            f4 xs[19];
+#pragma unroll
+            for (int i = 0; i < 19; ++i) xs[i] = (i < 3 && head_rows) ? hs[i < 3 ? i : 0] : cvt(rw[i]);
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                const int t = 16 * wave + tt;
+                f4 y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v = conv4(wqk[j], xs[tt][j], xs[tt + 1][j], xs[tt + 2][j], xs[tt + 3][j]);
+                    if constexpr (QKN) v = v * sigmoid_f(v);
+                    y[j] = t < Lc ? v : 0.f;
+                }
+                if constexpr (QKN) {  // unit length (+1e-6) over the head's channels; q also / sqrt(d)
+                    float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+                    ss = row16_sum(ss);
+                    if constexpr (D == 128) ss += __shfl_xor(ss, 16);
+                    const float sc = rsqrt_f(ss + 1e-6f) * (isq ? 1.0f / sqrtf((float)D) : 1.0f);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y[j] *= sc;
+                }
+                MH::put4(M, t, mc, y);
+                MQ::put4(img, t, mc, y);
+            }
+        }
+        asm volatile("" : "+v"(gin.al), "+v"(gin.be), "+v"(gin.alog), "+v"(gin.dtb));  // loaded by now
+        if (wave < min(R, L::heads)) gate_put(wave, gin);
+        lds_barrier();  // q, k and the first heads' gates are in LDS
+        gram();
+    } else {
+        // Two passes over the channel halves.  Wave w takes tokens 16w .. 16w+15, 8 per half wave
+        // (th), a lane 4 channels of each half: q channels 4g .. 4g+3 (g < 16) or k channels
+        // 4(g-16) .. (g >= 16), and the same plus DH.  A 16-lane row holds one token set's q or k,
+        // both halves, so the q / k norm's sum over the head is one row sum.
+        const int th = lane >> 5, g = lane & 31;
+        const bool isq = g < 16;
+        const int mc = 4 * (g & 15);         // channel within q or k (first half)
+        const int lc = (isq ? 0 : D) + mc;   // q | k channel (first half)
+        float *M = isq ? Q : K;
+        float *img = isq ? qdst : qdst + C * D;
+        const int t0w = 16 * wave + 8 * th;  // the lane's first token
+        f4 wqk[2][4];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wqk[hp][j] = *reinterpret_cast<const f4 *>(a.conv_w + (size_t)gchan(lc + DH * hp + j) * 4);
+        raw4 rw[2][11];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+            for (int i = 0; i < 11; ++i) rw[hp][i] = ld_raw(min(max(t0w - 3 + i, tmin), Lc - 1), lc + DH * hp);
+        const bool head_rows = c == 0 && t0w == 0;  // the first three rows precede the call
+        f4 hs[2][3] = {};
+        if (head_rows)
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int i = 0; i < 3; ++i) hs[hp][i] = hist4(i - 3, lc + DH * hp);
+        f4 y[2][8];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            f4 xs[11];
+#pragma unroll
+            for (int i = 0; i < 11; ++i) xs[i] = (i < 3 && head_rows) ? hs[hp][i < 3 ? i : 0] : cvt(rw[hp][i]);
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v = conv4(wqk[hp][j], xs[tt][j], xs[tt + 1][j], xs[tt + 2][j], xs[tt + 3][j]);
+                    if constexpr (QKN) v = v * sigmoid_f(v);
+                    y[hp][tt][j] = t0w + tt < Lc ? v : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            const int t = t0w + tt;
+            if constexpr (QKN) {  // unit length (+1e-6) over the head's channels; q also / sqrt(d)
+                float ss = 0.f;
+#pragma unroll
+                for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ss += y[hp][tt][j] * y[hp][tt][j];
+                ss = row16_sum(ss);
+                const float sc = rsqrt_f(ss + 1e-6f) * (isq ? 1.0f / sqrtf((float)D) : 1.0f);
+#pragma unroll
+                for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y[hp][tt][j] *= sc;
+            }
+            MH::put4(M, t, mc, y[0][tt]);
+            MQ::put4(img, t, mc, y[0][tt]);
+            MQ::put4(img, t, mc + DH, y[1][tt]);
+        }
+        asm volatile("" : "+v"(gin.al), "+v"(gin.be), "+v"(gin.alog), "+v"(gin.dtb));  // loaded by now
+        if (wave < min(R, L::heads)) gate_put(wave, gin);
+        lds_barrier();  // the first half of q and k and the first heads' gates are in LDS
+        gram();
+        lds_barrier();  // every wave has read the first half
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) MH::put4(M, t0w + tt, mc, y[1][tt]);
+        lds_barrier();  // the second half is in LDS
+        gram();
     }
     lds_barrier();  // q and k are consumed: their space holds A / T and P from here on
 #pragma unroll 1

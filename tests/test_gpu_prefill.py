@@ -73,6 +73,12 @@ PREFILL_CASES = {
     "bf16_d64_six_per_key_head_130": (W.shape_with(W.TINY_VERIFY, n_tok=130, n_kh=1, n_vh=6, act_dtype=W.BF16,
                                                    out_dtype=W.BF16), {"weak_decay": True}, 0),
     "bf16_d128_gqa4_70": (W.shape_with(W.CHUNKED_PREFILL, n_tok=70, n_kh=4, n_vh=16), {"weak_decay": True}, 0),
+    # the q / k norm flag with fp32 activations at d = 128 (two conv passes over the channel halves)
+    # and with bf16 at d = 64 (one pass)
+    "fp32_d128_qk_norm_130": (W.shape_with(W.CHUNKED_PREFILL, n_tok=130, n_kh=2, n_vh=4, act_dtype=W.F32,
+                                           out_dtype=W.F32), {"weak_decay": True}, 1),
+    "bf16_d64_qk_norm_150": (W.shape_with(W.TINY_VERIFY, n_tok=150, n_kh=2, n_vh=4, act_dtype=W.BF16,
+                                          out_dtype=W.BF16), {"weak_decay": True}, 1),
 }
 
 
