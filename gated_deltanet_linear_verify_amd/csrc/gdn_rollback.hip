@@ -12,9 +12,11 @@
 namespace gdn {
 
 // One entry's copy: ns float4 of recurrent state and nc float4 of conv state, spread over the
-// gridDim.x blocks that share the entry, four loads in flight per thread.  The state is written
-// with store_stream: plain stores leave its lines dirty in the caches, and the next verify, which
-// streams its 2 GiB capture, then pays for their write-back (measured: 441 vs 464 us per verify).
+// gridDim.x blocks that share the entry, four loads in flight per thread.  Everything is written
+// with store_stream: plain stores leave their lines dirty in the caches, and the next verify, which
+// streams its 2 GiB capture, then pays for their write-back (measured: 441 vs 464 us per verify
+// with plain state stores; streaming the last ~14% of the state and the conv state as well took
+// another ~2 us off it).
 __device__ __forceinline__ void copy_entry(const f4 *src_s, f4 *dst_s, size_t ns, const f4 *src_c, f4 *dst_c, size_t nc)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -26,8 +28,8 @@ __device__ __forceinline__ void copy_entry(const f4 *src_s, f4 *dst_s, size_t ns
         store_stream(dst_s + i + 2 * stride, v2);
         store_stream(dst_s + i + 3 * stride, v3);
     }
-    for (; i < ns; i += stride) dst_s[i] = src_s[i];
-    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < nc; j += stride) dst_c[j] = src_c[j];
+    for (; i < ns; i += stride) store_stream(dst_s + i, src_s[i]);
+    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < nc; j += stride) store_stream(dst_c + j, src_c[j]);
 }
 
 // Sources of entry (slot, idx) in one layer's capture: the state after position idx, and the conv
@@ -65,9 +67,12 @@ __global__ __launch_bounds__(256) void rollback_layers_kernel(RollbackLayersArgs
     rollback_entry(a.geo, L.cap_ssm, L.cap_conv, L.state, L.conv_state, slot, idx);
 }
 
-static unsigned copy_blocks(size_t ssm_elems, size_t conv_elems)
+// Blocks per entry: sized by the state alone, so that (for states of a multiple of 1024 float4)
+// every thread copies exactly four float4 of it in one unrolled step; the conv state's float4 go to
+// the first threads.
+static unsigned copy_blocks(size_t ssm_elems)
 {
-    const size_t vec = (ssm_elems + conv_elems) / 4;
+    const size_t vec = ssm_elems / 4;
     size_t blocks = (vec + 256 * 4 - 1) / (256 * 4);
     if (blocks > 512) blocks = 512;
     if (blocks < 1) blocks = 1;
@@ -77,7 +82,7 @@ static unsigned copy_blocks(size_t ssm_elems, size_t conv_elems)
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream)
 {
     if (a.n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rollback_kernel, dim3(copy_blocks(a.ssm_elems, a.conv_elems), (unsigned)a.n), dim3(256), 0,
+    hipLaunchKernelGGL(rollback_kernel, dim3(copy_blocks(a.ssm_elems), (unsigned)a.n), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -87,7 +92,7 @@ hipError_t launch_rollback_layers(const RollbackLayersArgs &a, hipStream_t strea
     if (a.geo.n <= 0 || a.n_layers <= 0) return hipSuccess;
     if (a.n_layers > kMaxLayersPerLaunch) return hipErrorInvalidValue;
     hipLaunchKernelGGL(rollback_layers_kernel,
-                       dim3(copy_blocks(a.geo.ssm_elems, a.geo.conv_elems), (unsigned)a.geo.n, (unsigned)a.n_layers),
+                       dim3(copy_blocks(a.geo.ssm_elems), (unsigned)a.geo.n, (unsigned)a.n_layers),
                        dim3(256), 0, stream, a);
     return hipGetLastError();
 }
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(SlotCopyArgs a)
 hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream)
 {
     if (a.n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(slot_copy_kernel, dim3(copy_blocks(a.ssm_elems, a.conv_elems), (unsigned)a.n), dim3(256), 0,
+    hipLaunchKernelGGL(slot_copy_kernel, dim3(copy_blocks(a.ssm_elems), (unsigned)a.n), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
 }
