@@ -416,11 +416,11 @@ __global__ __launch_bounds__(TreeWaves<D>::value * 64) void verify_tree_kernel(V
                 float y = conv4(wv, x[j][0], x[j][1], x[j][2], x[j][3]);
                 if constexpr (QKN) y = y * sigmoid_f(y);
                 dst[n * D] = y;
-                if (own) {  // 3-row conv state after node n: [ancestor 2, ancestor 1, n]
+                if (own) {  // 3-row conv state after node n: [ancestor 2, ancestor 1, n], non-temporal
                     float *cp = cct + (size_t)n * 3 * C + gc;
-                    cp[0] = x[j][1];
-                    cp[(size_t)C] = x[j][2];
-                    cp[(size_t)2 * C] = x[j][3];
+                    __builtin_nontemporal_store(x[j][1], cp);
+                    __builtin_nontemporal_store(x[j][2], cp + (size_t)C);
+                    __builtin_nontemporal_store(x[j][3], cp + (size_t)2 * C);
                 }
             }
         }
