@@ -65,6 +65,8 @@ TREE_CASES = {
     "bf16_d128_128_nodes": (W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=2, n_tok=128), 8, 0),
     "fp32_d64_200_nodes_depth12": (W.shape_with(W.TINY_VERIFY, n_tok=200, n_pool=2, n_batch=2), 12, 0),
     "bf16_d64_deep_comb_150": (W.shape_with(W.TINY_VERIFY, n_tok=150, act_dtype=W.BF16, out_dtype=W.BF16), 150, 0),
+    # the most nodes one call takes: 16 consecutive launches of 64
+    "fp32_d64_1024_nodes_max": (W.shape_with(W.TINY_VERIFY, n_tok=1024, n_pool=1, n_batch=1), 16, 0),
 }
 
 
