@@ -56,11 +56,18 @@ template <int GM, int GN, int WM, int WN, int NBUF = 2>
 struct LinTile {
     static constexpr int THREADS = 64 * GM * GN;
     static constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
-    static constexpr int XT = BM * kLChunks / THREADS;  // x transfers per thread and k tile
-    static constexpr int WT = BN * kLChunks / THREADS;  // W transfers per thread and k tile
+    // x and W transfers per thread and k tile (at most: with XE / WE false the last round of
+    // transfers covers only the first threads, whole waves)
+    static constexpr int XT = (BM * kLChunks + THREADS - 1) / THREADS;
+    static constexpr int WT = (BN * kLChunks + THREADS - 1) / THREADS;
+    static constexpr bool XE = BM * kLChunks % THREADS == 0, WE = BN * kLChunks % THREADS == 0;
     static constexpr size_t lds = NBUF * (size_t)(BM + BN) * kLBK * 2;  // NBUF buffers of x and W tiles
     static_assert(XT >= 1 && WT >= 1 && (NBUF - 1) * (XT + WT) < 64, "tile transfer counts");
-    static_assert(BM * kLChunks % THREADS == 0 && BN * kLChunks % THREADS == 0, "even transfers");
+    static_assert((BM * kLChunks % THREADS) % 64 == 0 && (BN * kLChunks % THREADS) % 64 == 0,
+                  "a partial round of transfers covers whole waves");
+    // with more than two buffers the wait for a k tile counts this thread's later transfers, which
+    // must then be the same for every thread
+    static_assert(NBUF == 2 || (XE && WE), "uneven transfer counts need two buffers");
 };
 
 // Wait until at most `later` k tiles of TPT transfers each are in flight (s_waitcnt takes an
@@ -118,9 +125,13 @@ __global__ __launch_bounds__(64 * GM * GN) void linear_kernel(LinearArgs a)
     auto issue = [&](int kt, int buf) {
         unsigned char *base = lds + buf * BUF;
 #pragma unroll
-        for (int i = 0; i < TL::XT; ++i) lds_dma16(xsrc[i] + kt * kLBK, base + (tid + kLThreads * i) * 16);
+        for (int i = 0; i < TL::XT; ++i)
+            if (TL::XE || i < TL::XT - 1 || tid + kLThreads * i < BM * kLChunks)
+                lds_dma16(xsrc[i] + kt * kLBK, base + (tid + kLThreads * i) * 16);
 #pragma unroll
-        for (int i = 0; i < TL::WT; ++i) lds_dma16(wsrc[i] + kt * kLBK, base + XB + (tid + kLThreads * i) * 16);
+        for (int i = 0; i < TL::WT; ++i)
+            if (TL::WE || i < TL::WT - 1 || tid + kLThreads * i < BN * kLChunks)
+                lds_dma16(wsrc[i] + kt * kLBK, base + XB + (tid + kLThreads * i) * 16);
     };
 
     f4 acc[WM][WN];
@@ -221,24 +232,35 @@ static hipError_t launch_tile(const LinearArgs &a, hipStream_t stream)
 }
 
 // Tile choice.  A k tile brings (BM + BN) x 64 operands into LDS for 2 BM BN x 64 flops, so larger
-// workgroup tiles need fewer bytes per flop from L2; 256 x 256 (16 waves of 64 x 64, one workgroup
-// per CU) is the fastest per CU, and is taken when its tiles fill at least three quarters of the
-// 256 CUs (1024 x 5120 -> 12352: 196 tiles, 134 us against 162 us with 128 x 128).  Otherwise
-// 128 x 128 tiles of 16 waves of 32 x 32, two workgroups per CU, spread a smaller product over
-// every CU (1024 x 4096 -> 5120: 320 tiles, 56 us against 106 us with 80 of 256 x 256).  A few rows
-// (one slot's drafted tokens) make the product a stream of the weight, read once: one-wave tiles
-// 16 (M <= 16) or 32 (M <= 32) rows by 16 columns spread it over N / 16 workgroups, and four
-// buffered k tiles keep three in flight per workgroup (16 x 5120 -> 12352: 20 us, 6.2 TB/s of
-// weight, against 40 us with double-buffered 32 x 64 tiles; 16 x 4096 -> 5120: 14.5 against
-// 31 us).  Up to 64 rows, four-buffered 32 x 64 tiles (64 x 4096 -> 5120: 21 against 32 us).
+// workgroup tiles need fewer bytes per flop from L2, but a launch needs enough of them to spread
+// over the 256 CUs, and smaller ones keep more k tiles in flight per CU.  The first of these whose
+// tile count reaches its threshold is taken (thresholds measured on the GDN block's projections,
+// 5120 -> 12352 and 4096 -> 5120, at 96 to 1024 rows):
+//   256 x 256, 16 waves of 64 x 64, one workgroup per CU: >= 140 tiles (1024 rows of the
+//     in-projection: 196 tiles, 134 us against 162 with 128 x 128; 768 rows: 129 against 146)
+//   128 x 128, 16 waves of 32 x 32, two per CU: >= 280 (the out-projection at 1024 rows, 57 us)
+//   64 x 128, 16 waves of 16 x 32: >= 280 (the in-projection at 192 - 256 rows, 52 - 55 us against
+//     63 - 64 with 128 x 128)
+//   64 x 64, 4 waves, three buffered k tiles: >= 280 (the out-projection at 256 - 384 rows, 30 us
+//     against 48 with 128 x 128, which keeps one k tile in flight and waits on it at every step)
+//   32 x 64, 4 waves, four buffered k tiles, otherwise (the out-projection up to 192 rows: 22 - 25
+//     against 47 us).
+// A few rows (one slot's drafted tokens) make the product a stream of the weight, read once:
+// one-wave tiles of 16 (M <= 16) or 32 (M <= 32) rows by 16 columns spread it over N / 16
+// workgroups with four buffered k tiles (16 x 5120 -> 12352: 20 us, 6.2 TB/s of weight, against
+// 40 us with double-buffered 32 x 64 tiles; 16 x 4096 -> 5120: 14.5 against 31 us).
 hipError_t launch_linear(const LinearArgs &a, hipStream_t stream)
 {
     if (a.M <= 16) return launch_tile<1, 1, 1, 1, 4>(a, stream);
     if (a.M <= 32) return launch_tile<1, 1, 2, 1, 4>(a, stream);
-    if (a.M <= 64) return launch_tile<2, 2, 1, 2, 4>(a, stream);
-    const long big = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (big >= 192) return launch_tile<4, 4, 4, 4>(a, stream);
-    return launch_tile<4, 4, 2, 2>(a, stream);
+    auto tiles = [&](int bm, int bn) { return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+    if (a.M > 64) {
+        if (tiles(256, 256) >= 140) return launch_tile<4, 4, 4, 4>(a, stream);
+        if (tiles(128, 128) >= 280) return launch_tile<4, 4, 2, 2>(a, stream);
+        if (tiles(64, 128) >= 280) return launch_tile<4, 4, 1, 2>(a, stream);
+        if (tiles(64, 64) >= 280) return launch_tile<2, 2, 2, 2, 3>(a, stream);
+    }
+    return launch_tile<2, 2, 1, 2, 4>(a, stream);
 }
 
 }  // namespace gdn

@@ -45,7 +45,11 @@ def _bf16_err(gpu, ref_):
                                    # few rows: one-wave 16 x 16 or 32 x 16 tiles, four buffered k
                                    # tiles (one k tile at K = 64, three at 192)
                                    (7, 1000, 192), (16, 17, 128), (16, 5120, 4096), (16, 12352, 512),
-                                   (24, 700, 320), (48, 5120, 4096)])
+                                   (24, 700, 320), (48, 5120, 4096),
+                                   # 65 - 1023 rows: 64 x 128 tiles (uneven x transfers), 64 x 64
+                                   # tiles with three buffered k tiles (at K = 128 and 192 fewer k
+                                   # tiles than buffers), 32 x 64 tiles
+                                   (300, 9000, 256), (130, 9000, 192), (200, 5000, 128), (100, 3000, 320)])
 def test_linear_fp32_out(M, N, K):
     """Ragged M and N (partial tiles, a single element), several K tiles; the last shape has enough
     256 x 256 tiles (5 x 40) to take that tiling, with partial tiles along both M and N."""
