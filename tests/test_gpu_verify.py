@@ -125,6 +125,30 @@ def test_verify_is_deterministic():
         assert torch.equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("n_batch", [2, 3, 8])
+def test_slot_permutation_gives_the_same_per_slot_results(n_batch):
+    """Batch entries listed in reverse order (their inputs and slot ids permuted together) leave
+    every slot with the same state, conv state and capture, bit for bit, and each entry's output
+    moves with it.  2 entries take the row split, 3 a workgroup per value head, 8 a workgroup per
+    key head."""
+    shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_pool=n_batch + 2, n_batch=n_batch)
+    say(f"[slot permutation] {n_batch} entries")
+    inp = W.make_inputs(shape, 11)
+    perm = np.arange(n_batch)[::-1].copy()
+    pinp = dict(inp)
+    for k in ("qkv", "z", "alpha", "beta", "slot_ids"):
+        pinp[k] = np.ascontiguousarray(np.asarray(inp[k])[perm])
+    dev = _dev()
+    a = dev.upload(shape, inp, fill_capture=0.0)  # the pool's unused slots keep a comparable fill
+    b = dev.upload(shape, pinp, fill_capture=0.0)
+    dev.verify(a)
+    dev.verify(b)
+    torch.cuda.synchronize()
+    for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["out"][torch.from_numpy(perm).cuda()], b["out"])
+
+
 def test_beta_zero_no_decay_is_identity_on_gpu():
     shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=5)
     inp = W.make_inputs(shape, 5)
