@@ -178,6 +178,30 @@ def test_tree_rollback_equals_chain_along_accepted_path(n_tok):
         assert torch.equal(t["conv_state"][s], c["conv_state"][s])
 
 
+def test_tree_slot_permutation_gives_the_same_per_slot_results():
+    """Tree entries listed in reverse order (inputs, parent arrays and slot ids permuted together)
+    give every slot the same node captures bit for bit, and each entry's outputs move with it; the
+    committed state is untouched either way."""
+    device, gdn = _mods()
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=5, n_batch=3, n_tok=40)
+    say("[tree slot permutation] 3 entries x 40 nodes")
+    inp = W.make_tree_inputs(shape, 2)
+    rng = np.random.default_rng(8)
+    inp["parent"] = np.stack([W.random_tree(rng, shape.n_tok, 8) for _ in range(shape.n_batch)])
+    perm = np.arange(shape.n_batch)[::-1].copy()
+    pinp = dict(inp)
+    for k in ("qkv", "z", "alpha", "beta", "slot_ids", "parent"):
+        pinp[k] = np.ascontiguousarray(np.asarray(inp[k])[perm])
+    a = _tree_upload(shape, inp, fill_capture=0.0)
+    b = _tree_upload(shape, pinp, fill_capture=0.0)
+    device.verify_tree(a)
+    device.verify_tree(b)
+    torch.cuda.synchronize()
+    for k in ("state", "conv_state", "cap_ssm", "cap_conv"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["out"][torch.from_numpy(perm).cuda()], b["out"])
+
+
 def test_tree_multiple_roots_and_malformed_parents():
     """Nodes with parent -1 start from the committed state; a malformed parent is treated as -1
     (or rejected with GDN_F_CHECK_INDICES before anything runs)."""
