@@ -149,6 +149,36 @@ def test_slot_permutation_gives_the_same_per_slot_results(n_batch):
     assert torch.equal(a["out"][torch.from_numpy(perm).cuda()], b["out"])
 
 
+@pytest.mark.parametrize("base", ["single_slot", "tiny_fp32"])
+def test_extreme_gates_and_gate_inputs(base):
+    """alpha far into both tails of softplus (rho down to e^-82, or 1 to the last bit), beta at 0
+    and 1, and z far into both tails of the SiLU, against the oracle at the usual bar.  Larger
+    alpha is left out: there rho, and with beta = 0 the whole state, falls below fp32's normal range
+    (2^-126), which an fp32 state cannot hold, so a relative comparison with the fp64 oracle has no
+    meaning."""
+    shape = W.shape_with(W.SINGLE_SLOT_VERIFY if base == "single_slot" else W.TINY_VERIFY, n_tok=16)
+    say(f"[extreme gates] {base}")
+    inp = W.make_inputs(shape, 12)
+    T, H = shape.n_tok, shape.n_vh
+    alpha = np.asarray(inp["alpha"]).copy()
+    beta = np.asarray(inp["beta"]).copy()
+    z = np.asarray(inp["z"]).copy()
+    for t in range(T):
+        alpha[:, t, :] = (-80.0, 30.0, -30.0, 0.0, 20.0)[t % 5]
+        if t % 4 == 1:
+            beta[:, t, :] = 0.0
+        elif t % 4 == 3:
+            beta[:, t, :] = 1.0
+    z[:, ::3] = 20.0
+    z[:, 1::3] *= -10.0
+    inp.update(alpha=alpha, beta=beta, z=z)
+    dev = _dev()
+    d = dev.upload(shape, inp)
+    dev.verify(d)
+    torch.cuda.synchronize()
+    _check_pool(shape, inp, d, tol_for(shape))
+
+
 def test_beta_zero_no_decay_is_identity_on_gpu():
     shape = W.shape_with(W.SINGLE_SLOT_VERIFY, n_tok=5)
     inp = W.make_inputs(shape, 5)
