@@ -342,8 +342,9 @@ struct PrepLds {
     static constexpr size_t pm = tm + sizeof(float) * C * kCP;   //                         [C][kCP] P
     static constexpr size_t scr = pm + sizeof(float) * C * kCP;  //                         [4][16][16] scratch
     static constexpr int heads = 4;  // value heads whose gates are resident at once
-    static constexpr size_t gate = qk_bytes > tp_bytes ? qk_bytes : tp_bytes;  // per head: Gamma, gamma, beta, decay [4][C]
-    static constexpr size_t total = gate + sizeof(float) * heads * 4 * C;
+    static constexpr size_t gate = qk_bytes > tp_bytes ? qk_bytes : tp_bytes;  // per head: Gamma (fp64), gamma, beta, decay
+    static constexpr int slot_floats = 5 * C;  // Gamma as C doubles, then gamma, beta, decay [3][C]
+    static constexpr size_t total = gate + sizeof(float) * heads * slot_floats;
 };
 static_assert(3 * PrepLds<128>::total <= 160 * 1024 && 3 * PrepLds<64>::total <= 160 * 1024,
               "three prep workgroups must fit one CU's LDS");
@@ -410,9 +411,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
     float *K = reinterpret_cast<float *>(smem + L::k);
     float *Tm = reinterpret_cast<float *>(smem + L::tm);
     float *Pm = reinterpret_cast<float *>(smem + L::pm);
-    // gates of value head hk R + hh, kept in slot hh % L::heads: Gamma_t, gamma_t = exp(Gamma_t),
-    // beta_t (0 past the end), exp(Gamma_C - Gamma_t)
-    auto gate_slot = [&](int hh) { return reinterpret_cast<float *>(smem + L::gate) + (hh % L::heads) * 4 * C; };
+    // gates of value head hk R + hh, kept in slot hh % L::heads: Gamma_t (fp64), then gamma_t =
+    // exp(Gamma_t), beta_t (0 past the end), exp(Gamma_C - Gamma_t) (fp32).  Gamma is a running sum
+    // of log decays that reaches hundreds within a chunk under strong decay, where an fp32 ulp
+    // (~6e-5 at 650) would leave the ratios exp(Gamma_t - Gamma_s) of nearby tokens that relative
+    // error; its differences are taken in fp64 and only then rounded.
+    auto gate_slot = [&](int hh) { return reinterpret_cast<float *>(smem + L::gate) + (hh % L::heads) * L::slot_floats; };
 
     const act_t *qkv = static_cast<const act_t *>(a.qkv);
     auto gchan = [&](int lc) -> int { return lc < D ? q0 + lc : k0 + (lc - D); };
@@ -462,17 +466,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
             g = -expf(in.alog) * softplus_f(word_f32(in.al) + in.dtb);
             b = word_f32(in.be);
         }
-        float x = g;
+        double x = g;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off);
+            const double y = __shfl_up(x, off);
             if (lane >= off) x += y;
         }
-        float *G = gate_slot(hh);
-        G[lane] = x;
-        G[C + lane] = expf(x);
-        G[2 * C + lane] = b;
-        G[3 * C + lane] = expf(__shfl(x, 63) - x);
+        reinterpret_cast<double *>(gate_slot(hh))[lane] = x;
+        float *G = gate_slot(hh) + 2 * C;
+        G[lane] = (float)exp(x);  // fp64 exponentials of fp64 sums, rounded once: 64 per head
+        G[C + lane] = b;
+        G[2 * C + lane] = (float)exp(__shfl(x, 63) - x);
     };
 
     // the first value heads' gate inputs travel with the q | k rows below
@@ -645,13 +649,15 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
             if (wave < min(R - hh, L::heads)) gate_put(hh + wave, gate_load(hh + wave));
             lds_barrier();
         }
-        const float *Gam = gate_slot(hh), *gam = Gam + C, *bet = gam + C, *dec = bet + C;
+        const double *Gam = reinterpret_cast<const double *>(gate_slot(hh));
+        const float *gam = gate_slot(hh) + 2 * C, *bet = gam + C, *dec = bet + C;
         {
             float *Dm = wave < 2 ? Tm : Pm;
             // Every gate this lane's 20 entries use is read before any entry is formed, and the
             // entries are selected, not branched to: a read under a lane condition would cost an
             // LDS round trip per entry.
-            float gt[5][4], bt[5][4], gs[5];
+            double gt[5][4], gs[5];
+            float bt[5][4];
 #pragma unroll
             for (int jt = 0; jt < 5; ++jt) {
                 gs[jt] = Gam[16 * tile_ct(jt) + (lane & 15)];
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * rt + (lane >> 4) * 4 + r;
-                    const float ratio = exp_decay(gt[jt][r] - gs[jt]);
+                    const float ratio = exp_decay((float)(gt[jt][r] - gs[jt]));
                     const float av = s_ < t ? bt[jt][r] * ratio * tiles[jt][r] : 0.f;
                     const float pv = s_ <= t ? ratio * tiles[jt][r] : 0.f;
                     Dm[t * kCP + s_] = wave < 2 ? av : pv;

@@ -79,6 +79,9 @@ PREFILL_CASES = {
                                            out_dtype=W.F32), {"weak_decay": True}, 1),
     "bf16_d64_qk_norm_150": (W.shape_with(W.TINY_VERIFY, n_tok=150, n_kh=2, n_vh=4, act_dtype=W.BF16,
                                           out_dtype=W.BF16), {"weak_decay": True}, 1),
+    # fp32 at the workloads' own decay (a 64-token chunk's running log decay reaches ~-90)
+    "fp32_d128_standard_decay_130": (W.shape_with(W.CHUNKED_PREFILL, n_tok=130, n_kh=2, n_vh=4,
+                                                  act_dtype=W.F32, out_dtype=W.F32), {}, 0),
 }
 
 
@@ -89,6 +92,31 @@ def test_prefill_parity(name):
     inp = W.make_inputs(shape, 0, **kw)
     d = _run_prefill(shape, inp, flags)
     _check(shape, inp, d, flags=flags)
+
+
+@pytest.mark.parametrize("base", ["bf16_d128", "fp32_d64"])
+def test_prefill_extreme_gates(base):
+    """alpha at -80 / +-30 / 20 (rho 1 to the last bit, or down to e^-82, so that the running decay
+    of a 64-token chunk falls far below fp32's range), beta at 0 and 1 and z far into both SiLU
+    tails, over four chunks with a ragged tail, against the sequential oracle at the usual bar."""
+    shape = (W.shape_with(W.CHUNKED_PREFILL, n_tok=200) if base == "bf16_d128"
+             else W.shape_with(W.TINY_VERIFY, n_tok=200, n_kh=2, n_vh=4))
+    say(f"[prefill extreme gates] {base}")
+    inp = W.make_inputs(shape, 13)
+    alpha = np.asarray(inp["alpha"]).copy()
+    beta = np.asarray(inp["beta"]).copy()
+    z = np.asarray(inp["z"]).copy()
+    for t in range(shape.n_tok):
+        alpha[:, t, :] = (-80.0, 30.0, -30.0, 0.0, 20.0)[t % 5]
+        if t % 4 == 1:
+            beta[:, t, :] = 0.0
+        elif t % 4 == 3:
+            beta[:, t, :] = 1.0
+    z[:, ::3] = 20.0
+    z[:, 1::3] *= -10.0
+    inp.update(alpha=alpha, beta=beta, z=z)
+    d = _run_prefill(shape, inp)
+    _check(shape, inp, d)
 
 
 def test_prefill_full_8192_every_head():
