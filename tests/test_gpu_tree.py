@@ -202,6 +202,37 @@ def test_tree_slot_permutation_gives_the_same_per_slot_results():
     assert torch.equal(a["out"][torch.from_numpy(perm).cuda()], b["out"])
 
 
+def test_tree_extreme_gates():
+    """Extreme gates on a 40-node tree: alpha at -80 / +-30 / 20, beta at 0 where rho is 1 to the
+    last bit and at 1 where alpha is 0, z far into both SiLU tails, against the oracle.  beta = 0
+    is kept off the strong decays: along a root path two of them (e^-82 each) would take the state
+    below fp32's range, which an fp32 state cannot hold."""
+    device, gdn = _mods()
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=1, n_tok=40)
+    say("[tree extreme gates] 40 nodes")
+    inp = W.make_tree_inputs(shape, 4)
+    rng = np.random.default_rng(9)
+    inp["parent"] = np.stack([W.random_tree(rng, shape.n_tok, 8) for _ in range(shape.n_batch)])
+    alpha = np.asarray(inp["alpha"]).copy()
+    beta = np.asarray(inp["beta"]).copy()
+    z = np.asarray(inp["z"]).copy()
+    for t in range(shape.n_tok):
+        alpha[:, t, :] = (-80.0, 30.0, -30.0, 0.0, 20.0)[t % 5]
+        if t % 5 == 0:
+            beta[:, t, :] = 0.0
+        elif t % 5 == 3:
+            beta[:, t, :] = 1.0
+    z[:, ::3] = 20.0
+    z[:, 1::3] *= -10.0
+    # round the edits to the storage dtype, so that the device and the oracle read the same values
+    act = shape.act_dtype
+    inp.update(alpha=W.round_to(alpha, act), beta=W.round_to(beta, act), z=W.round_to(z, act))
+    d = _tree_upload(shape, inp)
+    device.verify_tree(d)
+    torch.cuda.synchronize()
+    _check_tree(shape, inp, d)
+
+
 def test_tree_multiple_roots_and_malformed_parents():
     """Nodes with parent -1 start from the committed state; a malformed parent is treated as -1
     (or rejected with GDN_F_CHECK_INDICES before anything runs)."""

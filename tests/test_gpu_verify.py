@@ -171,7 +171,9 @@ def test_extreme_gates_and_gate_inputs(base):
             beta[:, t, :] = 1.0
     z[:, ::3] = 20.0
     z[:, 1::3] *= -10.0
-    inp.update(alpha=alpha, beta=beta, z=z)
+    # round the edits to the storage dtype, so that the device and the oracle read the same values
+    act = shape.act_dtype
+    inp.update(alpha=W.round_to(alpha, act), beta=W.round_to(beta, act), z=W.round_to(z, act))
     dev = _dev()
     d = dev.upload(shape, inp)
     dev.verify(d)
