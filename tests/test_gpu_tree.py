@@ -233,6 +233,45 @@ def test_tree_extreme_gates():
     _check_tree(shape, inp, d)
 
 
+def test_tree_captured_in_a_graph_matches_eager():
+    """A 130-node tree verify (three launches; the later ones start nodes from captures the earlier
+    ones wrote) recorded under stream capture and replayed three times, with new activations and a
+    new tree written in place before each replay and the eager call and a synchronisation between
+    replays: every replay leaves the eager call's node captures, conv captures and outputs bit for
+    bit, and the first matches the oracle."""
+    device, gdn = _mods()
+    shape = W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=2, n_tok=130)
+    inp = W.make_tree_inputs(shape, 21)
+    rng = np.random.default_rng(22)
+    inp["parent"] = np.stack([W.random_tree(rng, shape.n_tok, 8) for _ in range(shape.n_batch)])
+    eager = _tree_upload(shape, inp, fill_capture=0.0)
+    graph = _tree_upload(shape, inp, fill_capture=0.0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        device.verify_tree(graph)
+    keys = ("out", "cap_ssm", "cap_conv", "state", "conv_state")
+    for r in range(3):
+        say(f"[tree graph] replay {r}")
+        if r > 0:  # new activations and a new tree, written in place into both sets
+            nin = W.make_tree_inputs(shape, 600 + r)
+            nin["parent"] = np.stack([W.random_tree(rng, shape.n_tok, 4 + 4 * r) for _ in range(shape.n_batch)])
+            for k in ("qkv", "z", "alpha", "beta", "parent"):
+                src = torch.from_numpy(np.ascontiguousarray(nin[k])).to(eager[k].dtype).cuda()
+                eager[k].copy_(src)
+                graph[k].copy_(src)
+        graph["out"].fill_(7.0)
+        torch.cuda.synchronize()
+        device.verify_tree(eager)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(eager[k], graph[k]), (r, k)
+        if r == 0:
+            _check_tree(shape, inp, graph)
+
+
 def test_tree_multiple_roots_and_malformed_parents():
     """Nodes with parent -1 start from the committed state; a malformed parent is treated as -1
     (or rejected with GDN_F_CHECK_INDICES before anything runs)."""

@@ -112,6 +112,52 @@ def test_verify_without_capture_matches_capture_path():
     assert torch.equal(a["out"], b["out"])
 
 
+@pytest.mark.parametrize("where", ["fresh_stream", "stream_with_scratch"])
+def test_single_slot_verify_captured_in_a_graph_matches_eager(where):
+    """One slot x 16 tokens (the launch that splits each head's rows over four workgroups and
+    normalises in a second kernel) recorded under torch's stream capture and replayed three times,
+    the committed state restored in between with eager work and a synchronisation: every replay
+    leaves the eager call's state, conv state, captures and outputs bit for bit.  Captured on a
+    fresh stream, the call finds no readout scratch for that stream and must not allocate one, so it
+    records the one-kernel path; captured on a stream whose eager launch already holds a scratch,
+    it records the split launch and its norm kernel."""
+    shape = W.SINGLE_SLOT_VERIFY
+    say(f"[verify graph] 1 slot x 16, {where}")
+    inp = W.make_inputs(shape, 31)
+    dev = _dev()
+    d = dev.upload(shape, inp, fill_capture=0.0)
+    st0, cs0 = d["state"].clone(), d["conv_state"].clone()
+    keys = ("out", "state", "conv_state", "cap_ssm", "cap_conv")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        dev.verify(d)
+    torch.cuda.synchronize()
+    want = {k: d[k].clone() for k in keys}
+    _check_pool(shape, inp, d, tol_for(shape))
+    g = torch.cuda.CUDAGraph()
+    d["state"].copy_(st0)
+    d["conv_state"].copy_(cs0)
+    torch.cuda.synchronize()
+    if where == "fresh_stream":
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            dev.verify(d)
+    else:
+        with torch.cuda.graph(g, stream=side):
+            dev.verify(d)
+    for rep in range(3):
+        d["state"].copy_(st0)
+        d["conv_state"].copy_(cs0)
+        d["out"].fill_(7.0)
+        d["cap_ssm"].fill_(7.0)
+        with torch.cuda.stream(side):  # eager work on the capture's stream between replays
+            dev.verify(dev.upload(shape, W.make_inputs(shape, 40 + rep)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(d[k], want[k]), (rep, k)
+
+
 def test_verify_is_deterministic():
     shape = W.shape_with(W.MULTI_SLOT_VERIFY, n_pool=8, n_batch=8)
     inp = W.make_inputs(shape, 4)
