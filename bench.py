@@ -127,7 +127,7 @@ WARM_S = 0.25
 def time_launches(fn, n: int, warmup: int = 20, warm_s=None) -> float:
     """Average duration in microseconds of fn() over n launches, HIP events on the current stream,
     after `warmup` untimed launches and then more untimed launches until `warm_s` seconds (default
-    WARM_S) have passed.  Each component starts after host-side input generation has left the GPU
+    WARM_S) have passed or 1000 of them have run.  Each component starts after host-side input generation has left the GPU
     idle, and its first launches run slower for a few tens of milliseconds: the 1024-row
     in-projection took 155 us per launch over its first 70 launches and 133 us from about 30 ms of
     launches on, whatever its data.  The timed launches themselves are unchanged."""
@@ -137,10 +137,11 @@ def time_launches(fn, n: int, warmup: int = 20, warm_s=None) -> float:
         fn()
     torch.cuda.synchronize()
     span = WARM_S if warm_s is None else warm_s
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < span:
+    t0, extra = time.perf_counter(), 0
+    while time.perf_counter() - t0 < span and extra < 1000:
         for _ in range(4):
             fn()
+        extra += 4
         torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -281,7 +282,7 @@ def components(args) -> dict:
     us = time_launches(lambda: device.prefill(d), 20, warmup=40)
     fl = bytemodel.prefill_flops(s)
     out["chunked_prefill"] = {"workload": "1 slot x 8192 tokens, 16/32 heads, d=128, bf16, chunk 64",
-                              "timing": f"20 calls after 40 warm-up calls and {WARM_S} s of further untimed calls",
+                              "timing": f"20 calls after 40 warm-up calls and {WARM_S} s (at most 1000 calls) of further untimed calls",
                               "us": us, "tokens_per_s": s.n_tok / (us * 1e-6),
                               "hbm_gbps": bytemodel.prefill_bytes(s) / (us * 1e-6) / 1e9,
                               "algorithmic_flops": fl, "tflops": fl / (us * 1e-6) / 1e12,
