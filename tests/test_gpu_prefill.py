@@ -94,13 +94,14 @@ def test_prefill_parity(name):
     _check(shape, inp, d, flags=flags)
 
 
-@pytest.mark.parametrize("base", ["bf16_d128", "fp32_d64"])
+@pytest.mark.parametrize("base", ["bf16_d128", "fp32_d64", "bf16_d128_qk_norm"])
 def test_prefill_extreme_gates(base):
     """alpha at -80 / +-30 / 20 (rho 1 to the last bit, or down to e^-82, so that the running decay
     of a 64-token chunk falls far below fp32's range), beta at 0 and 1 and z far into both SiLU
     tails, over four chunks with a ragged tail, against the sequential oracle at the usual bar."""
-    shape = (W.shape_with(W.CHUNKED_PREFILL, n_tok=200) if base == "bf16_d128"
+    shape = (W.shape_with(W.CHUNKED_PREFILL, n_tok=200) if base.startswith("bf16_d128")
              else W.shape_with(W.TINY_VERIFY, n_tok=200, n_kh=2, n_vh=4))
+    flags = 1 if base.endswith("qk_norm") else 0  # SiLU after the conv, unit q / k, q / sqrt(d_k)
     say(f"[prefill extreme gates] {base}")
     inp = W.make_inputs(shape, 13)
     alpha = np.asarray(inp["alpha"]).copy()
@@ -117,8 +118,8 @@ def test_prefill_extreme_gates(base):
     # round the edits to the storage dtype, so that the device and the oracle read the same values
     act = shape.act_dtype
     inp.update(alpha=W.round_to(alpha, act), beta=W.round_to(beta, act), z=W.round_to(z, act))
-    d = _run_prefill(shape, inp)
-    _check(shape, inp, d)
+    d = _run_prefill(shape, inp, flags=flags)
+    _check(shape, inp, d, flags=flags)
 
 
 def test_prefill_full_8192_every_head():

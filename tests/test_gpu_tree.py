@@ -29,9 +29,12 @@ def _tree_upload(shape, inp, **kw):
     return device.upload(shape, inp, mode=gdn.GDN_TREE, **kw)
 
 
-def _check_tree(shape, inp, d, units=None, flags=0):
-    """Node states, node outputs and per-node conv states against the oracle."""
+def _check_tree(shape, inp, d, units=None, flags=0, out_tol=None):
+    """Node states, node outputs and per-node conv states against the oracle.  out_tol, if given,
+    maps the oracle's result to per-(unit, node) output tolerances [U][T]."""
     o = ref.tree_units(shape, inp, units, flags=flags)
+    tol = tol_for(shape)
+    otol = np.full((len(o["units"][0]), shape.n_tok), tol) if out_tol is None else out_tol(o)
     cap = d["cap_ssm"]
     out = to_np(d["out"])
     worst_s, worst_o = 0.0, 0.0
@@ -42,14 +45,14 @@ def _check_tree(shape, inp, d, units=None, flags=0):
         c = to_np(cap[s, :, h])
         for i in range(shape.n_tok):
             worst_s = max(worst_s, rel_err(c[i], o["cap"][u, i]))
-            worst_o = max(worst_o, out_err(shape, out[b, i, h], o["y"][u, i]))
+            worst_o = max(worst_o, out_err(shape, out[b, i, h], o["y"][u, i]) / otol[u, i] * tol)
     cc = to_np(d["cap_conv"])
     expect_cc = ref.tree_conv(shape, inp)
     for b in range(shape.n_batch):
         s = int(inp["slot_ids"][b])
         np.testing.assert_array_equal(cc[s, :shape.n_tok], expect_cc[b])
-    say(f"  tree {W.describe(shape)} worst rel err state {worst_s:.2e} out {worst_o:.2e}")
-    tol = tol_for(shape)
+    say(f"  tree {W.describe(shape)} worst rel err state {worst_s:.2e} out {worst_o:.2e}"
+        + ("" if out_tol is None else " (out scaled to the per-node bar)"))
     assert worst_s <= tol and worst_o <= tol
 
 
@@ -202,14 +205,17 @@ def test_tree_slot_permutation_gives_the_same_per_slot_results():
     assert torch.equal(a["out"][torch.from_numpy(perm).cuda()], b["out"])
 
 
-def test_tree_extreme_gates():
+@pytest.mark.parametrize("base", ["bf16_d128", "fp32_d64"])
+def test_tree_extreme_gates(base):
     """Extreme gates on a 40-node tree: alpha at -80 / +-30 / 20, beta at 0 where rho is 1 to the
     last bit and at 1 where alpha is 0, z far into both SiLU tails, against the oracle.  beta = 0
     is kept off the strong decays: along a root path two of them (e^-82 each) would take the state
-    below fp32's range, which an fp32 state cannot hold."""
+    below fp32's range, which an fp32 state cannot hold.  In fp32 each node's output is held to 1e-5,
+    or to about two ulps of |S| |q| where the readout cancels (_readout_bar)."""
     device, gdn = _mods()
-    shape = W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=1, n_tok=40)
-    say("[tree extreme gates] 40 nodes")
+    shape = (W.shape_with(W.TREE_VERIFY, n_pool=2, n_batch=1, n_tok=40) if base == "bf16_d128"
+             else W.shape_with(W.TINY_VERIFY, n_pool=2, n_batch=2, n_tok=40))
+    say(f"[tree extreme gates] 40 nodes, {base}")
     inp = W.make_tree_inputs(shape, 4)
     rng = np.random.default_rng(9)
     inp["parent"] = np.stack([W.random_tree(rng, shape.n_tok, 8) for _ in range(shape.n_batch)])
@@ -230,7 +236,34 @@ def test_tree_extreme_gates():
     d = _tree_upload(shape, inp)
     device.verify_tree(d)
     torch.cuda.synchronize()
-    _check_tree(shape, inp, d)
+    _check_tree(shape, inp, d, out_tol=None if base == "bf16_d128" else lambda o: _readout_bar(shape, inp, o))
+
+
+def _readout_bar(shape, inp, o):
+    """Per-(unit, node) output bar of an fp32 tree call: 1e-5 relative to the output, or 1e-7
+    (about two fp32 ulps) relative to |S| |q|, whichever is larger.  After a strong decay the state
+    is close to rank one (beta v k^T), and o = S q then rests on k.q alone; where q is nearly
+    orthogonal to k the readout cancels, and an fp32 dot product is exact only to its ulp relative
+    to its operands, not to the cancelled result.  |S| and q come from the oracle's own node states
+    and conv windows (parent's conv state rows, then the node's raw row)."""
+    cc = ref.tree_conv(shape, inp)
+    w = inp["conv_w"].astype(np.float64)
+    dk, R = shape.d_k, shape.n_vh // shape.n_kh
+    ub, uh = o["units"]
+    bar = np.empty((len(ub), shape.n_tok))
+    for u in range(len(ub)):
+        b, h = int(ub[u]), int(uh[u])
+        s = int(inp["slot_ids"][b])
+        hk = h // R
+        for i in range(shape.n_tok):
+            p = int(inp["parent"][b, i])
+            prev = inp["conv_state"][s] if p < 0 else cc[b, p]
+            win = np.vstack([prev.astype(np.float64), inp["qkv"][b, i].astype(np.float64)[None, :]])
+            q = (w.T * win).sum(0)[hk * dk:(hk + 1) * dk]
+            S = o["cap"][u, i]
+            cond = np.linalg.norm(S) * np.linalg.norm(q) / max(np.linalg.norm(S @ q), 1e-300)
+            bar[u, i] = max(tol_for(shape), 1e-7 * cond)
+    return bar
 
 
 def test_tree_captured_in_a_graph_matches_eager():
