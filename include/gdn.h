@@ -390,7 +390,10 @@ typedef struct gdn_out_seg {
 int gdn_linear(const void *x, const void *w, int32_t M, int32_t N, int32_t K, const gdn_out_seg *segs,
                int32_t n_segs, void *stream);
 
-/* Thread-local description of the last error of this thread ("" after success). */
+/* Thread-local description of the last error of this thread ("" after success).  The pages'
+ * header keeps one error-reporting channel that its loaders and graph builders write to, with
+ * calls returning failure and leaving the message there (lucebox-hub internal.h, set_last_error);
+ * every entry point here returns a status code and leaves its message for this call. */
 const char *gdn_last_error(void);
 
 /* Library version string. */
