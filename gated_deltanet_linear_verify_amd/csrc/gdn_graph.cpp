@@ -91,7 +91,7 @@ GDN_API int gdn_graph_create(const gdn_dims *dims, const gdn_layer *layers, int3
     int rc = GDN_OK;
     // A readout scratch for the capture stream, kept by the graph: row-split verify launches under
     // the capture use it (without one they take the unsplit path).
-    (void)gdn::split_scratch(st, true);
+    (void)gdn::split_scratch_reserve(st);
     if (hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal)) {
         rc = gdn::abi_fail(GDN_ERR_HIP, "gdn_graph_create: begin capture: %s", hipGetErrorString(e));
     } else {

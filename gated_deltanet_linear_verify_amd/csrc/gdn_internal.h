@@ -35,9 +35,13 @@ struct VerifyArgs {
 };
 
 // The row-split verify's readout scratch for stream st on the current device: the buffer kept for
-// the stream, else (allocate, and st not capturing) a new one of kSplitScratchBytes, else NULL.
+// the stream (while st is capturing, only one reserved for capture), else (allocate, and st not
+// capturing) a new one of kSplitScratchBytes, else NULL.
 constexpr size_t kSplitScratchBytes = size_t(4) << 20;
 void *split_scratch(hipStream_t st, bool allocate);
+// Keep a buffer for st that launches under a capture on st may use (allocated now if st has none
+// and is not capturing); false if there is none.
+bool split_scratch_reserve(hipStream_t st);
 // Remove the buffer kept for st and hand it to the caller (who frees it), or NULL.
 void *split_scratch_take(hipStream_t st);
 

@@ -127,9 +127,11 @@ typedef struct gdn_capture {
  * Memory: with few heads in flight (n_batch * H_v * 4 <= 256, n_tok >= 3) the rows of each head
  * are split over several workgroups, which need a readout scratch: the first such call on a
  * stream allocates 4 MiB of device memory, kept for that stream until the process ends (calls on
- * different streams never share one).  Under stream capture no memory is allocated: a capture
- * stream without a buffer gets the unsplit kernels, with the same results bit for bit
- * (gdn_graph_create reserves a buffer for its own capture stream).
+ * different streams never share one).  Under stream capture no memory is allocated and no
+ * stream's buffer is recorded (a recorded graph could be replayed on another stream while that
+ * stream runs later calls): the capture gets the unsplit kernels, with the same results bit for
+ * bit.  gdn_graph_create reserves a buffer for its own private capture stream and keeps it for the
+ * graph's lifetime.
  */
 int gdn_verify(const gdn_dims *dims, float *state, float *conv_state, const void *qkv,
                const void *z, const void *alpha, const void *beta, const float *A_log,

@@ -118,9 +118,9 @@ def test_single_slot_verify_captured_in_a_graph_matches_eager(where):
     normalises in a second kernel) recorded under torch's stream capture and replayed three times,
     the committed state restored in between with eager work and a synchronisation: every replay
     leaves the eager call's state, conv state, captures and outputs bit for bit.  Captured on a
-    fresh stream, the call finds no readout scratch for that stream and must not allocate one, so it
-    records the one-kernel path; captured on a stream whose eager launch already holds a scratch,
-    it records the split launch and its norm kernel."""
+    fresh stream the call must not allocate a readout scratch, and captured on a stream whose eager
+    launch already holds one it must not record that buffer (a replay on another stream could run
+    alongside that stream's later calls): both record the one-kernel path."""
     shape = W.SINGLE_SLOT_VERIFY
     say(f"[verify graph] 1 slot x 16, {where}")
     inp = W.make_inputs(shape, 31)
