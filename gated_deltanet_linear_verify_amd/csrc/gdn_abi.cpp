@@ -94,6 +94,11 @@ int check_capture(const gdn_capture *c, int mode, int n_tok, const gdn_dims *d)
 // Host copy + validation of device index arrays (GDN_F_CHECK_INDICES).
 int fetch_i32(const int32_t *dev, size_t n, hipStream_t st, std::vector<int32_t> &out)
 {
+    // A capturing stream can record neither the copy nor the wait, and trying would end the
+    // caller's capture: refuse before touching the stream.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return fail(GDN_ERR_ARG, "GDN_F_CHECK_INDICES copies indices to the host, which a capturing stream cannot do");
     out.resize(n);
     hipError_t e = hipMemcpyAsync(out.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);

@@ -39,7 +39,9 @@
  * - Batch entry b uses slot slot_ids[b] (device int32 [B]).  Slots within one call must be
  *   distinct.  Entries whose slot is outside [0, n_pool) are skipped by the kernels (nothing is
  *   read or written for them); GDN_F_CHECK_INDICES makes the host copy the index arrays back
- *   (synchronously) and fail with GDN_ERR_RANGE instead.
+ *   (synchronously) and fail with GDN_ERR_RANGE instead.  On a stream under capture that copy
+ *   cannot be recorded: with the flag set such a call returns GDN_ERR_ARG and leaves the stream
+ *   and its capture untouched.
  * - Return value: GDN_OK or an error code.  On error nothing has been enqueued and nothing is
  *   mutated; gdn_last_error() returns a thread-local description (lucebox-hub internal.h keeps
  *   one error sink, set_last_error).  GDN_ERR_HIP reports a failed launch.

@@ -383,6 +383,31 @@ def test_check_indices_rejects_bad_slots_without_mutation():
         assert torch.equal(before, d["state"])
 
 
+def test_check_indices_under_capture_is_refused_and_the_capture_survives():
+    """With GDN_F_CHECK_INDICES a call on a capturing stream returns GDN_ERR_ARG before touching
+    the stream (its host copy cannot be recorded); the capture goes on, and a verify recorded after
+    it replays to the eager call's results bit for bit."""
+    gdn = _gdn()
+    dev = _dev()
+    shape = W.shape_with(W.TINY_VERIFY, n_pool=3, n_batch=2, n_tok=5)
+    inp = W.make_inputs(shape, 18)
+    checked = dev.upload(shape, inp, flags=gdn.GDN_F_CHECK_INDICES)
+    eager = dev.upload(shape, inp, fill_capture=0.0)
+    graph = dev.upload(shape, inp, fill_capture=0.0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        with pytest.raises(gdn.GdnError) as ei:
+            dev.verify(checked)
+        dev.verify(graph)
+    assert ei.value.code == gdn.GDN_ERR_ARG
+    dev.verify(eager)
+    g.replay()
+    torch.cuda.synchronize()
+    for k in ("out", "state", "conv_state", "cap_ssm", "cap_conv"):
+        assert torch.equal(eager[k], graph[k]), k
+
+
 def test_out_of_range_slot_is_skipped_by_the_kernel():
     """Without the host check, an entry whose slot is outside the pool is skipped (its bounds
     check in the kernel stops it before any access); the other entries are unaffected."""
